@@ -1,0 +1,41 @@
+"""Pack per-tensor gradients into the bucket-major flat buffer, and back.
+
+"Data parallelism in depth" §4.2 (The Bucket mechanism) packs the gradients of
+several parameters into one bucket so that one collective serves them all;
+"Distributed Training: Data Parallel, Model Parallel and FSDP Strategies",
+section "Inside DDP", notes the buckets can be the gradients' own storage
+(gradient_as_bucket_view).  The flat buffer holds bucket b at [base_b, base_b+L_b):
+its tensors densely in bucket order, then zeros up to L_b.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .plan import Plan
+
+
+def pack(plan: Plan, grads, dtype=np.uint16) -> np.ndarray:
+    """grads: list (forward order) of 1-D arrays (bf16 bits as uint16 by default)
+    -> flat[flat_len] of the same dtype, pads zero."""
+    flat = np.zeros(plan.flat_len, dtype=dtype)
+    for t, g in enumerate(grads):
+        g = np.asarray(g, dtype=dtype).reshape(-1)
+        if g.size != plan.numel[t]:
+            raise ValueError(f"tensor {t}: {g.size} elements, plan says {plan.numel[t]}")
+        off = plan.tensor_offset[t]
+        flat[off:off + g.size] = g
+    return flat
+
+
+def unpack(plan: Plan, flat: np.ndarray):
+    """Inverse of pack: the per-tensor views of a flat buffer (forward order)."""
+    return [flat[plan.tensor_offset[t]:plan.tensor_offset[t] + n].copy()
+            for t, n in enumerate(plan.numel)]
+
+
+def owner_view(plan: Plan, flat: np.ndarray, r: int) -> np.ndarray:
+    """Rank r's chunks of a flat buffer, concatenated in bucket order (shard layout)."""
+    parts = [flat[slice(*plan.chunk_range(b, r))] for b in range(len(plan.buckets))]
+    if not parts:
+        return flat[:0].copy()
+    return np.concatenate(parts)

@@ -1,0 +1,135 @@
+"""ctypes wrappers around the two implementations of the input generator.
+
+host_fill / host_fill_idx run the C implementation (OpenMP) into NumPy arrays;
+dev_fill runs the HIP implementation into device memory on a stream.  Both
+produce the same bits for the same (workload id, kind, rank, element index).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+HOST_LIB = os.path.join(_HERE, "libsynth_host.so")
+DEV_LIB = os.path.join(_HERE, "libsynth_dev.so")
+
+MODE_F32 = 0
+MODE_ABS = 1
+MODE_BF16 = 2
+
+_host = None
+_dev = None
+
+
+def key1(cfg_id: int, kind: int, rank: int) -> int:
+    if not (0 <= cfg_id < 256 and 0 <= kind < 256 and 0 <= rank < 65536):
+        raise ValueError("generator key field out of range")
+    return (cfg_id << 24) | (kind << 16) | rank
+
+
+def scale_for(std: float) -> np.float32:
+    """fp32 multiplier that gives the Irwin-Hall sum the requested std."""
+    return np.float32(std / math.sqrt(8.0 * (65536.0 ** 2 - 1.0) / 3.0))
+
+
+def _load_host():
+    global _host
+    if _host is None:
+        if not os.path.exists(HOST_LIB):
+            raise RuntimeError(f"{HOST_LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(HOST_LIB)
+        lib.synth_fill_host.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64,
+                                        ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                                        ctypes.c_void_p]
+        lib.synth_fill_host.restype = ctypes.c_int
+        lib.synth_fill_host_idx.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                                            ctypes.c_void_p]
+        lib.synth_fill_host_idx.restype = ctypes.c_int
+        lib.synth_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_philox4x32_10.restype = None
+        _host = lib
+    return _host
+
+
+def _load_dev():
+    global _dev
+    if _dev is None:
+        if not os.path.exists(DEV_LIB):
+            raise RuntimeError(f"{DEV_LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(DEV_LIB)
+        lib.synth_fill_dev.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64,
+                                       ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_fill_dev.restype = ctypes.c_int
+        lib.synth_copy_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_void_p]
+        lib.synth_copy_dev.restype = ctypes.c_int
+        _dev = lib
+    return _dev
+
+
+def philox4x32_10(ctr, key):
+    """One Philox4x32-10 block (for the known-answer test)."""
+    lib = _load_host()
+    c = (ctypes.c_uint32 * 4)(*ctr)
+    k = (ctypes.c_uint32 * 2)(*key)
+    o = (ctypes.c_uint32 * 4)()
+    lib.synth_philox4x32_10(c, k, o)
+    return list(o)
+
+
+def _dtype(mode):
+    return np.uint16 if mode == MODE_BF16 else np.float32
+
+
+def host_fill(cfg_id, kind, rank, start, n, std, mode, seed=None, out=None):
+    from .workloads import SEED
+    seed = SEED if seed is None else seed
+    if out is None:
+        out = np.empty(n, dtype=_dtype(mode))
+    assert out.dtype == _dtype(mode) and out.flags.c_contiguous and out.size == n
+    rc = _load_host().synth_fill_host(seed, key1(cfg_id, kind, rank), start, n,
+                                      scale_for(std), mode, out.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("synth_fill_host failed")
+    return out
+
+
+def host_fill_idx(cfg_id, kind, rank, idx, std, mode, seed=None):
+    from .workloads import SEED
+    seed = SEED if seed is None else seed
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    out = np.empty(idx.size, dtype=_dtype(mode))
+    rc = _load_host().synth_fill_host_idx(seed, key1(cfg_id, kind, rank), idx.ctypes.data,
+                                          idx.size, scale_for(std), mode, out.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("synth_fill_host_idx failed")
+    return out
+
+
+def dev_fill(out, cfg_id, kind, rank, start, std, mode, seed=None, stream=None):
+    """Fill the contiguous device tensor `out` with value(start + i)."""
+    import torch
+    from .workloads import SEED
+    seed = SEED if seed is None else seed
+    want = torch.uint16 if mode == MODE_BF16 else torch.float32
+    if out.dtype != want or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("dev_fill needs a contiguous device tensor of the mode's dtype")
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    rc = _load_dev().synth_fill_dev(seed, key1(cfg_id, kind, rank), start, out.numel(),
+                                    scale_for(std), mode, out.data_ptr(), s)
+    if rc != 0:
+        raise RuntimeError(f"synth_fill_dev failed ({rc})")
+    return out
+
+
+def dev_copy(src, dst, nbytes, grid=0, stream=None):
+    import torch
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    rc = _load_dev().synth_copy_dev(src.data_ptr(), dst.data_ptr(), nbytes, grid, s)
+    if rc != 0:
+        raise RuntimeError(f"synth_copy_dev failed ({rc})")

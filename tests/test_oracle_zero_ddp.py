@@ -1,0 +1,60 @@
+"""Invariant pins on the composed oracle step: the ZeRO-1/2 shard updates of
+all P owners, concatenated, equal the unsharded DDP update bit for bit, and
+every DDP replica holds the same reduced gradient."""
+import numpy as np
+import pytest
+
+from oracle import pack as opack
+from oracle.layout import ag_read
+from oracle.plan import make_plan
+from oracle.step import ddp_step, zero_step_all_owners
+from synth import workloads as W
+from tests import oracle_inputs as OI
+
+
+@pytest.mark.parametrize("cfg", [0, 5])
+def test_zero_equals_ddp_bitwise(cfg):
+    w = W.by_id(cfg)
+    plan = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    flats = [OI.rank_flat(plan, w, q) for q in range(w.world_size)]
+    th, m, v = OI.full_state(plan, w)
+    z = zero_step_all_owners(plan, flats, th, m, v, w.hp)
+    d = ddp_step(plan, flats, th, m, v, w.hp)
+    for k in range(1, w.world_size):
+        assert np.array_equal(d["replicas"][k].view(np.uint32), d["g"].view(np.uint32))
+    assert z["norm"] == d["norm"] and z["coef"] == d["coef"]
+    assert abs(z["total"] - d["total"]) <= 1e-14 * d["total"]
+    for r in range(w.world_size):
+        assert np.array_equal(z["g"][r].view(np.uint32),
+                              opack.owner_view(plan, d["g"], r).view(np.uint32))
+        for key in ("theta", "m", "v"):
+            assert np.array_equal(z[key][r].view(np.uint32),
+                                  opack.owner_view(plan, d[key], r).view(np.uint32)), key
+        assert np.array_equal(ag_read(plan, r, z["gathered"]), opack.owner_view(plan, d["p"], r))
+    assert np.array_equal(z["gathered"], d["p"])
+    # pads stay exactly zero through the whole step
+    pad = np.ones(plan.flat_len, bool)
+    for t, n in enumerate(plan.numel):
+        pad[plan.tensor_offset[t]:plan.tensor_offset[t] + n] = False
+    assert pad.any()
+    for key in ("g", "theta", "m", "v", "p"):
+        assert not d[key][pad].any()
+    if cfg == 0:
+        assert z["coef"] == 1.0          # small gradients: no clipping
+    else:
+        assert z["coef"] < 0.1           # std 0.1 gradients: clipped hard
+
+
+def test_ring_traffic_zero_matches_ddp_elementwise():
+    """ZeRO-1/2 send the same number of elements as DDP: the reduce-scatter of
+    gradients plus the all-gather of (here bf16) parameters instead of
+    gradients; bytes differ only by the all-gather wire dtype."""
+    w = W.tiny()
+    plan = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    flats = [OI.rank_flat(plan, w, q) for q in range(w.world_size)]
+    from oracle.reduce import ring_allreduce_sim
+    _, rs, ag_fp32 = ring_allreduce_sim(plan, flats, rs_wire_bytes=4, ag_wire_bytes=4)
+    _, _, ag_bf16 = ring_allreduce_sim(plan, flats, rs_wire_bytes=4, ag_wire_bytes=2)
+    P = w.world_size
+    for k in range(P):
+        assert ag_fp32[k] // 4 == ag_bf16[k] // 2 == rs[k] // 4 == (P - 1) * plan.shard_len
