@@ -1,0 +1,18 @@
+"""MI355X (gfx950) data-parallel shard step: bucket pack, ring-order reduce-mean,
+clip-norm partial, fused AdamW with all-gather-layout output.
+
+The work runs in libgsz.so (HIP kernels behind a C ABI, include/gsz.h); this
+package is its ctypes binding and raises ImportError if the library is not
+built.
+"""
+from ._binding import (AdamWHP, GszError, LAYOUT_BUCKET_FLAT, LAYOUT_SHARD_COMPACT, LIB_PATH,
+                       MAX_RANKS, Plan, allgather_layout_write, bucket_pack, clip_coef, load,
+                       ledger_bytes_per_param, make_hp, shard_adamw_step, shard_grad_sqnorm,
+                       shard_reduce_mean, workspace_bytes)
+
+load()
+
+__all__ = ["AdamWHP", "GszError", "LAYOUT_BUCKET_FLAT", "LAYOUT_SHARD_COMPACT", "LIB_PATH",
+           "MAX_RANKS", "Plan", "allgather_layout_write", "bucket_pack", "clip_coef",
+           "ledger_bytes_per_param", "make_hp", "shard_adamw_step", "shard_grad_sqnorm",
+           "shard_reduce_mean", "workspace_bytes"]

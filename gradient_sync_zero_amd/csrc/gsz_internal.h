@@ -1,0 +1,56 @@
+// Internal declarations shared by the planner, the C-ABI layer and the kernels.
+#pragma once
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "gsz.h"
+
+namespace gsz {
+
+// Elements per pack tile; a tile is the unit a block copies at a time.
+constexpr int64_t kPackTile = 8192;
+// Tensor pointers per pack launch (they travel in the kernel argument block).
+constexpr int kPackBatch = 256;
+// Upper bound on blocks of the reduction kernels (sizes the caller's workspace).
+constexpr int kMaxRedBlocks = 4096;
+
+struct Bucket {
+    int32_t first_tensor;  // forward index of the first tensor in bucket order
+    int32_t n_tensors;
+    int64_t base, n, padded, chunk, shard_off;
+};
+
+void set_error(const char* fmt, ...);
+
+}  // namespace gsz
+
+struct gsz_plan {
+    std::vector<int64_t> numel;          // forward order
+    int32_t P = 1, align = 64;
+    int64_t cap = 0;
+    std::vector<gsz::Bucket> buckets;
+    std::vector<int64_t> tensor_off;     // forward index -> flat offset
+    std::vector<int32_t> tensor_bucket;  // forward index -> bucket
+    int64_t flat_len = 0, shard_len = 0, n_params = 0, total_pad = 0;
+    uint64_t hash = 0;
+
+    // Host copies of the device tables.
+    // seg: (B+1) rows of {shard_off, base, chunk}; the last row is {S, 0, 0}.
+    std::vector<int64_t> seg;
+    // pack: per bucket-order position k (tensor T-1-k): {dst offset, numel, tile_begin};
+    // then one sentinel row {0, 0, total tiles}.
+    std::vector<int64_t> pack;
+    // pads: per padded bucket {start, length}.
+    std::vector<int64_t> pads;
+
+    // Device tables (one allocation) and the device they live on.
+    std::mutex mu;
+    int device = -1;
+    void* dev_mem = nullptr;
+    const int64_t* d_seg = nullptr;
+    const int64_t* d_pack = nullptr;
+    const int64_t* d_pads = nullptr;
+};

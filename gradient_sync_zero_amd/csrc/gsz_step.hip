@@ -1,0 +1,672 @@
+// gfx950 kernels of the shard step and the device half of the C ABI.
+//
+// Every kernel here is HBM-bound streaming work (no contraction, so no MFMA):
+// 16-byte loads and stores per lane, 64-wide wavefronts, 256-thread blocks,
+// grid sized to the CU count, fixed-order fp64 reductions (wave shuffles, then
+// LDS, then one finalize block) so results are bit-reproducible run to run.
+//
+// Pages cited (title, section): see gsz.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "gsz_internal.h"
+
+#pragma clang fp contract(off)
+
+using gsz::set_error;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kBlocksPerCU = 8;
+
+struct RankPtrs { const uint16_t* p[GSZ_MAX_RANKS]; };
+struct PackPtrs { const uint16_t* p[gsz::kPackBatch]; };
+
+// fp32 constants of the AdamW update, each rounded once from double on the host.
+struct AdamScalars { float b1, omb1, b2, omb2, bc1, bc2, lr, eps, decay; };
+
+// ----------------------------------------------------------- device utils --
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ f32x4 ldf4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void stf4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+__device__ __forceinline__ void widen8(u32x4 w, float a[8]) {
+    a[0] = bf16_lo(w.x); a[1] = bf16_hi(w.x); a[2] = bf16_lo(w.y); a[3] = bf16_hi(w.y);
+    a[4] = bf16_lo(w.z); a[5] = bf16_hi(w.z); a[6] = bf16_lo(w.w); a[7] = bf16_hi(w.w);
+}
+
+// a[j] = a[j] + widen(w)[j]: one IEEE fp32 add per element, partial sum on the left.
+__device__ __forceinline__ void add8(u32x4 w, float a[8]) {
+    a[0] = a[0] + bf16_lo(w.x); a[1] = a[1] + bf16_hi(w.x);
+    a[2] = a[2] + bf16_lo(w.y); a[3] = a[3] + bf16_hi(w.y);
+    a[4] = a[4] + bf16_lo(w.z); a[5] = a[5] + bf16_hi(w.z);
+    a[6] = a[6] + bf16_lo(w.w); a[7] = a[7] + bf16_hi(w.w);
+}
+
+// Sum over the block in a fixed order; the result is valid in thread 0.
+__device__ double block_sum(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = x + __shfl_xor(x, o, 64);
+    __shared__ double part[kBlock / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < kBlock / 64; ++k) s = s + part[k];
+    }
+    return s;
+}
+
+// Walks the bucket segments of a shard in increasing order.  seg rows are
+// {shard_off, base, chunk}; row nseg is {S, 0, 0}.  For shard index i in bucket
+// b, the all-gather / flat position is i + delta with
+// delta = base_b + owner*C_b - shard_off_b.
+struct SegCursor {
+    const int64_t* seg;
+    int64_t owner, end, delta;
+    int b;
+    __device__ void seek(int64_t i, int nseg) {
+        int lo = 0, hi = nseg - 1;          // largest b with shard_off[b] <= i
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seg[3 * mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        load();
+    }
+    __device__ void load() {
+        end = seg[3 * (b + 1)];
+        delta = seg[3 * b + 1] + owner * seg[3 * b + 2] - seg[3 * b];
+    }
+    __device__ __forceinline__ int64_t map(int64_t i) {
+        while (i >= end) { ++b; load(); }
+        return i + delta;
+    }
+};
+
+// ------------------------------------------------------------------ pack --
+
+// Copies the tensors of one batch (bucket-order positions [k0, k0+nk)) into the
+// flat buffer.  tab rows: {dst offset, numel, first tile}; each block takes a
+// contiguous range of the batch's tiles [t_begin, t_end).
+__global__ __launch_bounds__(kBlock) void k_pack(PackPtrs pp, const int64_t* __restrict__ tab,
+                                                 int k0, int nk, int64_t t_begin, int64_t t_end,
+                                                 uint16_t* __restrict__ flat) {
+    const int64_t ntiles = t_end - t_begin;
+    const int64_t per = (ntiles + gridDim.x - 1) / gridDim.x;
+    int64_t tile = t_begin + (int64_t)blockIdx.x * per;
+    const int64_t stop = tile + per < t_end ? tile + per : t_end;
+    if (tile >= stop) return;
+    int lo = k0, hi = k0 + nk - 1;          // largest k with first_tile[k] <= tile
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tab[3 * mid + 2] <= tile) lo = mid; else hi = mid - 1;
+    }
+    int k = lo;
+    const int tid = threadIdx.x;
+    for (; tile < stop; ++tile) {
+        while (tab[3 * (k + 1) + 2] <= tile) ++k;
+        const int64_t n = tab[3 * k + 1];
+        const int64_t j0 = (tile - tab[3 * k + 2]) * gsz::kPackTile;
+        const int64_t j1 = j0 + gsz::kPackTile < n ? j0 + gsz::kPackTile : n;
+        const uint16_t* __restrict__ src = pp.p[k - k0];
+        uint16_t* __restrict__ dst = flat + tab[3 * k];
+        const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+        if (vec && j1 - j0 == gsz::kPackTile) {
+            constexpr int U = gsz::kPackTile / (8 * kBlock);
+            u32x4 w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) w[u] = ld16(src + j0 + 8 * (tid + u * kBlock));
+#pragma unroll
+            for (int u = 0; u < U; ++u) st16(dst + j0 + 8 * (tid + u * kBlock), w[u]);
+        } else if (vec) {
+            const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
+            for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kBlock) st16(dst + j, ld16(src + j));
+            for (int64_t j = jv + tid; j < j1; j += kBlock) dst[j] = src[j];
+        } else {
+            for (int64_t j = j0 + tid; j < j1; j += kBlock) dst[j] = src[j];
+        }
+    }
+}
+
+// Zeroes the padding at the end of each padded bucket; one block per bucket.
+__global__ __launch_bounds__(kBlock) void k_zero_pads(const int64_t* __restrict__ pads,
+                                                      uint16_t* __restrict__ flat) {
+    const int64_t s = pads[2 * blockIdx.x], n = pads[2 * blockIdx.x + 1];
+    for (int64_t j = threadIdx.x; j < n; j += kBlock) flat[s + j] = 0;
+}
+
+// ---------------------------------------------------------- reduce-mean --
+
+// g[i] = (((c0 + c1) + c2) + ... + c_{P-1}) / P with rp.p[k] = contribution of
+// rank (owner+1+k) mod P, so the owner's own value is added last.  Each lane
+// handles 8 consecutive shard elements per iteration (one 16-byte load per
+// rank).  PS > 0 fixes P at compile time; loads are issued in groups of up to
+// 16 ranks before their adds so many 16-byte requests are in flight.
+template <int PS, bool NORM, bool FLAT>
+__global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
+                                                        const int64_t* __restrict__ seg, int nseg,
+                                                        int64_t owner, int64_t nvec,
+                                                        float* __restrict__ g,
+                                                        double* __restrict__ ws) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    double sq = 0.0;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    if (FLAT && v < nvec) cur.seek(v * 8, nseg);
+    const float fP = (float)P;
+    for (; v < nvec; v += stride) {
+        const int64_t i = v * 8;
+        const int64_t off = FLAT ? cur.map(i) : i;
+        float a[8];
+        if constexpr (PS > 0) {
+            constexpr int G = PS < 16 ? PS : 16;
+#pragma unroll
+            for (int k0 = 0; k0 < PS; k0 += G) {
+                u32x4 w[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) w[j] = ld16(rp.p[k0 + j] + off);
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if (k0 + j == 0) widen8(w[j], a); else add8(w[j], a);
+                }
+            }
+        } else {
+            widen8(ld16(rp.p[0] + off), a);
+            int k = 1;
+            for (; k + 8 <= P; k += 8) {
+                u32x4 w[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) w[j] = ld16(rp.p[k + j] + off);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) add8(w[j], a);
+            }
+            for (; k < P; ++k) add8(ld16(rp.p[k] + off), a);
+        }
+        if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = a[j] * invP;   // exact: invP is a power of two
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = a[j] / fP;
+        }
+        stf4(g + i, f32x4{a[0], a[1], a[2], a[3]});
+        stf4(g + i + 4, f32x4{a[4], a[5], a[6], a[7]});
+        if (NORM) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double d = (double)a[j];
+                sq = __fma_rn(d, d, sq);                        // d*d is exact in fp64
+            }
+        }
+    }
+    if (NORM) {
+        const double s = block_sum(sq);
+        if (threadIdx.x == 0) ws[blockIdx.x] = s;
+    }
+}
+
+// Standalone squared norm of n fp32 values (16-byte aligned).
+__global__ __launch_bounds__(kBlock) void k_sqnorm(const float* __restrict__ g, int64_t n,
+                                                   double* __restrict__ ws) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t tid = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t n4 = n / 4;
+    double sq = 0.0;
+    for (int64_t v = tid; v < n4; v += stride) {
+        const f32x4 x = ldf4(g + 4 * v);
+        const double d0 = x.x, d1 = x.y, d2 = x.z, d3 = x.w;
+        sq = __fma_rn(d0, d0, sq); sq = __fma_rn(d1, d1, sq);
+        sq = __fma_rn(d2, d2, sq); sq = __fma_rn(d3, d3, sq);
+    }
+    if (tid < n - 4 * n4) {
+        const double d = g[4 * n4 + tid];
+        sq = __fma_rn(d, d, sq);
+    }
+    const double s = block_sum(sq);
+    if (threadIdx.x == 0) ws[blockIdx.x] = s;
+}
+
+// out = sum of the n block partials, in block order, one block.
+__global__ __launch_bounds__(kBlock) void k_finalize(const double* __restrict__ ws, int n,
+                                                     double* __restrict__ out) {
+    double s = 0.0;
+    for (int k = threadIdx.x; k < n; k += kBlock) s = s + ws[k];
+    s = block_sum(s);
+    if (threadIdx.x == 0) *out = s;
+}
+
+// total = partials[0] + ... + partials[n-1] (rank order); norm = fp32(sqrt(total));
+// coef = min(1, max_norm / (norm + 1e-6)); NaN propagates.
+__global__ void k_clip(const double* __restrict__ partials, int n, float max_norm,
+                       float* __restrict__ coef, float* __restrict__ norm,
+                       double* __restrict__ total) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    double t = 0.0;
+    for (int q = 0; q < n; ++q) t = t + partials[q];
+    const float nr = (float)sqrt(t);
+    const float c = max_norm / (nr + 1e-6f);
+    *coef = (c != c) ? c : (c < 1.0f ? c : 1.0f);
+    if (norm) *norm = nr;
+    if (total) *total = t;
+}
+
+// ----------------------------------------------------------------- AdamW --
+
+__device__ __forceinline__ void adamw1(float& th, float& mm, float& vv, float gg, float coef,
+                                       const AdamScalars& s) {
+    const float gc = gg * coef;
+    const float m1 = (s.b1 * mm) + (s.omb1 * gc);
+    const float v1 = (s.b2 * vv) + (s.omb2 * (gc * gc));
+    const float mh = m1 / s.bc1;
+    const float vh = v1 / s.bc2;
+    const float u = mh / (sqrtf(vh) + s.eps);
+    th = (th * s.decay) - (s.lr * u);
+    mm = m1;
+    vv = v1;
+}
+
+template <bool GATH, bool SHARD>
+__global__ __launch_bounds__(kBlock) void k_adamw(float* __restrict__ master, float* __restrict__ m,
+                                                  float* __restrict__ v, const float* __restrict__ g,
+                                                  const float* __restrict__ coefp, AdamScalars s,
+                                                  const int64_t* __restrict__ seg, int nseg,
+                                                  int64_t owner, int64_t nvec,
+                                                  uint16_t* __restrict__ gathered,
+                                                  uint16_t* __restrict__ shard_bf16) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int64_t vi = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const float coef = *coefp;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    if (GATH && vi < nvec) cur.seek(vi * 8, nseg);
+    for (; vi < nvec; vi += stride) {
+        const int64_t i = vi * 8;
+        const f32x4 g0 = ldf4(g + i), g1 = ldf4(g + i + 4);
+        f32x4 t0 = ldf4(master + i), t1 = ldf4(master + i + 4);
+        f32x4 m0 = ldf4(m + i), m1 = ldf4(m + i + 4);
+        f32x4 v0 = ldf4(v + i), v1 = ldf4(v + i + 4);
+        float th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) adamw1(th[j], mm[j], vv[j], gg[j], coef, s);
+        stf4(master + i, f32x4{th[0], th[1], th[2], th[3]});
+        stf4(master + i + 4, f32x4{th[4], th[5], th[6], th[7]});
+        stf4(m + i, f32x4{mm[0], mm[1], mm[2], mm[3]});
+        stf4(m + i + 4, f32x4{mm[4], mm[5], mm[6], mm[7]});
+        stf4(v + i, f32x4{vv[0], vv[1], vv[2], vv[3]});
+        stf4(v + i + 4, f32x4{vv[4], vv[5], vv[6], vv[7]});
+        const u32x4 p = u32x4{bf16_rne(th[0]) | (bf16_rne(th[1]) << 16),
+                              bf16_rne(th[2]) | (bf16_rne(th[3]) << 16),
+                              bf16_rne(th[4]) | (bf16_rne(th[5]) << 16),
+                              bf16_rne(th[6]) | (bf16_rne(th[7]) << 16)};
+        if (GATH) st16(gathered + cur.map(i), p);
+        if (SHARD) st16(shard_bf16 + i, p);
+    }
+}
+
+// gathered[i + delta_b] = shard[i] for shard index i of bucket b.
+__global__ __launch_bounds__(kBlock) void k_ag_write(const uint16_t* __restrict__ shard,
+                                                     const int64_t* __restrict__ seg, int nseg,
+                                                     int64_t owner, int64_t nvec,
+                                                     uint16_t* __restrict__ gathered) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    if (v < nvec) cur.seek(v * 8, nseg);
+    for (; v < nvec; v += stride) {
+        const int64_t i = v * 8;
+        st16(gathered + cur.map(i), ld16(shard + i));
+    }
+}
+
+// ------------------------------------------------------------ host side --
+
+std::atomic<int> g_dev_state[64];   // 0 unknown, 1 gfx950, -1 other
+std::atomic<int> g_dev_cus[64];
+
+int hip_fail(const char* what, hipError_t e) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return GSZ_ERR_HIP;
+}
+
+// Current device, checked to be gfx950; *cus receives its compute-unit count.
+int current_device(int* dev_out, int* cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev < 0 || dev >= 64) { set_error("device index %d unsupported", dev); return GSZ_ERR_DEVICE; }
+    int st = g_dev_state[dev].load();
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_dev_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256);
+        g_dev_state[dev].store(st);
+    }
+    if (st != 1) { set_error("device %d is not gfx950 (MI355X); this library targets gfx950 only", dev); return GSZ_ERR_DEVICE; }
+    *dev_out = dev;
+    if (cus) *cus = g_dev_cus[dev].load();
+    return GSZ_OK;
+}
+
+// Blocks for a grid-stride kernel over work_items lanes: enough to fill every
+// CU kBlocksPerCU times, never more than the reduction workspace holds.
+int grid_for(int64_t work_items, int cus) {
+    int64_t want = (work_items + kBlock - 1) / kBlock;
+    int64_t cap = (int64_t)cus * kBlocksPerCU;
+    if (cap > gsz::kMaxRedBlocks) cap = gsz::kMaxRedBlocks;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    return (int)want;
+}
+
+int launched(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(what, e);
+    return GSZ_OK;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+// Checks a plan for a device call: uploaded to the current device, vector granule.
+int check_plan(const gsz_plan* p, const char* who, int* cus) {
+    if (!p) { set_error("%s: NULL plan", who); return GSZ_ERR_INVALID_ARG; }
+    int dev = 0;
+    int rc = current_device(&dev, cus);
+    if (rc) return rc;
+    if (!p->dev_mem || p->device != dev) {
+        set_error("%s: plan has no device tables on device %d (call gsz_plan_upload)", who, dev);
+        return GSZ_ERR_NOT_UPLOADED;
+    }
+    if (p->align % 8 != 0) {
+        set_error("%s: device calls need align a multiple of 8 elements (plan has %d)", who, p->align);
+        return GSZ_ERR_INVALID_ARG;
+    }
+    return GSZ_OK;
+}
+
+int check_owner(const gsz_plan* p, int32_t owner, const char* who) {
+    if (owner < 0 || owner >= p->P) {
+        set_error("%s: owner %d outside [0, %d)", who, owner, p->P);
+        return GSZ_ERR_BAD_RANK;
+    }
+    return GSZ_OK;
+}
+
+template <int PS>
+void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPtrs& rp, int P,
+                   float invP, int pow2, const int64_t* seg, int nseg, int64_t owner, int64_t nvec,
+                   float* g, double* ws) {
+    if (norm && flat)
+        hipLaunchKernelGGL((k_reduce_mean<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+    else if (norm)
+        hipLaunchKernelGGL((k_reduce_mean<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+    else if (flat)
+        hipLaunchKernelGGL((k_reduce_mean<PS, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+    else
+        hipLaunchKernelGGL((k_reduce_mean<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI --
+
+extern "C" int gsz_plan_destroy(gsz_plan* p) {
+    if (!p) return GSZ_OK;
+    if (p->dev_mem) {
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(p->device) == hipSuccess) {
+            (void)hipFree(p->dev_mem);
+            (void)hipSetDevice(cur);
+        }
+    }
+    delete p;
+    return GSZ_OK;
+}
+
+extern "C" int gsz_plan_upload(gsz_plan* p) {
+    if (!p) { set_error("gsz_plan_upload: NULL plan"); return GSZ_ERR_INVALID_ARG; }
+    int dev = 0;
+    int rc = current_device(&dev, nullptr);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lock(p->mu);
+    if (p->dev_mem && p->device == dev) return GSZ_OK;
+    if (p->dev_mem) {
+        hipError_t e = hipSetDevice(p->device);
+        if (e == hipSuccess) e = hipFree(p->dev_mem);
+        (void)hipSetDevice(dev);
+        if (e != hipSuccess) return hip_fail("gsz_plan_upload: freeing old tables", e);
+        p->dev_mem = nullptr;
+        p->device = -1;
+    }
+    const size_t n_seg = p->seg.size(), n_pack = p->pack.size(), n_pads = p->pads.size();
+    const size_t bytes = (n_seg + n_pack + n_pads + 2) * sizeof(int64_t);
+    void* mem = nullptr;
+    hipError_t e = hipMalloc(&mem, bytes);
+    if (e != hipSuccess) return hip_fail("gsz_plan_upload: hipMalloc", e);
+    int64_t* d = static_cast<int64_t*>(mem);
+    std::vector<int64_t> img;
+    img.reserve(n_seg + n_pack + n_pads + 2);
+    img.insert(img.end(), p->seg.begin(), p->seg.end());
+    img.insert(img.end(), p->pack.begin(), p->pack.end());
+    img.insert(img.end(), p->pads.begin(), p->pads.end());
+    img.resize(img.size() + 2, 0);
+    e = hipMemcpy(mem, img.data(), img.size() * sizeof(int64_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) { (void)hipFree(mem); return hip_fail("gsz_plan_upload: hipMemcpy", e); }
+    p->dev_mem = mem;
+    p->device = dev;
+    p->d_seg = d;
+    p->d_pack = d + n_seg;
+    p->d_pads = d + n_seg + n_pack;
+    return GSZ_OK;
+}
+
+extern "C" int gsz_bucket_pack(const gsz_plan* p, const uint16_t* const* grads, uint16_t* flat,
+                               hipStream_t stream) {
+    int cus = 0;
+    int rc = check_plan(p, "gsz_bucket_pack", &cus);
+    if (rc) return rc;
+    const int T = (int)p->numel.size();
+    if (p->flat_len == 0) return GSZ_OK;
+    if (!flat || (T > 0 && !grads)) { set_error("gsz_bucket_pack: NULL buffer"); return GSZ_ERR_INVALID_ARG; }
+    if (misaligned(flat)) { set_error("gsz_bucket_pack: flat is not 16-byte aligned"); return GSZ_ERR_MISALIGNED; }
+    for (int t = 0; t < T; ++t)
+        if (p->numel[t] > 0 && !grads[t]) {
+            set_error("gsz_bucket_pack: gradient pointer %d is NULL", t); return GSZ_ERR_INVALID_ARG;
+        }
+    for (int k0 = 0; k0 < T; k0 += gsz::kPackBatch) {
+        const int nk = T - k0 < gsz::kPackBatch ? T - k0 : gsz::kPackBatch;
+        PackPtrs pp{};
+        for (int k = 0; k < nk; ++k) pp.p[k] = grads[T - 1 - (k0 + k)];
+        const int64_t tb = p->pack[3 * k0 + 2], te = p->pack[3 * (k0 + nk) + 2];
+        if (te == tb) continue;
+        const int64_t cap = (int64_t)cus * kBlocksPerCU;
+        const int grid = (int)(te - tb < cap ? te - tb : cap);
+        hipLaunchKernelGGL(k_pack, dim3(grid), dim3(kBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, flat);
+        if ((rc = launched("gsz_bucket_pack"))) return rc;
+    }
+    const int npad = (int)(p->pads.size() / 2);
+    if (npad > 0) {
+        hipLaunchKernelGGL(k_zero_pads, dim3(npad), dim3(kBlock), 0, stream, p->d_pads, flat);
+        if ((rc = launched("gsz_bucket_pack (pads)"))) return rc;
+    }
+    return GSZ_OK;
+}
+
+extern "C" int gsz_shard_reduce_mean(const gsz_plan* p, int32_t owner,
+                                     const uint16_t* const* contrib, int32_t layout, float* g,
+                                     double* partial_out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    const char* who = "gsz_shard_reduce_mean";
+    int cus = 0;
+    int rc = check_plan(p, who, &cus);
+    if (rc) return rc;
+    if ((rc = check_owner(p, owner, who))) return rc;
+    if (layout != GSZ_LAYOUT_BUCKET_FLAT && layout != GSZ_LAYOUT_SHARD_COMPACT) {
+        set_error("%s: unknown layout %d", who, layout); return GSZ_ERR_INVALID_ARG;
+    }
+    const int P = p->P;
+    const int64_t S = p->shard_len;
+    if (partial_out) {
+        size_t need = 0;
+        gsz_workspace_bytes(&need);
+        if (!ws || ws_bytes < need) { set_error("%s: workspace of %zu bytes required", who, need); return GSZ_ERR_SIZE; }
+        if (misaligned(ws)) { set_error("%s: workspace is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED; }
+    }
+    if (S > 0) {
+        if (!g || !contrib) { set_error("%s: NULL buffer", who); return GSZ_ERR_INVALID_ARG; }
+        if (misaligned(g)) { set_error("%s: g is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED; }
+        for (int q = 0; q < P; ++q) {
+            if (!contrib[q]) { set_error("%s: contribution %d is NULL", who, q); return GSZ_ERR_INVALID_ARG; }
+            if (misaligned(contrib[q])) { set_error("%s: contribution %d is not 16-byte aligned", who, q); return GSZ_ERR_MISALIGNED; }
+        }
+    }
+    const int64_t nvec = S / 8;
+    const int grid = grid_for(nvec, cus);
+    if (S > 0) {
+        RankPtrs rp{};
+        for (int k = 0; k < P; ++k) rp.p[k] = contrib[(owner + 1 + k) % P];
+        const int pow2 = (P & (P - 1)) == 0;
+        const float invP = pow2 ? 1.0f / (float)P : 0.0f;
+        const bool norm = partial_out != nullptr;
+        const bool flat = layout == GSZ_LAYOUT_BUCKET_FLAT;
+        const int nseg = (int)p->buckets.size();
+        double* wsd = static_cast<double*>(ws);
+        const dim3 gr(grid);
+        switch (P) {
+            case 2: launch_reduce<2>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
+            case 4: launch_reduce<4>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
+            case 8: launch_reduce<8>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
+            case 16: launch_reduce<16>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
+            case 32: launch_reduce<32>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
+            case 64: launch_reduce<64>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
+            default: launch_reduce<0>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
+        }
+        if ((rc = launched(who))) return rc;
+    }
+    if (partial_out) {
+        hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kBlock), 0, stream,
+                           static_cast<const double*>(ws), S > 0 ? grid : 0, partial_out);
+        if ((rc = launched(who))) return rc;
+    }
+    return GSZ_OK;
+}
+
+extern "C" int gsz_shard_grad_sqnorm(const float* g, int64_t n, double* partial_out, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+    const char* who = "gsz_shard_grad_sqnorm";
+    int dev = 0, cus = 0;
+    int rc = current_device(&dev, &cus);
+    if (rc) return rc;
+    size_t need = 0;
+    gsz_workspace_bytes(&need);
+    if (n < 0 || !partial_out || (n > 0 && !g)) { set_error("%s: bad arguments", who); return GSZ_ERR_INVALID_ARG; }
+    if (!ws || ws_bytes < need) { set_error("%s: workspace of %zu bytes required", who, need); return GSZ_ERR_SIZE; }
+    if (misaligned(ws) || (n > 0 && misaligned(g))) { set_error("%s: misaligned pointer", who); return GSZ_ERR_MISALIGNED; }
+    int grid = 0;
+    if (n > 0) {
+        grid = grid_for((n + 3) / 4, cus);
+        hipLaunchKernelGGL(k_sqnorm, dim3(grid), dim3(kBlock), 0, stream, g, n, static_cast<double*>(ws));
+        if ((rc = launched(who))) return rc;
+    }
+    hipLaunchKernelGGL(k_finalize, dim3(1), dim3(kBlock), 0, stream, static_cast<const double*>(ws),
+                       grid, partial_out);
+    return launched(who);
+}
+
+extern "C" int gsz_clip_coef(const double* partials, int32_t n_partials, float max_norm,
+                             float* coef_out, float* norm_out, double* total_out,
+                             hipStream_t stream) {
+    const char* who = "gsz_clip_coef";
+    int dev = 0;
+    int rc = current_device(&dev, nullptr);
+    if (rc) return rc;
+    if (n_partials < 0 || (n_partials > 0 && !partials) || !coef_out) {
+        set_error("%s: bad arguments", who); return GSZ_ERR_INVALID_ARG;
+    }
+    hipLaunchKernelGGL(k_clip, dim3(1), dim3(64), 0, stream, partials, n_partials, max_norm,
+                       coef_out, norm_out, total_out);
+    return launched(who);
+}
+
+extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* master, float* m,
+                                    float* v, const float* g, const float* coef,
+                                    const gsz_adamw_hp* hp, uint16_t* gathered,
+                                    uint16_t* shard_bf16, hipStream_t stream) {
+    const char* who = "gsz_shard_adamw_step";
+    int cus = 0;
+    int rc = check_plan(p, who, &cus);
+    if (rc) return rc;
+    if ((rc = check_owner(p, owner, who))) return rc;
+    if (!hp || !coef) { set_error("%s: NULL hyperparameters or coefficient", who); return GSZ_ERR_INVALID_ARG; }
+    if (hp->step < 1) { set_error("%s: step must be >= 1", who); return GSZ_ERR_INVALID_ARG; }
+    if (!gathered && !shard_bf16) { set_error("%s: need gathered and/or shard_bf16 output", who); return GSZ_ERR_INVALID_ARG; }
+    const int64_t S = p->shard_len;
+    if (S == 0) return GSZ_OK;
+    if (!master || !m || !v || !g) { set_error("%s: NULL state buffer", who); return GSZ_ERR_INVALID_ARG; }
+    if (misaligned(master) || misaligned(m) || misaligned(v) || misaligned(g) ||
+        (gathered && misaligned(gathered)) || (shard_bf16 && misaligned(shard_bf16))) {
+        set_error("%s: a buffer is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED;
+    }
+    AdamScalars s;
+    s.b1 = (float)hp->beta1;
+    s.omb1 = (float)(1.0 - hp->beta1);
+    s.b2 = (float)hp->beta2;
+    s.omb2 = (float)(1.0 - hp->beta2);
+    s.bc1 = (float)(1.0 - std::pow(hp->beta1, (double)hp->step));
+    s.bc2 = (float)(1.0 - std::pow(hp->beta2, (double)hp->step));
+    s.lr = (float)hp->lr;
+    s.eps = (float)hp->eps;
+    s.decay = (float)(1.0 - hp->lr * hp->weight_decay);
+    const int64_t nvec = S / 8;
+    const dim3 grid(grid_for(nvec, cus));
+    const int nseg = (int)p->buckets.size();
+    if (gathered && shard_bf16)
+        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, nvec, gathered, shard_bf16);
+    else if (gathered)
+        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, nvec, gathered, shard_bf16);
+    else
+        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, nvec, gathered, shard_bf16);
+    return launched(who);
+}
+
+extern "C" int gsz_allgather_layout_write(const gsz_plan* p, int32_t owner,
+                                          const uint16_t* shard_bf16, uint16_t* gathered,
+                                          hipStream_t stream) {
+    const char* who = "gsz_allgather_layout_write";
+    int cus = 0;
+    int rc = check_plan(p, who, &cus);
+    if (rc) return rc;
+    if ((rc = check_owner(p, owner, who))) return rc;
+    const int64_t S = p->shard_len;
+    if (S == 0) return GSZ_OK;
+    if (!shard_bf16 || !gathered) { set_error("%s: NULL buffer", who); return GSZ_ERR_INVALID_ARG; }
+    if (misaligned(shard_bf16) || misaligned(gathered)) { set_error("%s: misaligned buffer", who); return GSZ_ERR_MISALIGNED; }
+    const int64_t nvec = S / 8;
+    hipLaunchKernelGGL(k_ag_write, dim3(grid_for(nvec, cus)), dim3(kBlock), 0, stream, shard_bf16,
+                       p->d_seg, (int)p->buckets.size(), (int64_t)owner, nvec, gathered);
+    return launched(who);
+}

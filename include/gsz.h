@@ -1,0 +1,238 @@
+/*
+ * gsz.h -- C ABI of libgsz: one rank's share of a synchronous data-parallel
+ * training step with ZeRO-1/2 sharding, on one AMD Instinct MI355X (gfx950).
+ *
+ * The step, as the pages on data-parallel gradient synchronisation state it:
+ *   1. pack per-parameter bf16 gradients into ~25 MB buckets in reverse layer
+ *      order                                          (gsz_bucket_pack)
+ *   2. the reduce-scatter half of a ring all-reduce: the fp32 mean of P rank
+ *      contributions for the chunks this rank owns   (gsz_shard_reduce_mean)
+ *   3. the squared-norm partial of the owned shard and the clip coefficient
+ *      for clipping the global norm at max_norm     (gsz_shard_grad_sqnorm,
+ *                                                    gsz_clip_coef)
+ *   4. AdamW on the owned shard (fp32 master, m, v) writing bf16 parameters
+ *      in all-gather layout                         (gsz_shard_adamw_step,
+ *                                                    gsz_allgather_layout_write)
+ *
+ * Pages cited (title, section):
+ *   "Data parallelism in depth" (infra-guide chapter 4.1)
+ *   "Distributed Training: Data Parallel, Model Parallel and FSDP Strategies"
+ *   "Data Parallelism: DDP, ZeRO and FSDP"
+ *   "Data Parallelism: From Parameter Server to Ring All-Reduce"
+ *
+ * Conventions for every call:
+ *   - Return value: GSZ_OK (0) or a negative gsz_status.  On error nothing
+ *     is enqueued and gsz_last_error() (thread-local) describes the failure.
+ *     Arguments are validated before any work is enqueued.
+ *   - Sizes are int64_t element counts.  bf16 values travel as uint16_t bit
+ *     patterns.
+ *   - "device" pointers are HIP device memory owned by the caller; "host"
+ *     pointers are ordinary host memory read during the call only.  Device
+ *     vector pointers must be 16-byte aligned (GSZ_ERR_MISALIGNED otherwise).
+ *   - Device work is enqueued on the caller's hipStream_t (0 = the null
+ *     stream) and is asynchronous; no call synchronises the host except
+ *     gsz_plan_upload.
+ *   - The library allocates device memory only in gsz_plan_upload (the plan's
+ *     device tables, freed by gsz_plan_destroy).  Scratch space comes from the
+ *     caller (gsz_workspace_bytes).
+ *   - Device calls refuse any device that is not gfx950 (GSZ_ERR_DEVICE).
+ */
+#ifndef GSZ_H
+#define GSZ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gsz_status {
+    GSZ_OK = 0,
+    GSZ_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad enum ...     */
+    GSZ_ERR_MISALIGNED = -2,    /* a device pointer is not 16-byte aligned        */
+    GSZ_ERR_SIZE = -3,          /* sizes disagree with the plan or a limit         */
+    GSZ_ERR_BAD_RANK = -4,      /* owner rank outside [0, world_size)              */
+    GSZ_ERR_PLAN_MISMATCH = -5, /* two ranks built different bucket plans          */
+    GSZ_ERR_NOT_UPLOADED = -6,  /* plan has no device tables on the current device */
+    GSZ_ERR_DEVICE = -7,        /* current device is not gfx950                    */
+    GSZ_ERR_HIP = -8,           /* a HIP runtime call failed (text in last_error)  */
+    GSZ_ERR_NO_MEMORY = -9      /* host allocation failed                          */
+} gsz_status;
+
+/* Largest number of simulated ranks one call accepts (contribution pointers
+ * travel in the kernel argument block). */
+#define GSZ_MAX_RANKS 256
+
+/* Contribution layouts for gsz_shard_reduce_mean. */
+#define GSZ_LAYOUT_BUCKET_FLAT 0    /* contrib[q]: rank q's whole bucket-major flat
+                                       buffer (flat_len elements); the owner's chunk
+                                       of bucket b is read at base_b + owner*C_b     */
+#define GSZ_LAYOUT_SHARD_COMPACT 1  /* contrib[q]: the shard_len elements rank q
+                                       sends to this owner, chunks in bucket order   */
+
+typedef struct gsz_plan gsz_plan;
+
+typedef struct gsz_plan_info {
+    int32_t n_tensors;
+    int32_t n_buckets;
+    int32_t world_size;        /* P */
+    int32_t align;             /* padding granule per rank, elements */
+    int64_t bucket_cap_bytes;
+    int64_t flat_len;          /* sum of padded bucket lengths */
+    int64_t shard_len;         /* S = flat_len / P */
+    int64_t n_params;          /* sum of tensor sizes */
+    uint64_t hash;             /* FNV-1a 64 of the plan's canonical description */
+} gsz_plan_info;
+
+typedef struct gsz_bucket_info {
+    int32_t first_tensor;      /* forward index of the bucket's first tensor; the
+                                  bucket holds first_tensor, first_tensor-1, ...  */
+    int32_t n_tensors;
+    int64_t base;              /* flat offset of the bucket */
+    int64_t n_elems;           /* gradient elements before padding */
+    int64_t padded;            /* L_b, a multiple of world_size * align */
+    int64_t chunk;             /* C_b = L_b / world_size */
+    int64_t shard_off;         /* offset of this bucket's chunk inside every shard */
+} gsz_bucket_info;
+
+typedef struct gsz_adamw_hp {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+    int64_t step;              /* t >= 1: the exponent of this update's bias corrections */
+} gsz_adamw_hp;
+
+/* ---------------------------------------------------------------- plan --- */
+
+/* Builds the bucket plan ("Data parallelism in depth" §4.2, The Bucket
+ * mechanism; "Data Parallelism: DDP, ZeRO and FSDP", DDP section; "Data
+ * Parallelism: From Parameter Server to Ring All-Reduce" §5).
+ *   numel[n_tensors] (host): tensor sizes in forward (compute) order.
+ * Tensors are taken in reverse order; each is appended to the open bucket,
+ * which closes as soon as its bf16 byte size reaches bucket_cap_bytes; the
+ * last bucket holds the rest.  A bucket of n elements is zero-padded to
+ * L = ceil(n / (P*align)) * P*align; rank r owns chunk r (length L/P) of every
+ * bucket and its shard is those chunks concatenated in bucket order.
+ * Host only (no device call).  *out receives a plan owned by the caller;
+ * release it with gsz_plan_destroy.  n_tensors may be 0; sizes may be 0. */
+int gsz_plan_create(const int64_t* numel, int32_t n_tensors, int64_t bucket_cap_bytes,
+                    int32_t world_size, int32_t align_elems, gsz_plan** out);
+
+/* Frees the plan and its device tables.  NULL is accepted. */
+int gsz_plan_destroy(gsz_plan* plan);
+
+int gsz_plan_get_info(const gsz_plan* plan, gsz_plan_info* out);
+
+/* Bucket b in bucket order (0 = the bucket holding the last forward tensors). */
+int gsz_plan_bucket(const gsz_plan* plan, int32_t b, gsz_bucket_info* out);
+
+/* Flat offset and bucket of forward tensor t. */
+int gsz_plan_tensor(const gsz_plan* plan, int32_t t, int64_t* flat_offset, int32_t* bucket);
+
+/* Every rank must issue its buckets in the same order ("Data Parallelism:
+ * DDP, ZeRO and FSDP", DDP section; "Data parallelism in depth" §4.2 on
+ * unused parameters).  Compares this plan's hash with a peer's:
+ * GSZ_OK if equal, GSZ_ERR_PLAN_MISMATCH otherwise. */
+int gsz_plan_check(const gsz_plan* plan, uint64_t peer_hash);
+
+/* Copies the plan's device tables to the current device (allocating them
+ * there; the plan owns them) and waits for the copy.  Must precede every
+ * device call that takes this plan, on the device it will run on. */
+int gsz_plan_upload(gsz_plan* plan);
+
+/* ------------------------------------------------------------- ledger --- */
+
+/* Model-state bytes per parameter per rank ("Data Parallelism: DDP, ZeRO and
+ * FSDP", sections The memory ledger and The three stages): zero_stage 0 (DDP)
+ * 16, 1: 4 + 12/P, 2: 2 + 14/P, 3: 16/P. */
+int gsz_ledger_bytes_per_param(int32_t world_size, int32_t zero_stage, double* out);
+
+/* Bytes of device scratch that gsz_shard_reduce_mean and
+ * gsz_shard_grad_sqnorm need (per call in flight).  Needs no initialisation. */
+int gsz_workspace_bytes(size_t* out);
+
+/* -------------------------------------------------------------- steps --- */
+
+/* Step 1: flat[base_b + ...] <- gradients of bucket b in bucket order, zero pads.
+ *   grads (host array of n_tensors device pointers, forward order): tensor t
+ *     holds numel[t] bf16 values; any alignment (unaligned tensors take a
+ *     slower element path); NULL only when numel[t] == 0.
+ *   flat (device, flat_len bf16, 16-byte aligned): written entirely.
+ * Source: "Data parallelism in depth" §4.2; "Distributed Training ...",
+ * section Inside DDP (25 MB buckets, gradient_as_bucket_view). */
+int gsz_bucket_pack(const gsz_plan* plan, const uint16_t* const* grads, uint16_t* flat,
+                    hipStream_t stream);
+
+/* Step 2 (+ the squared-norm partial of step 3 when partial_out != NULL):
+ *   g[i] = (((c[r+1] + c[r+2]) + ...) + c[r]) / P     in fp32, i in [0, S)
+ * with c[q] the bf16 value rank q contributes for element i of owner r's shard
+ * (indices mod P); each addition is an IEEE fp32 add, the division is exact
+ * IEEE division.  This is the reduce-scatter of "Data Parallelism: From
+ * Parameter Server to Ring All-Reduce" §5 (the received chunk is added into
+ * the local partial sum; after N-1 steps the owner holds the reduced chunk),
+ * averaged as in "Data parallelism in depth" §2, accumulated in fp32 as in
+ * "Distributed Training ...", section FSDP1 vs FSDP2 (reduce_dtype=fp32).
+ *   contrib (host array of P device pointers), layout GSZ_LAYOUT_*.
+ *   g (device, S fp32): written.
+ *   partial_out (device, one double, may be NULL): sum of g[i]^2 in fp64.
+ *   ws (device, >= gsz_workspace_bytes): scratch, required if partial_out.
+ * Deterministic: the same inputs give the same bits on the same device. */
+int gsz_shard_reduce_mean(const gsz_plan* plan, int32_t owner,
+                          const uint16_t* const* contrib, int32_t layout,
+                          float* g, double* partial_out, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Step 3, standalone: *partial_out = sum_i g[i]^2 in fp64, i in [0, n)
+ * (device pointers; ws as above).  Clipping at 1.0 by the global L2 norm:
+ * "Distributed Training ...", section Inside DDP (clip_grad_norm_(..., 1.0)). */
+int gsz_shard_grad_sqnorm(const float* g, int64_t n, double* partial_out, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Step 3, finalize (one tiny kernel, no host sync):
+ *   total = partials[0] + partials[1] + ... (fp64, rank order)
+ *   norm  = fp32(sqrt(total));  coef = min(1, max_norm / (norm + 1e-6)) in fp32.
+ *   partials (device, n_partials doubles); coef_out (device float);
+ *   norm_out (device float, may be NULL); total_out (device double, may be NULL). */
+int gsz_clip_coef(const double* partials, int32_t n_partials, float max_norm, float* coef_out,
+                  float* norm_out, double* total_out, hipStream_t stream);
+
+/* Step 4: AdamW on owner r's shard, in place, element by element in fp32 with
+ * one IEEE rounding per operation and no fused multiply-add:
+ *   gc = g*coef; m = b1*m + (1-b1)*gc; v = b2*v + (1-b2)*(gc*gc);
+ *   u = (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps); theta = theta*(1-lr*wd) - lr*u;
+ *   p = bf16(theta) (round to nearest even).
+ * The fp32 constants are formed in double from hp and rounded once.
+ * AdamW(lr=2e-4, weight_decay=0.1): "Distributed Training ...", section
+ * Inside DDP; the owned-shard update and all-gather of updated parameters:
+ * "Data Parallelism: DDP, ZeRO and FSDP", section The three stages.
+ *   master, m, v, g (device, S fp32); coef (device float, from gsz_clip_coef).
+ *   gathered (device, flat_len bf16, may be NULL): p written at
+ *     base_b + r*C_b + j (all-gather layout); other elements untouched.
+ *   shard_bf16 (device, S bf16, may be NULL): p in shard layout.
+ *   At least one of gathered / shard_bf16 must be given. */
+int gsz_shard_adamw_step(const gsz_plan* plan, int32_t owner, float* master, float* m, float* v,
+                         const float* g, const float* coef, const gsz_adamw_hp* hp,
+                         uint16_t* gathered, uint16_t* shard_bf16, hipStream_t stream);
+
+/* All-gather layout writer: gathered[base_b + r*C_b + j] = shard[shard_off_b + j]
+ * for every bucket b ("Data Parallelism: DDP, ZeRO and FSDP", section The three
+ * stages; "Data Parallelism: From Parameter Server to Ring All-Reduce" §5,
+ * all-gather).  shard_bf16 (device, S bf16); gathered (device, flat_len bf16). */
+int gsz_allgather_layout_write(const gsz_plan* plan, int32_t owner, const uint16_t* shard_bf16,
+                               uint16_t* gathered, hipStream_t stream);
+
+/* ------------------------------------------------------------ errors --- */
+
+const char* gsz_last_error(void);
+const char* gsz_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSZ_H */

@@ -10,7 +10,8 @@ shard it owns and the partials are summed.
 Readings: partials are exact squares of fp32 values summed in fp64; the P
 partials are added in rank order; the norm is sqrt in fp64 rounded once to
 fp32; the coefficient is min(1, max_norm / (norm + 1e-6)) in fp32, the form of
-PyTorch's clip_grad_norm_ that the page calls; the gradient is then scaled by
+PyTorch's clip_grad_norm_ that the page calls (a NaN norm gives a NaN
+coefficient, as its clamp does); the gradient is then scaled by
 the coefficient (a multiply by exactly 1 when no clipping happens).
 """
 from __future__ import annotations
@@ -38,5 +39,5 @@ def clip_coef(total_sq: float, max_norm: float = 1.0):
     """Returns (norm32, coef32)."""
     norm32 = np.float32(math.sqrt(total_sq))
     c = np.float32(max_norm) / (norm32 + np.float32(1e-6))
-    coef32 = np.float32(min(np.float32(1.0), np.float32(c)))
+    coef32 = np.minimum(np.float32(1.0), np.float32(c))   # NaN propagates, as in torch.clamp
     return np.float32(norm32), coef32

@@ -62,7 +62,7 @@ __global__ void synth_copy_kernel(const uint4* __restrict__ src, uint4* __restri
 int grid_for(int64_t n, int block) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
     int64_t want = (n + block - 1) / block;
     int64_t cap = (int64_t)cus * 16;
     if (want > cap) want = cap;

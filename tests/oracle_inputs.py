@@ -76,3 +76,29 @@ def values_at(w, kind, rank, std, mode, param_idx):
     if ok.any():
         out[ok] = gen.host_fill_idx(w.cfg_id, kind, rank, param_idx[ok], std, mode)
     return out
+
+
+def param_index_of_flat(plan, flat_pos):
+    """Parameter index (forward-order concatenation) of flat positions; -1 for pads."""
+    flat_pos = np.asarray(flat_pos, dtype=np.int64)
+    order = [t for bk in plan.buckets for t in bk.tensors]      # increasing flat offset
+    offs = np.array([plan.tensor_offset[t] for t in order], dtype=np.int64)
+    ns = np.array([plan.numel[t] for t in order], dtype=np.int64)
+    pre = np.array(prefix(plan.numel), dtype=np.int64)
+    pres = np.array([pre[t] for t in order], dtype=np.int64)
+    k = np.searchsorted(offs, flat_pos, side="right") - 1
+    ok = k >= 0
+    kk = np.where(ok, k, 0)
+    inside = ok & (flat_pos < offs[kk] + ns[kk])
+    return np.where(inside, pres[kk] + (flat_pos - offs[kk]), -1)
+
+
+def flat_pos_of_shard(plan, r, shard_idx):
+    """Flat (and all-gather) position of owner r's shard indices."""
+    shard_idx = np.asarray(shard_idx, dtype=np.int64)
+    so = np.array([bk.shard_off for bk in plan.buckets], dtype=np.int64)
+    base = np.array([bk.base for bk in plan.buckets], dtype=np.int64)
+    ch = np.array([bk.chunk for bk in plan.buckets], dtype=np.int64)
+    # the last bucket whose chunk starts at or before i (empty chunks are skipped)
+    b = np.searchsorted(so, shard_idx, side="right") - 1
+    return base[b] + r * ch[b] + (shard_idx - so[b])

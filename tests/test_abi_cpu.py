@@ -1,0 +1,149 @@
+"""CPU tests of the C ABI: the library loads and exports every symbol the
+header declares; the C++ planner reproduces the oracle's plan exactly; the
+plan hash detects ranks that disagree (failure injection: a rank that skips an
+unused parameter); ledger and argument validation.  No device call is made."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gradient_sync_zero_amd as G
+from oracle import ledger as oledger
+from oracle.plan import make_plan
+from synth import workloads as W
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gsz.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(gsz_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert len(syms) >= 17
+    lib = ctypes.CDLL(G.LIB_PATH)
+    missing = [s for s in syms if not hasattr(lib, s)]
+    assert not missing, missing
+    for s in ("gsz_bucket_pack", "gsz_shard_reduce_mean", "gsz_shard_grad_sqnorm",
+              "gsz_clip_coef", "gsz_shard_adamw_step", "gsz_allgather_layout_write"):
+        assert s in syms
+
+
+def assert_same_plan(cplan, oplan):
+    assert (cplan.flat_len, cplan.shard_len, cplan.n_buckets) == \
+        (oplan.flat_len, oplan.shard_len, len(oplan.buckets))
+    for b, ob in enumerate(oplan.buckets):
+        cb = cplan.bucket(b)
+        tensors = tuple(cb["first_tensor"] - k for k in range(cb["n_tensors"]))
+        assert tensors == ob.tensors
+        assert (cb["base"], cb["n_elems"], cb["padded"], cb["chunk"], cb["shard_off"]) == \
+            (ob.base, ob.n, ob.padded, ob.chunk, ob.shard_off)
+    for t in range(len(oplan.numel)):
+        assert cplan.tensor(t) == (oplan.tensor_offset[t], oplan.tensor_bucket[t])
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_planner_matches_oracle_on_workloads(cfg):
+    w = W.by_id(cfg)
+    c = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    o = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    assert_same_plan(c, o)
+    assert c.n_params == w.n_params
+
+
+def test_planner_matches_oracle_on_random_cases():
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        T = int(rng.integers(0, 40))
+        numel = [int(x) for x in rng.integers(0, 5000, T)]
+        if T and rng.random() < 0.3:
+            numel[int(rng.integers(0, T))] = 0
+        cap = int(rng.integers(1, 20000))
+        P = int(rng.integers(1, 9))
+        align = int(rng.choice([1, 2, 8, 64]))
+        assert_same_plan(G.Plan(numel, cap, P, align), make_plan(numel, cap, P, align))
+
+
+def fnv1a64(values):
+    h = 0xcbf29ce484222325
+    for x in values:
+        for byte in int(x).to_bytes(8, "little", signed=True):
+            h ^= byte
+            h = (h * 0x100000001b3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def test_plan_hash_is_fnv1a_of_the_canonical_description():
+    w = W.tiny()
+    c = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    vals = [w.world_size, 64, w.bucket_cap_bytes, len(w.numel), *w.numel, c.n_buckets]
+    for b in c.buckets():
+        vals += [b["first_tensor"], b["n_tensors"], b["base"], b["n_elems"], b["padded"]]
+    assert c.hash == fnv1a64(vals)
+    assert fnv1a64([]) == 0xcbf29ce484222325
+
+
+def test_plan_mismatch_is_an_error_not_a_hang():
+    w = W.gpt2_small()
+    ranks = [G.Plan(w.numel, w.bucket_cap_bytes, w.world_size) for _ in range(3)]
+    for r in ranks[1:]:
+        ranks[0].check(r.hash)                               # identical plans agree
+    # one rank drops a parameter that took no part in its forward pass
+    skipped = list(w.numel)
+    skipped[5] = 0
+    odd = G.Plan(skipped, w.bucket_cap_bytes, w.world_size)
+    with pytest.raises(G.GszError) as e:
+        ranks[0].check(odd.hash)
+    assert e.value.name == "GSZ_ERR_PLAN_MISMATCH"
+    for variant in (dict(cap=w.bucket_cap_bytes * 2), dict(P=4), dict(align=128)):
+        p = G.Plan(w.numel, variant.get("cap", w.bucket_cap_bytes), variant.get("P", 8),
+                   variant.get("align", 64))
+        with pytest.raises(G.GszError):
+            ranks[0].check(p.hash)
+
+
+def test_ledger_matches_oracle():
+    for P in (1, 2, 8, 64):
+        for st in range(4):
+            assert G.ledger_bytes_per_param(P, st) == oledger.bytes_per_param(P, st)
+    with pytest.raises(G.GszError):
+        G.ledger_bytes_per_param(0, 1)
+    with pytest.raises(G.GszError):
+        G.ledger_bytes_per_param(8, 4)
+
+
+def test_argument_validation():
+    with pytest.raises(G.GszError) as e:
+        G.Plan([1, 2], 100, 0)
+    assert e.value.name == "GSZ_ERR_INVALID_ARG"
+    with pytest.raises(G.GszError):
+        G.Plan([1, -2], 100, 2)
+    with pytest.raises(G.GszError):
+        G.Plan([1], 100, G.MAX_RANKS + 1)
+    p = G.Plan([5], 100, 2)
+    with pytest.raises(G.GszError):
+        p.bucket(1)
+    with pytest.raises(G.GszError):
+        p.tensor(-1)
+    assert G.workspace_bytes() >= 8 * 1024
+    lib = G.load()
+    assert lib.gsz_status_string(-5) == b"plan mismatch"
+    assert lib.gsz_plan_destroy(None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    """The product path has no CPU fallback: host tensors are rejected before
+    any call reaches the library."""
+    import torch
+    w = W.tiny()
+    p = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    grads = [torch.zeros(n, dtype=torch.bfloat16) for n in w.numel]
+    with pytest.raises(ValueError):
+        G.bucket_pack(p, grads, torch.zeros(p.flat_len, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        G.shard_reduce_mean(p, 0, [torch.zeros(p.shard_len, dtype=torch.bfloat16)] * 4,
+                            G.LAYOUT_SHARD_COMPACT, torch.zeros(p.shard_len))

@@ -1,0 +1,140 @@
+"""GPU parity at the full workload sizes (1.3B, 7B share, 70B share), in the
+launch configuration the benchmark times.  The oracle cannot redo a whole
+shard here, so it recomputes sampled elements one by one (random indices plus
+the first and last vectors of every bucket's chunk) from the same seeded
+inputs; the squared-norm partial is checked by a property that holds at any
+size (it equals the fp64 sum of squares of the produced gradient)."""
+import numpy as np
+import pytest
+import torch
+
+import gradient_sync_zero_amd as G
+from oracle.adamw import adamw as o_adamw
+from oracle.plan import make_plan
+from oracle.reduce import reduce_mean as o_reduce
+from synth import gen
+from synth import workloads as W
+from tests import gpu_inputs as GI
+from tests import oracle_inputs as OI
+from tests.parity import assert_bits, host
+
+pytestmark = pytest.mark.gpu
+
+COEF = np.float32(0.0345)       # a clip coefficient chosen by the test (oracle side)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def sample_indices(oplan, n_random, seed):
+    rng = np.random.default_rng(seed)
+    S = oplan.shard_len
+    edges = []
+    for bk in oplan.buckets:
+        if bk.chunk:
+            edges += list(range(bk.shard_off, bk.shard_off + 8))
+            edges += list(range(bk.shard_off + bk.chunk - 8, bk.shard_off + bk.chunk))
+    idx = np.concatenate([rng.integers(0, S, n_random), np.array(edges, np.int64), [0, S - 1]])
+    return np.unique(idx)
+
+
+def gather_dev(t, idx):
+    if t.dtype == torch.uint16:
+        t = t.view(torch.int16)
+        return host(t[torch.from_numpy(idx).cuda()].view(torch.uint16))
+    return host(t[torch.from_numpy(idx).cuda()])
+
+
+@pytest.mark.parametrize("cfg,layout,owners", [
+    (2, G.LAYOUT_BUCKET_FLAT, (0, 7)),
+    (3, G.LAYOUT_BUCKET_FLAT, (0,)),
+    (4, G.LAYOUT_SHARD_COMPACT, (0,)),
+])
+def test_full_size_sampled(cfg, layout, owners):
+    w = W.by_id(cfg)
+    P = w.world_size
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    oplan = make_plan(w.numel, w.bucket_cap_bytes, P)
+    assert plan.shard_len == oplan.shard_len
+    S = plan.shard_len
+    flats = None
+    if layout == G.LAYOUT_BUCKET_FLAT:
+        say(f"[{w.name}] generating and packing {P} ranks x {w.n_params} gradients")
+        buf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+        flats = []
+        for q in range(P):
+            _, views = GI.rank_grads(w, q, buf)
+            flat = torch.empty(plan.flat_len, dtype=torch.uint16, device="cuda")
+            G.bucket_pack(plan, views, flat)
+            flats.append(flat)
+        torch.cuda.synchronize()
+        del buf, views
+        # pack parity on sampled flat positions of every rank
+        rng = np.random.default_rng(cfg)
+        fpos = np.unique(np.concatenate([rng.integers(0, plan.flat_len, 1 << 18),
+                                         [0, plan.flat_len - 1]]))
+        pidx = OI.param_index_of_flat(oplan, fpos)
+        for q in range(P):
+            ref = OI.values_at(w, W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16, pidx)
+            assert_bits(gather_dev(flats[q], fpos), ref, f"pack rank {q} (sampled)")
+
+    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    for r in owners:
+        contribs = flats if flats is not None else None
+        if contribs is None:
+            say(f"[{w.name}] generating {P} shard-compact contributions for owner {r}")
+            contribs = GI.compact_contribs(plan, w, r)
+        say(f"[{w.name}] owner {r}: reduce-mean over {P} ranks, S={S}")
+        g = torch.empty(S, dtype=torch.float32, device="cuda")
+        part = torch.zeros(1, dtype=torch.float64, device="cuda")
+        G.shard_reduce_mean(plan, r, contribs, layout, g, part, ws)
+        torch.cuda.synchronize()
+        if flats is None:
+            del contribs
+            torch.cuda.empty_cache()
+
+        idx = sample_indices(oplan, 1 << 20, 100 + r)
+        fp = OI.flat_pos_of_shard(oplan, r, idx)
+        pidx = OI.param_index_of_flat(oplan, fp)
+        cs = [OI.values_at(w, W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16, pidx) for q in range(P)]
+        g_ref = o_reduce(cs, r)
+        assert_bits(gather_dev(g, idx), g_ref, f"g owner {r} (sampled)")
+
+        # property at full size: the partial is the fp64 sum of squares of g
+        prop = 0.0
+        for c in torch.split(g, 1 << 28):
+            prop += float(torch.sum(c.double() * c.double()))
+        got = float(host(part)[0])
+        assert abs(got - prop) <= 1e-12 * prop, (got, prop)
+
+        say(f"[{w.name}] owner {r}: AdamW with coefficient {COEF}")
+        th, m, v = GI.owner_state(plan, w, r)
+        coef = torch.full((1,), float(COEF), dtype=torch.float32, device="cuda")
+        gathered = shard_out = None
+        if layout == G.LAYOUT_BUCKET_FLAT:
+            gathered = torch.zeros(plan.flat_len, dtype=torch.uint16, device="cuda")
+        else:
+            shard_out = torch.zeros(S, dtype=torch.uint16, device="cuda")
+        G.shard_adamw_step(plan, r, th, m, v, g, coef, w.hp, gathered, shard_out)
+        torch.cuda.synchronize()
+        st = [OI.values_at(w, kind, 0, std, mode, pidx) for kind, std, mode in OI.STATE_KINDS]
+        hp = w.hp
+        t1, m1, v1, p1 = o_adamw(st[0], st[1], st[2], g_ref, COEF, hp.lr, hp.beta1, hp.beta2,
+                                 hp.eps, hp.weight_decay, hp.step)
+        assert_bits(gather_dev(th, idx), t1, f"master owner {r} (sampled)")
+        assert_bits(gather_dev(m, idx), m1, f"m owner {r} (sampled)")
+        assert_bits(gather_dev(v, idx), v1, f"v owner {r} (sampled)")
+        if gathered is not None:
+            assert_bits(gather_dev(gathered, fp), p1, f"bf16 all-gather layout owner {r}")
+        else:
+            assert_bits(gather_dev(shard_out, idx), p1, f"bf16 shard owner {r}")
+        del th, m, v, g, gathered, shard_out
+        torch.cuda.empty_cache()

@@ -50,3 +50,12 @@ def test_clip_special_values():
     assert n == 0.5 and c == 1.0
     n, c = clip_coef(1.0, 1.0)                              # exactly at the threshold: 1/(1+1e-6)
     assert n == 1.0 and c == np.float32(1.0) / (np.float32(1.0) + np.float32(1e-6)) and c < 1
+
+
+def test_clip_propagates_nan_like_torch():
+    n, c = clip_coef(float("nan"), 1.0)
+    assert np.isnan(n) and np.isnan(c)
+    t = torch.nn.Parameter(torch.zeros(2))
+    t.grad = torch.tensor([float("nan"), 1.0])
+    torch.nn.utils.clip_grad_norm_([t], 1.0)
+    assert torch.isnan(t.grad).all()

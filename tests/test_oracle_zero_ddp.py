@@ -58,3 +58,17 @@ def test_ring_traffic_zero_matches_ddp_elementwise():
     P = w.world_size
     for k in range(P):
         assert ag_fp32[k] // 4 == ag_bf16[k] // 2 == rs[k] // 4 == (P - 1) * plan.shard_len
+
+
+def test_sampled_index_helpers_match_full_maps():
+    """The sampled-parity helpers agree with the whole-shard maps."""
+    for cfg in (0, 1):
+        w = W.by_id(cfg)
+        plan = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
+        for r in (0, w.world_size - 1):
+            full = OI.shard_param_index(plan, r)
+            idx = np.arange(plan.shard_len, dtype=np.int64)
+            fp = OI.flat_pos_of_shard(plan, r, idx)
+            assert np.array_equal(OI.param_index_of_flat(plan, fp), full)
+            flat = np.arange(plan.flat_len, dtype=np.int64)
+            assert np.array_equal(opack.owner_view(plan, flat, r), fp)
