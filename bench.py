@@ -1,0 +1,414 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's share of a synchronous data-parallel step on one
+MI355X: bucket pack -> ring-order reduce-mean (+ squared-norm partial) ->
+clip coefficient -> AdamW writing bf16 parameters in all-gather layout.
+
+Workload (default): the 7B Llama-shaped share -- 6,738,415,616 parameters in
+291 tensors, P = 8 simulated ranks, 25 MiB buckets, owner 0's shard of
+842,301,952 elements.  All P ranks' bucket-major gradient buffers are resident
+in HBM; each timed step packs owner 0's per-tensor gradients into its own flat
+buffer, reduces owner 0's chunks over the 8 flat buffers, forms the clip
+coefficient, and updates the shard's fp32 master/m/v in place.
+
+Prints one JSON line (see the fields below).  Only N = 1 is supported: the
+simulated ranks live on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("params/s and achieved HBM GB/s (% of peak) for reduce-mean + AdamW shard step")
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="turn a rocprofv3 kernel_stats.csv into profiles/kernel_stats_<workload>.txt")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) into profiles/traffic_<workload>.txt")
+    ap.add_argument("--command", default="", help="command line recorded in a summary")
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload id (synth.workloads)")
+    ap.add_argument("--owner", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=4.0,
+                    help="size of the plain copy used as the measured HBM ceiling")
+    return ap.parse_args()
+
+
+def ensure_built():
+    need = [os.path.join(ROOT, "gradient_sync_zero_amd", "libgsz.so"),
+            os.path.join(ROOT, "synth", "libsynth_dev.so"),
+            os.path.join(ROOT, "synth", "libsynth_host.so")]
+    if not all(os.path.exists(p) for p in need):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+SHORT = {"k_pack": "k_pack", "k_reduce_mean": "k_reduce_mean", "k_adamw": "k_adamw",
+         "k_clip": "k_clip", "k_finalize": "k_finalize", "k_zero_pads": "k_zero_pads",
+         "synth_copy_kernel": "copy", "synth_fill_kernel": "synth_fill", "k_ag_write": "k_ag_write",
+         "k_sqnorm": "k_sqnorm"}
+
+
+def short_name(full):
+    for k, v in SHORT.items():
+        if k in full:
+            return v
+    if "FillFunctor" in full:
+        return "torch_fill"
+    if "rocclr" in full:
+        return "hip_runtime_copy"
+    return full.split("(")[0][-40:]
+
+
+def summarize_trace(csv_path, workload, command):
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    out = [f"# rocprofv3 kernel statistics: {workload}", "#", f"# command: {command}", "#",
+           f"# {'kernel':<16} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_ms':>10}"]
+    for r in rows:
+        out.append(f"  {short_name(r['Name']):<16} {int(r['Calls']):>6} "
+                   f"{float(r['AverageNs']) / 1e3:>10.1f} {float(r['MinNs']) / 1e3:>10.1f} "
+                   f"{float(r['MaxNs']) / 1e3:>10.1f} {float(r['TotalDurationNs']) / 1e6:>10.2f}")
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt")
+    open(path, "w").write("\n".join(out) + "\n")
+    print(path)
+
+
+def _pmc_per_dispatch(csv_path, counter):
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        d = r["Dispatch_Id"]
+        name = short_name(r["Kernel_Name"])
+        per.setdefault(d, [name, 0.0])
+        per[d][1] += float(r["Counter_Value"])
+    by = {}
+    for name, v in per.values():
+        by.setdefault(name, []).append(v)
+    return by
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, command, copy_bytes):
+    """FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by the ratio
+    of known bytes to what it reads for the plain copy of copy_bytes."""
+    import hashlib
+    import numpy as np
+    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    cf = float(np.median(f["copy"])) * 1024
+    cw = float(np.median(w["copy"])) * 1024
+    sf, sw = copy_bytes / cf, copy_bytes / cw
+    src = open(os.path.join(ROOT, "gradient_sync_zero_amd", "csrc", "gsz_step.hip"), "rb").read()
+    out = [f"# HBM traffic per launch from rocprofv3 counters: {workload}", "#",
+           f"# command: {command}", "#",
+           f"# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the copy kernel's",
+           f"# known bytes ({copy_bytes} read, {copy_bytes} written): fetch x {sf:.4f}, "
+           f"write x {sw:.4f}.", "# A kernel edited after this file was written gets traffic = null.",
+           f"source_sha256 = {hashlib.sha256(src).hexdigest()}",
+           f"copy.fetch_scale = {sf:.6f}", f"copy.write_scale = {sw:.6f}"]
+    for name in sorted(set(f) & set(w)):
+        if name in ("synth_fill", "torch_fill", "hip_runtime_copy"):
+            continue
+        fb = float(np.mean(f[name])) * 1024 * sf
+        wb = float(np.mean(w[name])) * 1024 * sw
+        out += [f"{name}.launches = {len(f[name])}",
+                f"{name}.fetch_bytes_per_launch = {fb:.0f}",
+                f"{name}.write_bytes_per_launch = {wb:.0f}",
+                f"{name}.hbm_bytes_per_launch = {fb + wb:.0f}"]
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    open(path, "w").write("\n".join(out) + "\n")
+    print(path)
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None if it
+    is missing or was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^\s*([\w.]+)\s*=\s*(\S+)\s*$", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    src = open(os.path.join(ROOT, "gradient_sync_zero_amd", "csrc", "gsz_step.hip"), "rb").read()
+    if kv.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    key = f"{kernel}.hbm_bytes_per_launch"
+    return float(kv[key]) if key in kv else None
+
+
+def cpu_baseline(w, owner):
+    """The oracle as it stands, on one core, over the trailing buckets of the
+    same workload (the first buckets of its plan): owner's pack, reduce-mean,
+    squared norm, clip and AdamW + all-gather layout.  Input generation is not
+    timed."""
+    import numpy as np
+    from oracle import pack as opack
+    from oracle.adamw import adamw
+    from oracle.layout import ag_write
+    from oracle.norm import clip_coef, sqnorm_partial, total
+    from oracle.plan import make_plan
+    from oracle.reduce import reduce_mean
+    from synth import gen
+    from synth import workloads as W
+
+    numel = w.numel
+    m, s = 0, 0
+    while s < 256_000_000 and m < len(numel):
+        m += 1
+        s += numel[-m]
+    sub = numel[-m:]
+    pre = sum(numel[:-m])
+    P = w.world_size
+    plan = make_plan(sub, w.bucket_cap_bytes, P)
+    offs = np.cumsum([0] + sub)
+    log(f"[cpu] generating the oracle sample: {len(plan.buckets)} buckets, {s} params x {P} ranks")
+    grads = []
+    for q in range(P):
+        G = gen.host_fill(w.cfg_id, W.KIND_GRAD, q, pre, s, w.grad_std, gen.MODE_BF16)
+        grads.append([G[offs[i]:offs[i + 1]] for i in range(m)])
+    others = [opack.pack(plan, grads[q]) for q in range(P) if q != owner]
+    S = plan.shard_len
+    state = []
+    for kind, std, mode in ((W.KIND_MASTER, W.MASTER_STD, gen.MODE_F32),
+                            (W.KIND_EXP_AVG, W.EXP_AVG_STD, gen.MODE_F32),
+                            (W.KIND_EXP_AVG_SQ, W.EXP_AVG_SQ_STD, gen.MODE_ABS)):
+        state.append(gen.host_fill(w.cfg_id, kind, 0, pre, S, std, mode))
+    hp = w.hp
+    log(f"[cpu] timing the oracle step on S = {S} shard elements")
+    t0 = time.perf_counter()
+    mine = opack.pack(plan, grads[owner])
+    flats = others[:owner] + [mine] + others[owner:]
+    g = reduce_mean([opack.owner_view(plan, f, owner) for f in flats], owner)
+    part = sqnorm_partial(g)
+    _, coef = clip_coef(total([part] * P), hp.max_norm)
+    th, m1, v1, p = adamw(state[0], state[1], state[2], g, coef, hp.lr, hp.beta1, hp.beta2,
+                          hp.eps, hp.weight_decay, hp.step)
+    gathered = np.zeros(plan.flat_len, dtype=np.uint16)
+    ag_write(plan, owner, p, gathered)
+    dt = time.perf_counter() - t0
+    return dict(value=S / dt, unit="params/s", cores=1, kind="oracle",
+                sample=(f"{w.name}: the first {len(plan.buckets)} buckets of the plan "
+                        f"({m} trailing tensors, {s} params, owner {owner} shard of {S}); "
+                        f"pack + reduce-mean + norm + clip + AdamW + all-gather layout, "
+                        f"{dt:.2f} s single-threaded NumPy"))
+
+
+def main():
+    args = parse()
+    if args.summarize_trace or args.summarize_pmc:
+        from synth import workloads as W
+        wname = W.by_id(args.config).name
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace, wname, args.command)
+        if args.summarize_pmc:
+            nb = int(args.copy_gib * (1 << 30)) // 16 * 16
+            summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], wname, args.command, nb)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: only --gpus 1 is supported: the P data-parallel ranks are simulated "
+              "as P contribution buffers on one GPU; the multi-GPU exchange is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    ensure_built()
+    import numpy as np
+    import torch
+
+    import gradient_sync_zero_amd as G
+    from synth import gen
+    from synth import workloads as W
+    from tests import gpu_inputs as GI
+
+    torch.cuda.set_device(0)
+    w = W.by_id(args.config)
+    P, r = w.world_size, args.owner
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    S, L = plan.shard_len, plan.flat_len
+    dev = torch.cuda.get_device_properties(0)
+    log(f"[gpu] {dev.name} ({getattr(dev, 'gcnArchName', '?')}), {w.name}: "
+        f"Psi={w.n_params} S={S} flat={L} buckets={plan.n_buckets}")
+
+    # Inputs: every rank's gradients packed into its bucket-major flat buffer.
+    t0 = time.perf_counter()
+    gbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+    flats = [torch.empty(L, dtype=torch.uint16, device="cuda") for _ in range(P)]
+    for q in list(range(P - 1, -1, -1)):
+        if q == r:
+            continue
+        _, views = GI.rank_grads(w, q, gbuf)
+        G.bucket_pack(plan, views, flats[q])
+    _, my_grads = GI.rank_grads(w, r, gbuf)      # the owner's own per-tensor gradients
+    master, m, v = GI.owner_state(plan, w, r)
+    g = torch.empty(S, dtype=torch.float32, device="cuda")
+    gathered = torch.zeros(L, dtype=torch.uint16, device="cuda")
+    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    partials = torch.zeros(P, dtype=torch.float64, device="cuda")
+    coef = torch.empty(1, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[gpu] inputs ready in {time.perf_counter() - t0:.1f} s; "
+        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+
+    # The other ranks' partials come from the exchange that one GPU does not
+    # perform; they are stand-ins equal to this shard's partial.
+    G.bucket_pack(plan, my_grads, flats[r])
+    G.shard_reduce_mean(plan, r, flats, G.LAYOUT_BUCKET_FLAT, g, partials[r:r + 1], ws)
+    torch.cuda.synchronize()
+    partials.fill_(float(partials[r]))
+
+    names = ["bucket_pack", "shard_reduce_mean", "clip_coef", "shard_adamw_step"]
+    launches = {"bucket_pack": -(-plan.n_tensors // 256), "shard_reduce_mean": 1,
+                "clip_coef": 1, "shard_adamw_step": 1}
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        G.bucket_pack(plan, my_grads, flats[r])
+        if e: e[1].record()
+        G.shard_reduce_mean(plan, r, flats, G.LAYOUT_BUCKET_FLAT, g, partials[r:r + 1], ws)
+        if e: e[2].record()
+        G.clip_coef(partials, w.hp.max_norm, coef)
+        if e: e[3].record()
+        G.shard_adamw_step(plan, r, master, m, v, g, coef, w.hp, gathered, None)
+        if e: e[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    per = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
+           for i, n in enumerate(names)}
+
+    # Algorithmic bytes (what the method must move), per call.
+    byts = {"bucket_pack": 4 * w.n_params + 2 * (L - w.n_params),
+            "shard_reduce_mean": (2 * P + 4) * S,
+            "clip_coef": 8 * P + 12,
+            "shard_adamw_step": 30 * S}
+    step_bytes = sum(byts.values())
+    kern = {n: dict(ms=per[n], launches=launches[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9,
+                    bytes=byts[n]) for n in names}
+    for n in names:
+        kern[n]["frac"] = kern[n]["GBps"] / HBM_PEAK_GBPS
+    dom = max(names, key=lambda n: per[n])
+    dom_bytes = byts[dom] / launches[dom]
+    dom_ms = per[dom] / launches[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    kernel_symbol = {"bucket_pack": "k_pack", "shard_reduce_mean": "k_reduce_mean",
+                     "clip_coef": "k_clip", "shard_adamw_step": "k_adamw"}[dom]
+    traffic = read_traffic(kernel_symbol, w.name)
+    step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"[gpu] {ms_step:.3f} ms/step; " + "; ".join(
+        f"{n} {kern[n]['ms']:.3f} ms {kern[n]['GBps']:.0f} GB/s" for n in names))
+
+    # The standalone forms of two rows the step runs fused: the squared norm of
+    # g (fused into the reduce) and the all-gather layout writer (fused into
+    # the AdamW store).
+    def time_call(fn, reps=5):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    shard_bf16 = torch.zeros(S, dtype=torch.uint16, device="cuda")
+    part1 = torch.zeros(1, dtype=torch.float64, device="cuda")
+    standalone = {}
+    for name, fn, nbytes in (
+            ("shard_grad_sqnorm", lambda: G.shard_grad_sqnorm(g, part1, ws), 4 * S),
+            ("allgather_layout_write",
+             lambda: G.allgather_layout_write(plan, r, shard_bf16, gathered), 4 * S)):
+        ms = time_call(fn)
+        standalone[name] = dict(ms=ms, bytes=nbytes, GBps=nbytes / (ms * 1e-3) / 1e9,
+                                frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+    log("[gpu] standalone: " + "; ".join(f"{n} {v['ms']:.3f} ms {v['GBps']:.0f} GB/s"
+                                         for n, v in standalone.items()))
+    del shard_bf16
+
+    # Plain streaming probes, run after the timed steps so that their
+    # allocations do not fragment the memory the working set was placed in:
+    # copy (the practical ceiling for half-read/half-write traffic and the
+    # calibration kernel of the counter runs), read-only and write-only.
+    nb = int(args.copy_gib * (1 << 30)) // 16 * 16
+    a = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    sink = torch.empty(dev.multi_processor_count * 8 * 256, dtype=torch.int32, device="cuda")
+    ceil = {}
+    for name, fn, nbytes in (("copy", lambda: gen.dev_copy(a, b, nb), 2 * nb),
+                             ("read", lambda: gen.dev_read(a, sink, nb), nb),
+                             ("write", lambda: gen.dev_write(b, nb), nb)):
+        for _ in range(2):
+            fn()
+        ms = time_call(fn, reps=10)
+        ceil[name] = nbytes / (ms * 1e-3) / 1e9
+    copy_gbps = ceil["copy"]
+    del a, b, sink
+    log("[gpu] streaming ceilings (GB/s): " + ", ".join(f"{k} {v:.0f}" for k, v in ceil.items()))
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, r)
+    out = {
+        "metric": METRIC,
+        "value": S / (ms_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "world_size_P": P, "owner": r, "model_params": w.n_params,
+                   "shard_params": S, "bucket_cap_MiB": w.bucket_cap_bytes // (1 << 20),
+                   "buckets": plan.n_buckets, "contribution_layout": "bucket-flat",
+                   "precision": "bf16 grads/params, fp32 accumulation and master/m/v",
+                   "step": "bucket_pack + shard_reduce_mean(+sqnorm) + clip_coef + "
+                           "shard_adamw_step(all-gather layout)"},
+        "hbm_GBps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "step_bytes": step_bytes,
+        "copy_ceiling_GBps": copy_gbps,
+        "streaming_ceilings_GBps": ceil,
+        "kernels_standalone": standalone,
+        "kernels": kern,
+        "roofline": {"bound": "hbm", "kernel": kernel_symbol, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "bytes_per_launch": dom_bytes,
+                     "ms_per_launch": dom_ms},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

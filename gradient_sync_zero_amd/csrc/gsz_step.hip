@@ -20,11 +20,17 @@ using gsz::set_error;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kBlocksPerCU = 8;
+// Blocks per CU of the grid-stride kernels (pack, reduce, norm, all-gather
+// writer) and of AdamW, and AdamW's block size: the fastest settings measured
+// on MI355X for the 7B share.
+constexpr int kBlocksPerCU = 16;
+constexpr int kAdamBlock = 512;
+constexpr int kAdamBlocksPerCU = 8;
 
 struct RankPtrs { const uint16_t* p[GSZ_MAX_RANKS]; };
 struct PackPtrs { const uint16_t* p[gsz::kPackBatch]; };
@@ -286,43 +292,53 @@ __device__ __forceinline__ void adamw1(float& th, float& mm, float& vv, float gg
     vv = v1;
 }
 
+// A wave owns 512 consecutive shard elements per iteration, as two groups of
+// 256; lane l updates elements 4l..4l+3 of each group, so every 16-byte load
+// and store instruction of the wave covers 1 KiB of whole 128-byte lines (a
+// lane that loads 32 contiguous bytes as two 16-byte halves makes each
+// instruction touch half of every line, and half-line misses to the same line
+// are fetched twice).  The bf16 result goes out as 8 bytes per lane.
 template <bool GATH, bool SHARD>
-__global__ __launch_bounds__(kBlock) void k_adamw(float* __restrict__ master, float* __restrict__ m,
-                                                  float* __restrict__ v, const float* __restrict__ g,
-                                                  const float* __restrict__ coefp, AdamScalars s,
-                                                  const int64_t* __restrict__ seg, int nseg,
-                                                  int64_t owner, int64_t nvec,
-                                                  uint16_t* __restrict__ gathered,
-                                                  uint16_t* __restrict__ shard_bf16) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    int64_t vi = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+__global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master, float* __restrict__ m,
+                                                      float* __restrict__ v, const float* __restrict__ g,
+                                                      const float* __restrict__ coefp, AdamScalars s,
+                                                      const int64_t* __restrict__ seg, int nseg,
+                                                      int64_t owner, int64_t S,
+                                                      uint16_t* __restrict__ gathered,
+                                                      uint16_t* __restrict__ shard_bf16) {
+    constexpr int kWaves = kAdamBlock / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    int64_t wv = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t ntile = (S + 511) / 512;
     const float coef = *coefp;
     SegCursor cur{seg, owner, 0, 0, 0};
-    if (GATH && vi < nvec) cur.seek(vi * 8, nseg);
-    for (; vi < nvec; vi += stride) {
-        const int64_t i = vi * 8;
-        const f32x4 g0 = ldf4(g + i), g1 = ldf4(g + i + 4);
-        f32x4 t0 = ldf4(master + i), t1 = ldf4(master + i + 4);
-        f32x4 m0 = ldf4(m + i), m1 = ldf4(m + i + 4);
-        f32x4 v0 = ldf4(v + i), v1 = ldf4(v + i + 4);
-        float th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-        float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    if (GATH && wv < ntile) {
+        const int64_t first = wv * 512 + 4 * lane;
+        cur.seek(first < S ? first : S - 4, nseg);
+    }
+    for (; wv < ntile; wv += nwaves) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) adamw1(th[j], mm[j], vv[j], gg[j], coef, s);
-        stf4(master + i, f32x4{th[0], th[1], th[2], th[3]});
-        stf4(master + i + 4, f32x4{th[4], th[5], th[6], th[7]});
-        stf4(m + i, f32x4{mm[0], mm[1], mm[2], mm[3]});
-        stf4(m + i + 4, f32x4{mm[4], mm[5], mm[6], mm[7]});
-        stf4(v + i, f32x4{vv[0], vv[1], vv[2], vv[3]});
-        stf4(v + i + 4, f32x4{vv[4], vv[5], vv[6], vv[7]});
-        const u32x4 p = u32x4{bf16_rne(th[0]) | (bf16_rne(th[1]) << 16),
-                              bf16_rne(th[2]) | (bf16_rne(th[3]) << 16),
-                              bf16_rne(th[4]) | (bf16_rne(th[5]) << 16),
-                              bf16_rne(th[6]) | (bf16_rne(th[7]) << 16)};
-        if (GATH) st16(gathered + cur.map(i), p);
-        if (SHARD) st16(shard_bf16 + i, p);
+        for (int h = 0; h < 2; ++h) {
+            const int64_t i = wv * 512 + h * 256 + 4 * lane;
+            if (i < S) {                       // S and i are multiples of 4
+                const f32x4 g4 = ldf4(g + i);
+                const f32x4 t4 = ldf4(master + i), m4 = ldf4(m + i), v4 = ldf4(v + i);
+                float th[4] = {t4.x, t4.y, t4.z, t4.w};
+                float mm[4] = {m4.x, m4.y, m4.z, m4.w};
+                float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+                const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) adamw1(th[j], mm[j], vv[j], gg[j], coef, s);
+                stf4(master + i, f32x4{th[0], th[1], th[2], th[3]});
+                stf4(m + i, f32x4{mm[0], mm[1], mm[2], mm[3]});
+                stf4(v + i, f32x4{vv[0], vv[1], vv[2], vv[3]});
+                const u32x2 p = u32x2{bf16_rne(th[0]) | (bf16_rne(th[1]) << 16),
+                                      bf16_rne(th[2]) | (bf16_rne(th[3]) << 16)};
+                if (GATH) *reinterpret_cast<u32x2*>(gathered + cur.map(i)) = p;
+                if (SHARD) *reinterpret_cast<u32x2*>(shard_bf16 + i) = p;
+            }
+        }
     }
 }
 
@@ -641,15 +657,18 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
     s.lr = (float)hp->lr;
     s.eps = (float)hp->eps;
     s.decay = (float)(1.0 - hp->lr * hp->weight_decay);
-    const int64_t nvec = S / 8;
-    const dim3 grid(grid_for(nvec, cus));
+    const int64_t ntile = (S + 511) / 512;
+    int64_t blocks = (ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64);
+    const int64_t cap = (int64_t)cus * kAdamBlocksPerCU;
+    if (blocks > cap) blocks = cap;
+    const dim3 grid((unsigned)blocks);
     const int nseg = (int)p->buckets.size();
     if (gathered && shard_bf16)
-        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, nvec, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, S, gathered, shard_bf16);
     else if (gathered)
-        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, nvec, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, S, gathered, shard_bf16);
     else
-        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, nvec, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, S, gathered, shard_bf16);
     return launched(who);
 }
 

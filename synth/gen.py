@@ -68,6 +68,12 @@ def _load_dev():
         lib.synth_copy_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int, ctypes.c_void_p]
         lib.synth_copy_dev.restype = ctypes.c_int
+        lib.synth_read_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_void_p]
+        lib.synth_read_dev.restype = ctypes.c_int
+        lib.synth_write_dev.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_void_p]
+        lib.synth_write_dev.restype = ctypes.c_int
         _dev = lib
     return _dev
 
@@ -133,3 +139,20 @@ def dev_copy(src, dst, nbytes, grid=0, stream=None):
     rc = _load_dev().synth_copy_dev(src.data_ptr(), dst.data_ptr(), nbytes, grid, s)
     if rc != 0:
         raise RuntimeError(f"synth_copy_dev failed ({rc})")
+
+
+def dev_read(src, out, nbytes, grid=0, stream=None):
+    """Read-only bandwidth probe; out must hold grid*256 uint32 (grid 0 = 8 per CU)."""
+    import torch
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    rc = _load_dev().synth_read_dev(src.data_ptr(), out.data_ptr(), nbytes, grid, s)
+    if rc != 0:
+        raise RuntimeError(f"synth_read_dev failed ({rc})")
+
+
+def dev_write(dst, nbytes, grid=0, stream=None):
+    import torch
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    rc = _load_dev().synth_write_dev(dst.data_ptr(), nbytes, grid, s)
+    if rc != 0:
+        raise RuntimeError(f"synth_write_dev failed ({rc})")

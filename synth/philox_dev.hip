@@ -51,12 +51,63 @@ __global__ void synth_fill_kernel(uint32_t seed, uint32_t key1, uint64_t start, 
     }
 }
 
-// Plain 16-byte-per-lane copy: n16 vectors of 16 bytes.
-__global__ void synth_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                  int64_t n16) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-        dst[i] = src[i];
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Plain copy of n16 16-byte vectors.  Each block copies runs of 8 * 256
+// vectors (8 loads in flight per lane, then 8 stores), with nontemporal hints:
+// the fastest of the simple copy variants measured on MI355X.
+__global__ __launch_bounds__(256) void synth_copy_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst, int64_t n16) {
+    constexpr int U = 8;
+    const int64_t per_block = 256 * U;
+    const int64_t nblk = (n16 + per_block - 1) / per_block;
+    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int64_t base = blk * per_block + threadIdx.x;
+        u32x4 w[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t i = base + (int64_t)k * 256;
+            if (i < n16) w[k] = __builtin_nontemporal_load(src + i);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t i = base + (int64_t)k * 256;
+            if (i < n16) __builtin_nontemporal_store(w[k], dst + i);
+        }
+    }
+}
+
+// Read-only stream of n16 vectors (8 nontemporal loads in flight per lane); one
+// word per thread is written so the loads are not removed.
+__global__ __launch_bounds__(256) void synth_read_kernel(const u32x4* __restrict__ src,
+                                                         unsigned* __restrict__ out, int64_t n16) {
+    constexpr int U = 8;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    unsigned acc = 0;
+    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < n16; b += stride * U) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t i = b + k * stride;
+            if (i < n16) {
+                const u32x4 w = __builtin_nontemporal_load(src + i);
+                acc ^= w.x ^ w.y ^ w.z ^ w.w;
+            }
+        }
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// Write-only stream of n16 vectors (4 stores per lane per iteration).
+__global__ __launch_bounds__(256) void synth_write_kernel(u32x4* __restrict__ dst, int64_t n16) {
+    constexpr int U = 4;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < n16; b += stride * U) {
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t i = b + k * stride;
+            if (i < n16) dst[i] = u32x4{(unsigned)i, 1u, 2u, 3u};
+        }
+    }
 }
 
 int grid_for(int64_t n, int block) {
@@ -95,7 +146,33 @@ int synth_copy_dev(const void* src, void* dst, int64_t nbytes, int grid, hipStre
     const int64_t n16 = nbytes / 16;
     const int g = grid > 0 ? grid : grid_for(n16, block);
     hipLaunchKernelGGL(synth_copy_kernel, dim3(g), dim3(block), 0, stream,
-                       (const uint4*)src, (uint4*)dst, n16);
+                       (const u32x4*)src, (u32x4*)dst, n16);
+    return (int)hipGetLastError();
+}
+
+// Read-only probe over nbytes of src (a multiple of 16, 16-byte aligned).
+// `out` must hold grid * 256 words; grid <= 0 picks 8 blocks per CU.
+int synth_read_dev(const void* src, void* out, int64_t nbytes, int grid, hipStream_t stream) {
+    if (nbytes <= 0 || (nbytes & 15) || ((uintptr_t)src & 15) || !out) return -1;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const int g = grid > 0 ? grid : cus * 8;
+    hipLaunchKernelGGL(synth_read_kernel, dim3(g), dim3(256), 0, stream, (const u32x4*)src,
+                       (unsigned*)out, nbytes / 16);
+    return (int)hipGetLastError();
+}
+
+// Write-only probe over nbytes of dst; grid <= 0 picks 2 blocks per CU.
+int synth_write_dev(void* dst, int64_t nbytes, int grid, hipStream_t stream) {
+    if (nbytes <= 0 || (nbytes & 15) || ((uintptr_t)dst & 15)) return -1;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const int g = grid > 0 ? grid : cus * 2;
+    hipLaunchKernelGGL(synth_write_kernel, dim3(g), dim3(256), 0, stream, (u32x4*)dst, nbytes / 16);
     return (int)hipGetLastError();
 }
 

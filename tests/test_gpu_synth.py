@@ -29,3 +29,20 @@ def test_copy_probe():
     gen.dev_copy(src, dst, src.numel() * 4)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def test_read_and_write_probes():
+    n = 1 << 22
+    a = torch.arange(n, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(torch.cuda.get_device_properties(0).multi_processor_count * 8 * 256,
+                       dtype=torch.int32, device="cuda")
+    gen.dev_read(a, sink, n * 4)
+    b = torch.zeros(n, dtype=torch.int32, device="cuda")
+    gen.dev_write(b, n * 4)
+    torch.cuda.synchronize()
+    w = b.view(-1, 4).cpu()
+    assert torch.equal(w[:, 0], torch.arange(n // 4, dtype=torch.int32))
+    assert (w[:, 1] == 1).all() and (w[:, 3] == 3).all()
+    # every loaded word is folded into some lane's xor: the lanes' xor is the xor of all words
+    assert int(np.bitwise_xor.reduce(sink.cpu().numpy())) == \
+        int(np.bitwise_xor.reduce(np.arange(n, dtype=np.int32)))
