@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload id (synth.workloads)")
     ap.add_argument("--owner", type=int, default=0)
+    ap.add_argument("--variant", choices=["zero", "ddp"], default="zero",
+                    help="zero: the ZeRO-1/2 shard step (default); ddp: the unsharded step "
+                         "(all-reduce, replicated AdamW, unpack)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-gib", type=float, default=4.0,
                     help="size of the plain copy used as the measured HBM ceiling")
@@ -216,6 +219,88 @@ def cpu_baseline(w, owner):
                         f"{dt:.2f} s single-threaded NumPy"))
 
 
+def bench_ddp(args):
+    """The unsharded (DDP / NO_SHARD) step of one rank: pack its gradients,
+    all-reduce mean over the P flat buffers (local arithmetic), squared norm,
+    clip, AdamW over every parameter, unpack the bf16 parameters into the
+    per-tensor buffers.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import gradient_sync_zero_amd as G
+    from synth import workloads as W
+    from tests import gpu_inputs as GI
+
+    torch.cuda.set_device(0)
+    w = W.by_id(args.config)
+    P, r = w.world_size, args.owner
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    L = plan.flat_len
+    need = (P + 1) * 2 * L + 2 * w.n_params + 20 * L + 2 * L
+    if need > 240e9:
+        print(f"bench.py: the unsharded step of {w.name} needs {need / 1e9:.0f} GB of HBM; "
+              "use a smaller --config", file=sys.stderr)
+        sys.exit(2)
+    gbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+    flats = [torch.empty(L, dtype=torch.uint16, device="cuda") for _ in range(P)]
+    for q in range(P - 1, -1, -1):
+        if q != r:
+            _, views = GI.rank_grads(w, q, gbuf)
+            G.bucket_pack(plan, views, flats[q])
+    _, my_grads = GI.rank_grads(w, r, gbuf)
+    master, m, v = GI.full_state(plan, w)
+    g = torch.empty(L, dtype=torch.float32, device="cuda")
+    pflat = torch.empty(L, dtype=torch.uint16, device="cuda")
+    pbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+    params = [pbuf[s0:s0 + n] for s0, n in zip(GI.prefix(w.numel), w.numel)]
+    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    part = torch.zeros(1, dtype=torch.float64, device="cuda")
+    coef = torch.empty(1, dtype=torch.float32, device="cuda")
+    names = ["bucket_pack", "allreduce_mean", "shard_grad_sqnorm", "clip_coef", "adamw_step",
+             "bucket_unpack"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+
+    def step(e=None):
+        calls = [lambda: G.bucket_pack(plan, my_grads, flats[r]),
+                 lambda: G.allreduce_mean(plan, flats, g),
+                 lambda: G.shard_grad_sqnorm(g, part, ws),
+                 lambda: G.clip_coef(part, w.hp.max_norm, coef),
+                 lambda: G.adamw_step(master, m, v, g, coef, w.hp, pflat),
+                 lambda: G.bucket_unpack(plan, pflat, params)]
+        for i, c in enumerate(calls):
+            if e: e[i].record()
+            c()
+        if e: e[6].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    per = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
+           for i, n in enumerate(names)}
+    byts = {"bucket_pack": 4 * w.n_params + 2 * (L - w.n_params),
+            "allreduce_mean": (2 * P + 4) * L, "shard_grad_sqnorm": 4 * L, "clip_coef": 20,
+            "adamw_step": 30 * L, "bucket_unpack": 4 * w.n_params}
+    kern = {n: dict(ms=per[n], bytes=byts[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9) for n in names}
+    step_gbps = sum(byts.values()) / (ms_step * 1e-3) / 1e9
+    log(f"[gpu] DDP {w.name}: {ms_step:.3f} ms/step; " + "; ".join(
+        f"{n} {kern[n]['ms']:.3f} ms {kern[n]['GBps']:.0f} GB/s" for n in names))
+    print(json.dumps({
+        "metric": "params/s and achieved HBM GB/s for the unsharded (DDP) step of one rank",
+        "value": w.n_params / (ms_step * 1e-3), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "variant": "ddp", "world_size_P": P,
+                   "model_params": w.n_params, "step": " + ".join(names)},
+        "hbm_GBps": step_gbps, "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS, "kernels": kern}),
+        flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace or args.summarize_pmc:
@@ -233,6 +318,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     ensure_built()
+    if args.variant == "ddp":
+        return bench_ddp(args)
     import numpy as np
     import torch
 
@@ -250,48 +337,69 @@ def main():
     log(f"[gpu] {dev.name} ({getattr(dev, 'gcnArchName', '?')}), {w.name}: "
         f"Psi={w.n_params} S={S} flat={L} buckets={plan.n_buckets}")
 
-    # Inputs: every rank's gradients packed into its bucket-major flat buffer.
+    # Inputs.  When all P ranks' bucket-major flat buffers fit next to the
+    # state (every config but the 70B share), the step packs the owner's own
+    # per-tensor gradients and reduces over the P flat buffers.  Otherwise the
+    # contributions are the shard-compact buffers the P ranks send to this
+    # owner, and the step is the reduce + clip + AdamW the metric names (the
+    # owner's full-model pack would need 2 x 138 GB more than the GPU holds).
     t0 = time.perf_counter()
-    gbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
-    flats = [torch.empty(L, dtype=torch.uint16, device="cuda") for _ in range(P)]
-    for q in list(range(P - 1, -1, -1)):
-        if q == r:
-            continue
-        _, views = GI.rank_grads(w, q, gbuf)
-        G.bucket_pack(plan, views, flats[q])
-    _, my_grads = GI.rank_grads(w, r, gbuf)      # the owner's own per-tensor gradients
+    flat_mode = (P + 2) * 2 * L + 2 * w.n_params + 18 * S < 240e9
+    if flat_mode:
+        gbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+        flats = [torch.empty(L, dtype=torch.uint16, device="cuda") for _ in range(P)]
+        for q in list(range(P - 1, -1, -1)):
+            if q == r:
+                continue
+            _, views = GI.rank_grads(w, q, gbuf)
+            G.bucket_pack(plan, views, flats[q])
+        _, my_grads = GI.rank_grads(w, r, gbuf)      # the owner's own per-tensor gradients
+        contribs, layout = flats, G.LAYOUT_BUCKET_FLAT
+        gathered, shard_out = torch.zeros(L, dtype=torch.uint16, device="cuda"), None
+    else:
+        contribs, layout = GI.compact_contribs(plan, w, r), G.LAYOUT_SHARD_COMPACT
+        gathered, shard_out = None, torch.zeros(S, dtype=torch.uint16, device="cuda")
     master, m, v = GI.owner_state(plan, w, r)
     g = torch.empty(S, dtype=torch.float32, device="cuda")
-    gathered = torch.zeros(L, dtype=torch.uint16, device="cuda")
     ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
     partials = torch.zeros(P, dtype=torch.float64, device="cuda")
     coef = torch.empty(1, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    log(f"[gpu] inputs ready in {time.perf_counter() - t0:.1f} s; "
+    log(f"[gpu] inputs ready in {time.perf_counter() - t0:.1f} s "
+        f"({'bucket-flat' if flat_mode else 'shard-compact'} contributions); "
         f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
 
     # The other ranks' partials come from the exchange that one GPU does not
     # perform; they are stand-ins equal to this shard's partial.
-    G.bucket_pack(plan, my_grads, flats[r])
-    G.shard_reduce_mean(plan, r, flats, G.LAYOUT_BUCKET_FLAT, g, partials[r:r + 1], ws)
+    if flat_mode:
+        G.bucket_pack(plan, my_grads, flats[r])
+    G.shard_reduce_mean(plan, r, contribs, layout, g, partials[r:r + 1], ws)
     torch.cuda.synchronize()
     partials.fill_(float(partials[r]))
 
-    names = ["bucket_pack", "shard_reduce_mean", "clip_coef", "shard_adamw_step"]
+    names = (["bucket_pack"] if flat_mode else []) + ["shard_reduce_mean", "clip_coef",
+                                                       "shard_adamw_step"]
     launches = {"bucket_pack": -(-plan.n_tensors // 256), "shard_reduce_mean": 1,
                 "clip_coef": 1, "shard_adamw_step": 1}
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    nev = len(names) + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
 
     def step(e=None):
-        if e: e[0].record()
-        G.bucket_pack(plan, my_grads, flats[r])
-        if e: e[1].record()
-        G.shard_reduce_mean(plan, r, flats, G.LAYOUT_BUCKET_FLAT, g, partials[r:r + 1], ws)
-        if e: e[2].record()
+        k = 0
+        if e: e[k].record()
+        if flat_mode:
+            G.bucket_pack(plan, my_grads, flats[r])
+            k += 1
+            if e: e[k].record()
+        G.shard_reduce_mean(plan, r, contribs, layout, g, partials[r:r + 1], ws)
+        k += 1
+        if e: e[k].record()
         G.clip_coef(partials, w.hp.max_norm, coef)
-        if e: e[3].record()
-        G.shard_adamw_step(plan, r, master, m, v, g, coef, w.hp, gathered, None)
-        if e: e[4].record()
+        k += 1
+        if e: e[k].record()
+        G.shard_adamw_step(plan, r, master, m, v, g, coef, w.hp, gathered, shard_out)
+        k += 1
+        if e: e[k].record()
 
     for _ in range(args.warmup):
         step()
@@ -310,6 +418,7 @@ def main():
             "shard_reduce_mean": (2 * P + 4) * S,
             "clip_coef": 8 * P + 12,
             "shard_adamw_step": 30 * S}
+    byts = {n: byts[n] for n in names}
     step_bytes = sum(byts.values())
     kern = {n: dict(ms=per[n], launches=launches[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9,
                     bytes=byts[n]) for n in names}
@@ -323,6 +432,9 @@ def main():
                      "clip_coef": "k_clip", "shard_adamw_step": "k_adamw"}[dom]
     traffic = read_traffic(kernel_symbol, w.name)
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    # The reduce-mean + AdamW shard step alone ((2P + 34) bytes per shard element).
+    fused_ms = per["shard_reduce_mean"] + per["clip_coef"] + per["shard_adamw_step"]
+    fused_gbps = (2 * P + 34) * S / (fused_ms * 1e-3) / 1e9
     log(f"[gpu] {ms_step:.3f} ms/step; " + "; ".join(
         f"{n} {kern[n]['ms']:.3f} ms {kern[n]['GBps']:.0f} GB/s" for n in names))
 
@@ -342,10 +454,17 @@ def main():
     shard_bf16 = torch.zeros(S, dtype=torch.uint16, device="cuda")
     part1 = torch.zeros(1, dtype=torch.float64, device="cuda")
     standalone = {}
-    for name, fn, nbytes in (
-            ("shard_grad_sqnorm", lambda: G.shard_grad_sqnorm(g, part1, ws), 4 * S),
-            ("allgather_layout_write",
-             lambda: G.allgather_layout_write(plan, r, shard_bf16, gathered), 4 * S)):
+    rows = [("shard_grad_sqnorm", lambda: G.shard_grad_sqnorm(g, part1, ws), 4 * S),
+            ("shard_reduce_mean_bf16_wire",
+             lambda: G.shard_reduce_mean(plan, r, contribs, layout, g, part1, ws, bf16_wire=True),
+             (2 * P + 4) * S)]
+    if gathered is not None:
+        rows.append(("allgather_layout_write",
+                     lambda: G.allgather_layout_write(plan, r, shard_bf16, gathered), 4 * S))
+    if flat_mode:
+        rows.append(("bucket_accumulate",
+                     lambda: G.bucket_accumulate(plan, my_grads, flats[r]), 6 * w.n_params))
+    for name, fn, nbytes in rows:
         ms = time_call(fn)
         standalone[name] = dict(ms=ms, bytes=nbytes, GBps=nbytes / (ms * 1e-3) / 1e9,
                                 frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
@@ -390,10 +509,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "world_size_P": P, "owner": r, "model_params": w.n_params,
                    "shard_params": S, "bucket_cap_MiB": w.bucket_cap_bytes // (1 << 20),
-                   "buckets": plan.n_buckets, "contribution_layout": "bucket-flat",
+                   "buckets": plan.n_buckets,
+                   "contribution_layout": "bucket-flat" if flat_mode else "shard-compact",
                    "precision": "bf16 grads/params, fp32 accumulation and master/m/v",
-                   "step": "bucket_pack + shard_reduce_mean(+sqnorm) + clip_coef + "
-                           "shard_adamw_step(all-gather layout)"},
+                   "step": " + ".join(names) + (" (all-gather layout)" if flat_mode
+                                                 else " (shard-layout bf16)")},
+        "reduce_adamw_ms": fused_ms,
+        "reduce_adamw_GBps": fused_gbps,
+        "reduce_adamw_frac_of_peak": fused_gbps / HBM_PEAK_GBPS,
         "hbm_GBps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "step_bytes": step_bytes,

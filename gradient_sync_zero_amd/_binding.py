@@ -69,6 +69,11 @@ _SIGS = {
     "gsz_clip_coef": [_P, _I32, ctypes.c_float, _P, _P, _P, _P],
     "gsz_shard_adamw_step": [_P, _I32, _P, _P, _P, _P, _P, ctypes.POINTER(AdamWHP), _P, _P, _P],
     "gsz_allgather_layout_write": [_P, _I32, _P, _P, _P],
+    "gsz_bucket_unpack": [_P, _P, _P, _P],
+    "gsz_bucket_accumulate": [_P, _P, _P, _P],
+    "gsz_shard_reduce_mean_bf16_wire": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+    "gsz_allreduce_mean": [_P, _P, _P, _P],
+    "gsz_adamw_step": [_P, _P, _P, _P, _I64, _P, ctypes.POINTER(AdamWHP), _P, _P],
 }
 
 _lib = None
@@ -215,14 +220,27 @@ def bucket_pack(plan, grads, flat, stream=None):
     _check(load().gsz_bucket_pack(plan.handle, ptrs, _ptr(flat, "flat", bt), _stream(stream)))
 
 
-def shard_reduce_mean(plan, owner, contribs, layout, g, partial_out=None, ws=None, stream=None):
+def bucket_accumulate(plan, grads, flat, stream=None):
+    bt = _bf16_types()
+    if len(grads) != plan.n_tensors:
+        raise ValueError("need one gradient per plan tensor")
+    ptrs = (_P * max(len(grads), 1))(*[_ptr(t, f"grads[{i}]", bt) if t.numel() else None
+                                       for i, t in enumerate(grads)])
+    _check(load().gsz_bucket_accumulate(plan.handle, ptrs, _ptr(flat, "flat", bt),
+                                        _stream(stream)))
+
+
+def shard_reduce_mean(plan, owner, contribs, layout, g, partial_out=None, ws=None, stream=None,
+                      bf16_wire=False):
+    """gsz_shard_reduce_mean (or gsz_shard_reduce_mean_bf16_wire when bf16_wire)."""
     bt = _bf16_types()
     if len(contribs) != plan.world_size:
         raise ValueError("need one contribution per rank")
     ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", bt) for i, t in enumerate(contribs)])
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(load().gsz_shard_reduce_mean(plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32()),
+    fn = load().gsz_shard_reduce_mean_bf16_wire if bf16_wire else load().gsz_shard_reduce_mean
+    _check(fn(plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32()),
                                         _ptr(partial_out, "partial_out", _f64(), allow_none=True),
                                         wsp, nbytes, _stream(stream)))
 
@@ -265,3 +283,31 @@ def allgather_layout_write(plan, owner, shard_bf16, gathered, stream=None):
     bt = _bf16_types()
     _check(load().gsz_allgather_layout_write(plan.handle, owner, _ptr(shard_bf16, "shard_bf16", bt),
                                              _ptr(gathered, "gathered", bt), _stream(stream)))
+
+
+def bucket_unpack(plan, flat, params, stream=None):
+    bt = _bf16_types()
+    if len(params) != plan.n_tensors:
+        raise ValueError("need one parameter tensor per plan tensor")
+    ptrs = (_P * max(len(params), 1))(*[_ptr(t, f"params[{i}]", bt) if t.numel() else None
+                                        for i, t in enumerate(params)])
+    _check(load().gsz_bucket_unpack(plan.handle, _ptr(flat, "flat", bt), ptrs, _stream(stream)))
+
+
+def allreduce_mean(plan, contribs, g_flat, stream=None):
+    bt = _bf16_types()
+    if len(contribs) != plan.world_size:
+        raise ValueError("need one contribution per rank")
+    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", bt) for i, t in enumerate(contribs)])
+    _check(load().gsz_allreduce_mean(plan.handle, ptrs, _ptr(g_flat, "g_flat", _f32()),
+                                     _stream(stream)))
+
+
+def adamw_step(master, m, v, g, coef, hp, out_bf16, stream=None):
+    bt = _bf16_types()
+    if not isinstance(hp, AdamWHP):
+        hp = AdamWHP(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step)
+    _check(load().gsz_adamw_step(_ptr(master, "master", _f32()), _ptr(m, "m", _f32()),
+                                 _ptr(v, "v", _f32()), _ptr(g, "g", _f32()), g.numel(),
+                                 _ptr(coef, "coef", _f32()), ctypes.byref(hp),
+                                 _ptr(out_bf16, "out_bf16", bt), _stream(stream)))

@@ -68,6 +68,12 @@ __device__ __forceinline__ void add8(u32x4 w, float a[8]) {
     a[6] = a[6] + bf16_lo(w.w); a[7] = a[7] + bf16_hi(w.w);
 }
 
+// a[j] <- bf16(a[j]) (round to nearest even), kept as fp32.
+__device__ __forceinline__ void round8_bf16(float a[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = __uint_as_float(bf16_rne(a[j]) << 16);
+}
+
 // Sum over the block in a fixed order; the result is valid in thread 0.
 __device__ double block_sum(double x) {
 #pragma unroll
@@ -112,9 +118,27 @@ struct SegCursor {
 
 // ------------------------------------------------------------------ pack --
 
-// Copies the tensors of one batch (bucket-order positions [k0, k0+nk)) into the
-// flat buffer.  tab rows: {dst offset, numel, first tile}; each block takes a
-// contiguous range of the batch's tiles [t_begin, t_end).
+// Pack modes: copy tensors into the flat buffer, copy flat ranges back into the
+// tensors, or add tensors into the flat buffer (bf16 += bf16 in fp32, rounded
+// to nearest even).
+enum PackMode { kPack = 0, kUnpack = 1, kAccumulate = 2 };
+
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
+    return bf16_rne(bf16_lo(a) + bf16_lo(b)) | (bf16_rne(bf16_hi(a) + bf16_hi(b)) << 16);
+}
+__device__ __forceinline__ u32x4 add_bf16x8(u32x4 a, u32x4 b) {
+    return u32x4{add_bf16x2(a.x, b.x), add_bf16x2(a.y, b.y), add_bf16x2(a.z, b.z),
+                 add_bf16x2(a.w, b.w)};
+}
+__device__ __forceinline__ uint16_t add_bf16(uint16_t a, uint16_t b) {
+    return (uint16_t)bf16_rne(__uint_as_float((uint32_t)a << 16) + __uint_as_float((uint32_t)b << 16));
+}
+
+// Moves the tensors of one batch (bucket-order positions [k0, k0+nk)) to or
+// from the flat buffer as MODE says.  tab rows: {flat offset, numel, first
+// tile}; each block takes a contiguous range of the batch's tiles
+// [t_begin, t_end).
+template <int MODE>
 __global__ __launch_bounds__(kBlock) void k_pack(PackPtrs pp, const int64_t* __restrict__ tab,
                                                  int k0, int nk, int64_t t_begin, int64_t t_end,
                                                  uint16_t* __restrict__ flat) {
@@ -135,22 +159,32 @@ __global__ __launch_bounds__(kBlock) void k_pack(PackPtrs pp, const int64_t* __r
         const int64_t n = tab[3 * k + 1];
         const int64_t j0 = (tile - tab[3 * k + 2]) * gsz::kPackTile;
         const int64_t j1 = j0 + gsz::kPackTile < n ? j0 + gsz::kPackTile : n;
-        const uint16_t* __restrict__ src = pp.p[k - k0];
-        uint16_t* __restrict__ dst = flat + tab[3 * k];
+        const uint16_t* __restrict__ src = MODE == kUnpack ? flat + tab[3 * k] : pp.p[k - k0];
+        uint16_t* __restrict__ dst = MODE == kUnpack ? const_cast<uint16_t*>(pp.p[k - k0]) : flat + tab[3 * k];
         const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
         if (vec && j1 - j0 == gsz::kPackTile) {
             constexpr int U = gsz::kPackTile / (8 * kBlock);
             u32x4 w[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = ld16(src + j0 + 8 * (tid + u * kBlock));
+            if (MODE == kAccumulate) {
+                u32x4 d[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) d[u] = ld16(dst + j0 + 8 * (tid + u * kBlock));
+#pragma unroll
+                for (int u = 0; u < U; ++u) w[u] = add_bf16x8(d[u], w[u]);
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) st16(dst + j0 + 8 * (tid + u * kBlock), w[u]);
         } else if (vec) {
             const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
-            for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kBlock) st16(dst + j, ld16(src + j));
-            for (int64_t j = jv + tid; j < j1; j += kBlock) dst[j] = src[j];
+            for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kBlock)
+                st16(dst + j, MODE == kAccumulate ? add_bf16x8(ld16(dst + j), ld16(src + j)) : ld16(src + j));
+            for (int64_t j = jv + tid; j < j1; j += kBlock)
+                dst[j] = MODE == kAccumulate ? add_bf16(dst[j], src[j]) : src[j];
         } else {
-            for (int64_t j = j0 + tid; j < j1; j += kBlock) dst[j] = src[j];
+            for (int64_t j = j0 + tid; j < j1; j += kBlock)
+                dst[j] = MODE == kAccumulate ? add_bf16(dst[j], src[j]) : src[j];
         }
     }
 }
@@ -168,8 +202,12 @@ __global__ __launch_bounds__(kBlock) void k_zero_pads(const int64_t* __restrict_
 // rank (owner+1+k) mod P, so the owner's own value is added last.  Each lane
 // handles 8 consecutive shard elements per iteration (one 16-byte load per
 // rank).  PS > 0 fixes P at compile time; loads are issued in groups of up to
-// 16 ranks before their adds so many 16-byte requests are in flight.
-template <int PS, bool NORM, bool FLAT>
+// 16 ranks before their adds so many 16-byte requests are in flight.  With
+// OUTFLAT (bucket-flat input only) g is indexed by flat position instead of
+// shard index: P launches, one per chunk owner, give the all-reduce result.
+// W16: the partial sum is rounded to bf16 after every addition (a ring whose
+// wire carries bf16 partial sums); the final division stays fp32.
+template <int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
                                                         const int64_t* __restrict__ seg, int nseg,
                                                         int64_t owner, int64_t nvec,
@@ -194,7 +232,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
                 for (int j = 0; j < G; ++j) w[j] = ld16(rp.p[k0 + j] + off);
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
-                    if (k0 + j == 0) widen8(w[j], a); else add8(w[j], a);
+                    if (k0 + j == 0) widen8(w[j], a);
+                    else { add8(w[j], a); if (W16) round8_bf16(a); }
                 }
             }
         } else {
@@ -205,9 +244,9 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
 #pragma unroll
                 for (int j = 0; j < 8; ++j) w[j] = ld16(rp.p[k + j] + off);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) add8(w[j], a);
+                for (int j = 0; j < 8; ++j) { add8(w[j], a); if (W16) round8_bf16(a); }
             }
-            for (; k < P; ++k) add8(ld16(rp.p[k] + off), a);
+            for (; k < P; ++k) { add8(ld16(rp.p[k] + off), a); if (W16) round8_bf16(a); }
         }
         if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
 #pragma unroll
@@ -216,8 +255,9 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
 #pragma unroll
             for (int j = 0; j < 8; ++j) a[j] = a[j] / fP;
         }
-        stf4(g + i, f32x4{a[0], a[1], a[2], a[3]});
-        stf4(g + i + 4, f32x4{a[4], a[5], a[6], a[7]});
+        const int64_t o = OUTFLAT ? off : i;    // all-reduce output: the flat position
+        stf4(g + o, f32x4{a[0], a[1], a[2], a[3]});
+        stf4(g + o + 4, f32x4{a[4], a[5], a[6], a[7]});
         if (NORM) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -407,6 +447,21 @@ int launched(const char* what) {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
 
+// The fp32 constants of the update, each formed in double and rounded once.
+AdamScalars adam_scalars(const gsz_adamw_hp& hp) {
+    AdamScalars s;
+    s.b1 = (float)hp.beta1;
+    s.omb1 = (float)(1.0 - hp.beta1);
+    s.b2 = (float)hp.beta2;
+    s.omb2 = (float)(1.0 - hp.beta2);
+    s.bc1 = (float)(1.0 - std::pow(hp.beta1, (double)hp.step));
+    s.bc2 = (float)(1.0 - std::pow(hp.beta2, (double)hp.step));
+    s.lr = (float)hp.lr;
+    s.eps = (float)hp.eps;
+    s.decay = (float)(1.0 - hp.lr * hp.weight_decay);
+    return s;
+}
+
 // Checks a plan for a device call: uploaded to the current device, vector granule.
 int check_plan(const gsz_plan* p, const char* who, int* cus) {
     if (!p) { set_error("%s: NULL plan", who); return GSZ_ERR_INVALID_ARG; }
@@ -435,8 +490,21 @@ int check_owner(const gsz_plan* p, int32_t owner, const char* who) {
 template <int PS>
 void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPtrs& rp, int P,
                    float invP, int pow2, const int64_t* seg, int nseg, int64_t owner, int64_t nvec,
-                   float* g, double* ws) {
-    if (norm && flat)
+                   float* g, double* ws, bool outflat = false, bool wire16 = false) {
+    if (wire16) {
+        if (norm && flat)
+            hipLaunchKernelGGL((k_reduce_mean<PS, true, true, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        else if (norm)
+            hipLaunchKernelGGL((k_reduce_mean<PS, true, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        else if (flat)
+            hipLaunchKernelGGL((k_reduce_mean<PS, false, true, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        else
+            hipLaunchKernelGGL((k_reduce_mean<PS, false, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        return;
+    }
+    if (outflat)
+        hipLaunchKernelGGL((k_reduce_mean<PS, false, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+    else if (norm && flat)
         hipLaunchKernelGGL((k_reduce_mean<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
     else if (norm)
         hipLaunchKernelGGL((k_reduce_mean<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
@@ -500,43 +568,64 @@ extern "C" int gsz_plan_upload(gsz_plan* p) {
     return GSZ_OK;
 }
 
-extern "C" int gsz_bucket_pack(const gsz_plan* p, const uint16_t* const* grads, uint16_t* flat,
-                               hipStream_t stream) {
+namespace {
+
+// Launches the pack kernel in MODE over every tensor: ptrs is the host array of
+// the T tensor pointers (sources for kPack/kAccumulate, destinations for kUnpack).
+int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, uint16_t* flat, int mode,
+             hipStream_t stream, const char* who) {
     int cus = 0;
-    int rc = check_plan(p, "gsz_bucket_pack", &cus);
+    int rc = check_plan(p, who, &cus);
     if (rc) return rc;
     const int T = (int)p->numel.size();
     if (p->flat_len == 0) return GSZ_OK;
-    if (!flat || (T > 0 && !grads)) { set_error("gsz_bucket_pack: NULL buffer"); return GSZ_ERR_INVALID_ARG; }
-    if (misaligned(flat)) { set_error("gsz_bucket_pack: flat is not 16-byte aligned"); return GSZ_ERR_MISALIGNED; }
+    if (!flat || (T > 0 && !ptrs)) { set_error("%s: NULL buffer", who); return GSZ_ERR_INVALID_ARG; }
+    if (misaligned(flat)) { set_error("%s: flat is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED; }
     for (int t = 0; t < T; ++t)
-        if (p->numel[t] > 0 && !grads[t]) {
-            set_error("gsz_bucket_pack: gradient pointer %d is NULL", t); return GSZ_ERR_INVALID_ARG;
+        if (p->numel[t] > 0 && !ptrs[t]) {
+            set_error("%s: tensor pointer %d is NULL", who, t); return GSZ_ERR_INVALID_ARG;
         }
     for (int k0 = 0; k0 < T; k0 += gsz::kPackBatch) {
         const int nk = T - k0 < gsz::kPackBatch ? T - k0 : gsz::kPackBatch;
         PackPtrs pp{};
-        for (int k = 0; k < nk; ++k) pp.p[k] = grads[T - 1 - (k0 + k)];
+        for (int k = 0; k < nk; ++k) pp.p[k] = ptrs[T - 1 - (k0 + k)];
         const int64_t tb = p->pack[3 * k0 + 2], te = p->pack[3 * (k0 + nk) + 2];
         if (te == tb) continue;
         const int64_t cap = (int64_t)cus * kBlocksPerCU;
         const int grid = (int)(te - tb < cap ? te - tb : cap);
-        hipLaunchKernelGGL(k_pack, dim3(grid), dim3(kBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, flat);
-        if ((rc = launched("gsz_bucket_pack"))) return rc;
+        if (mode == kPack)
+            hipLaunchKernelGGL(k_pack<kPack>, dim3(grid), dim3(kBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, flat);
+        else if (mode == kUnpack)
+            hipLaunchKernelGGL(k_pack<kUnpack>, dim3(grid), dim3(kBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, flat);
+        else
+            hipLaunchKernelGGL(k_pack<kAccumulate>, dim3(grid), dim3(kBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, flat);
+        if ((rc = launched(who))) return rc;
     }
     const int npad = (int)(p->pads.size() / 2);
-    if (npad > 0) {
+    if (mode == kPack && npad > 0) {
         hipLaunchKernelGGL(k_zero_pads, dim3(npad), dim3(kBlock), 0, stream, p->d_pads, flat);
-        if ((rc = launched("gsz_bucket_pack (pads)"))) return rc;
+        if ((rc = launched(who))) return rc;
     }
     return GSZ_OK;
 }
 
-extern "C" int gsz_shard_reduce_mean(const gsz_plan* p, int32_t owner,
-                                     const uint16_t* const* contrib, int32_t layout, float* g,
-                                     double* partial_out, void* ws, size_t ws_bytes,
-                                     hipStream_t stream) {
-    const char* who = "gsz_shard_reduce_mean";
+}  // namespace
+
+extern "C" int gsz_bucket_pack(const gsz_plan* p, const uint16_t* const* grads, uint16_t* flat,
+                               hipStream_t stream) {
+    return run_pack(p, grads, flat, kPack, stream, "gsz_bucket_pack");
+}
+
+extern "C" int gsz_bucket_accumulate(const gsz_plan* p, const uint16_t* const* grads,
+                                     uint16_t* flat, hipStream_t stream) {
+    return run_pack(p, grads, flat, kAccumulate, stream, "gsz_bucket_accumulate");
+}
+
+namespace {
+
+int reduce_impl(const gsz_plan* p, int32_t owner, const uint16_t* const* contrib, int32_t layout,
+                float* g, double* partial_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                bool wire16, const char* who) {
     int cus = 0;
     int rc = check_plan(p, who, &cus);
     if (rc) return rc;
@@ -573,13 +662,13 @@ extern "C" int gsz_shard_reduce_mean(const gsz_plan* p, int32_t owner,
         double* wsd = static_cast<double*>(ws);
         const dim3 gr(grid);
         switch (P) {
-            case 2: launch_reduce<2>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
-            case 4: launch_reduce<4>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
-            case 8: launch_reduce<8>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
-            case 16: launch_reduce<16>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
-            case 32: launch_reduce<32>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
-            case 64: launch_reduce<64>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
-            default: launch_reduce<0>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd); break;
+            case 2: launch_reduce<2>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
+            case 4: launch_reduce<4>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
+            case 8: launch_reduce<8>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
+            case 16: launch_reduce<16>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
+            case 32: launch_reduce<32>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
+            case 64: launch_reduce<64>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
+            default: launch_reduce<0>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
         }
         if ((rc = launched(who))) return rc;
     }
@@ -589,6 +678,24 @@ extern "C" int gsz_shard_reduce_mean(const gsz_plan* p, int32_t owner,
         if ((rc = launched(who))) return rc;
     }
     return GSZ_OK;
+}
+
+}  // namespace
+
+extern "C" int gsz_shard_reduce_mean(const gsz_plan* p, int32_t owner,
+                                     const uint16_t* const* contrib, int32_t layout, float* g,
+                                     double* partial_out, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    return reduce_impl(p, owner, contrib, layout, g, partial_out, ws, ws_bytes, stream, false,
+                       "gsz_shard_reduce_mean");
+}
+
+extern "C" int gsz_shard_reduce_mean_bf16_wire(const gsz_plan* p, int32_t owner,
+                                               const uint16_t* const* contrib, int32_t layout,
+                                               float* g, double* partial_out, void* ws,
+                                               size_t ws_bytes, hipStream_t stream) {
+    return reduce_impl(p, owner, contrib, layout, g, partial_out, ws, ws_bytes, stream, true,
+                       "gsz_shard_reduce_mean_bf16_wire");
 }
 
 extern "C" int gsz_shard_grad_sqnorm(const float* g, int64_t n, double* partial_out, void* ws,
@@ -647,16 +754,7 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
         (gathered && misaligned(gathered)) || (shard_bf16 && misaligned(shard_bf16))) {
         set_error("%s: a buffer is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED;
     }
-    AdamScalars s;
-    s.b1 = (float)hp->beta1;
-    s.omb1 = (float)(1.0 - hp->beta1);
-    s.b2 = (float)hp->beta2;
-    s.omb2 = (float)(1.0 - hp->beta2);
-    s.bc1 = (float)(1.0 - std::pow(hp->beta1, (double)hp->step));
-    s.bc2 = (float)(1.0 - std::pow(hp->beta2, (double)hp->step));
-    s.lr = (float)hp->lr;
-    s.eps = (float)hp->eps;
-    s.decay = (float)(1.0 - hp->lr * hp->weight_decay);
+    const AdamScalars s = adam_scalars(*hp);
     const int64_t ntile = (S + 511) / 512;
     int64_t blocks = (ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64);
     const int64_t cap = (int64_t)cus * kAdamBlocksPerCU;
@@ -687,5 +785,73 @@ extern "C" int gsz_allgather_layout_write(const gsz_plan* p, int32_t owner,
     const int64_t nvec = S / 8;
     hipLaunchKernelGGL(k_ag_write, dim3(grid_for(nvec, cus)), dim3(kBlock), 0, stream, shard_bf16,
                        p->d_seg, (int)p->buckets.size(), (int64_t)owner, nvec, gathered);
+    return launched(who);
+}
+
+extern "C" int gsz_bucket_unpack(const gsz_plan* p, const uint16_t* flat, uint16_t* const* params,
+                                 hipStream_t stream) {
+    return run_pack(p, const_cast<const uint16_t* const*>(params), const_cast<uint16_t*>(flat),
+                    kUnpack, stream, "gsz_bucket_unpack");
+}
+
+extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* contrib, float* g_flat,
+                                  hipStream_t stream) {
+    const char* who = "gsz_allreduce_mean";
+    int cus = 0;
+    int rc = check_plan(p, who, &cus);
+    if (rc) return rc;
+    const int P = p->P;
+    const int64_t S = p->shard_len;
+    if (S == 0) return GSZ_OK;
+    if (!g_flat || !contrib) { set_error("%s: NULL buffer", who); return GSZ_ERR_INVALID_ARG; }
+    if (misaligned(g_flat)) { set_error("%s: g_flat is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED; }
+    for (int q = 0; q < P; ++q) {
+        if (!contrib[q]) { set_error("%s: contribution %d is NULL", who, q); return GSZ_ERR_INVALID_ARG; }
+        if (misaligned(contrib[q])) { set_error("%s: contribution %d is not 16-byte aligned", who, q); return GSZ_ERR_MISALIGNED; }
+    }
+    const int64_t nvec = S / 8;
+    const dim3 gr(grid_for(nvec, cus));
+    const int pow2 = (P & (P - 1)) == 0;
+    const float invP = pow2 ? 1.0f / (float)P : 0.0f;
+    const int nseg = (int)p->buckets.size();
+    for (int c = 0; c < P; ++c) {      // chunk c of every bucket, summed in ring order ending at rank c
+        RankPtrs rp{};
+        for (int k = 0; k < P; ++k) rp.p[k] = contrib[(c + 1 + k) % P];
+        switch (P) {
+            case 2: launch_reduce<2>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
+            case 4: launch_reduce<4>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
+            case 8: launch_reduce<8>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
+            case 16: launch_reduce<16>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
+            case 32: launch_reduce<32>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
+            case 64: launch_reduce<64>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
+            default: launch_reduce<0>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
+        }
+        if ((rc = launched(who))) return rc;
+    }
+    return GSZ_OK;
+}
+
+extern "C" int gsz_adamw_step(float* master, float* m, float* v, const float* g, int64_t n,
+                              const float* coef, const gsz_adamw_hp* hp, uint16_t* out_bf16,
+                              hipStream_t stream) {
+    const char* who = "gsz_adamw_step";
+    int dev = 0, cus = 0;
+    int rc = current_device(&dev, &cus);
+    if (rc) return rc;
+    if (!hp || !coef || n < 0) { set_error("%s: bad arguments", who); return GSZ_ERR_INVALID_ARG; }
+    if (hp->step < 1) { set_error("%s: step must be >= 1", who); return GSZ_ERR_INVALID_ARG; }
+    if (n % 8 != 0) { set_error("%s: n must be a multiple of 8 (got %lld)", who, (long long)n); return GSZ_ERR_SIZE; }
+    if (n == 0) return GSZ_OK;
+    if (!master || !m || !v || !g || !out_bf16) { set_error("%s: NULL buffer", who); return GSZ_ERR_INVALID_ARG; }
+    if (misaligned(master) || misaligned(m) || misaligned(v) || misaligned(g) || misaligned(out_bf16)) {
+        set_error("%s: a buffer is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED;
+    }
+    const AdamScalars s = adam_scalars(*hp);
+    const int64_t ntile = (n + 511) / 512;
+    int64_t blocks = (ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64);
+    const int64_t cap = (int64_t)cus * kAdamBlocksPerCU;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL((k_adamw<false, true>), dim3((unsigned)blocks), dim3(kAdamBlock), 0, stream, master, m, v, g,
+                       coef, s, nullptr, 0, (int64_t)0, n, nullptr, out_bf16);
     return launched(who);
 }

@@ -226,6 +226,59 @@ int gsz_shard_adamw_step(const gsz_plan* plan, int32_t owner, float* master, flo
 int gsz_allgather_layout_write(const gsz_plan* plan, int32_t owner, const uint16_t* shard_bf16,
                                uint16_t* gathered, hipStream_t stream);
 
+/* --------------------------------------- gradient accumulation --- */
+
+/* Gradient accumulation between synchronisations (the no_sync loop of
+ * "Distributed Training: Data Parallel, Model Parallel and FSDP Strategies",
+ * section Selecting and Tuning Your Strategy; gradients as views of the
+ * buckets, section Inside DDP): for every tensor,
+ *   flat[off_t + j] = bf16(f32(flat[off_t + j]) + f32(grads[t][j]))
+ * (one fp32 add, rounded to nearest even).  Pads are not touched.  The first
+ * micro-batch of a window is written with gsz_bucket_pack.  Arguments as for
+ * gsz_bucket_pack. */
+int gsz_bucket_accumulate(const gsz_plan* plan, const uint16_t* const* grads, uint16_t* flat,
+                          hipStream_t stream);
+
+/* --------------------------------------------- reduce-dtype variant --- */
+
+/* gsz_shard_reduce_mean with bf16 partial sums on the wire ("Data Parallelism:
+ * From Parameter Server to Ring All-Reduce" §8: the communication dtype changes
+ * numerics): after every addition the partial sum is rounded to bf16 (nearest
+ * even), as a ring carrying bf16 does; the owner's sum is divided by P in
+ * fp32.  Same arguments and outputs as gsz_shard_reduce_mean. */
+int gsz_shard_reduce_mean_bf16_wire(const gsz_plan* plan, int32_t owner,
+                                    const uint16_t* const* contrib, int32_t layout, float* g,
+                                    double* partial_out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* ------------------------------------------- unshard side and DDP --- */
+
+/* Inverse of gsz_bucket_pack: params[t][j] = flat[off_t + j] for every tensor
+ * (the reader of all-gathered parameters, "Data Parallelism: DDP, ZeRO and
+ * FSDP", section How FSDP actually runs; the consumer side of ZeRO-1/2's
+ * all-gather, section The three stages).  flat (device, flat_len bf16,
+ * 16-byte aligned); params (host array of n_tensors device pointers, forward
+ * order, any alignment; NULL only for empty tensors).  Pads are not read. */
+int gsz_bucket_unpack(const gsz_plan* plan, const uint16_t* flat, uint16_t* const* params,
+                      hipStream_t stream);
+
+/* DDP / NO_SHARD all-reduce as local arithmetic ("Data parallelism in depth"
+ * §4 and §5.1: all-reduce = reduce-scatter + all-gather; "Data Parallelism:
+ * From Parameter Server to Ring All-Reduce" §5): g_flat[p] = the ring-order
+ * mean of the P bucket-flat contributions at flat position p, where the ring
+ * of chunk c ends at rank c -- so chunk c of g_flat is bit-identical to what
+ * gsz_shard_reduce_mean gives owner c.  contrib (host array of P device
+ * pointers, each flat_len bf16); g_flat (device, flat_len fp32). */
+int gsz_allreduce_mean(const gsz_plan* plan, const uint16_t* const* contrib, float* g_flat,
+                       hipStream_t stream);
+
+/* The replicated (DDP) optimizer update: the AdamW of gsz_shard_adamw_step on
+ * n contiguous elements, bf16 result written contiguously to out_bf16.
+ * n must be a multiple of 8; all pointers device, 16-byte aligned. */
+int gsz_adamw_step(float* master, float* m, float* v, const float* g, int64_t n,
+                   const float* coef, const gsz_adamw_hp* hp, uint16_t* out_bf16,
+                   hipStream_t stream);
+
 /* ------------------------------------------------------------ errors --- */
 
 const char* gsz_last_error(void);

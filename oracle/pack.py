@@ -39,3 +39,26 @@ def owner_view(plan: Plan, flat: np.ndarray, r: int) -> np.ndarray:
     if not parts:
         return flat[:0].copy()
     return np.concatenate(parts)
+
+
+def accumulate(plan: Plan, flat: np.ndarray, grads) -> np.ndarray:
+    """Gradient accumulation into the bucket buffer between synchronisations.
+
+    "Distributed Training: Data Parallel, Model Parallel and FSDP Strategies",
+    section "Selecting and Tuning Your Strategy" (no_sync code): gradients of
+    micro-batches that skip synchronisation accumulate, and only the last
+    micro-batch synchronises.  With gradient_as_bucket_view (section "Inside
+    DDP") the gradients are views of the bucket buffer, so each backward adds
+    into it in the gradient dtype: flat = bf16(f32(flat) + f32(grad)), one
+    round to nearest even per addition.  Pads are untouched.  Returns a new
+    array.
+    """
+    from .bf16 import narrow, widen
+    out = np.array(flat, dtype=np.uint16, copy=True)
+    for t, g in enumerate(grads):
+        g = np.asarray(g, dtype=np.uint16).reshape(-1)
+        if g.size != plan.numel[t]:
+            raise ValueError(f"tensor {t}: {g.size} elements, plan says {plan.numel[t]}")
+        off = plan.tensor_offset[t]
+        out[off:off + g.size] = narrow(widen(out[off:off + g.size]) + widen(g))
+    return out

@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .bf16 import widen
+from .bf16 import narrow, widen
 
 
 def reduce_mean(contribs, r: int) -> np.ndarray:
@@ -42,13 +42,16 @@ def reduce_mean(contribs, r: int) -> np.ndarray:
     return (acc / np.float32(P)).astype(np.float32)
 
 
-def ring_allreduce_sim(plan, flats, rs_wire_bytes: int = 4, ag_wire_bytes: int = 4):
+def ring_allreduce_sim(plan, flats, rs_wire_bytes: int = 4, ag_wire_bytes: int = 4,
+                      bf16_partials: bool = False):
     """Message-passing simulation of ring reduce-scatter then all-gather.
 
     flats[k]: rank k's bucket-major flat bf16 buffer.  Returns
     (results, rs_sent, ag_sent): results[k] is rank k's fp32 flat buffer after
     the all-reduce (mean); rs_sent[k] / ag_sent[k] count the bytes rank k sent
-    in each phase (elements times the wire dtype's size).
+    in each phase (elements times the wire dtype's size).  With bf16_partials
+    every partial sum is rounded to bf16 before it is sent on (and the owner's
+    final sum too), as a ring with a bf16 wire does.
     """
     P = plan.world_size
     if len(flats) != P:
@@ -70,6 +73,8 @@ def ring_allreduce_sim(plan, flats, rs_wire_bytes: int = 4, ag_wire_bytes: int =
             for k, c, m in msgs:
                 dst = (k + 1) % P
                 buf[dst][c] = m + buf[dst][c]
+                if bf16_partials:
+                    buf[dst][c] = widen(narrow(buf[dst][c]))
         for c in range(P):                           # owner c divides its sum
             buf[c][c] = (buf[c][c] / np.float32(P)).astype(np.float32)
         for s in range(P - 1):                       # all-gather
@@ -100,3 +105,22 @@ def central_gather_sim(plan, flats, wire_bytes: int = 4):
     result = (acc / np.float32(P)).astype(np.float32)
     sent = (P - 1) * plan.flat_len * wire_bytes
     return result, sent + recv
+
+
+def reduce_mean_bf16_wire(contribs, r: int) -> np.ndarray:
+    """The same ring, with bf16 partial sums on the wire.
+
+    "Data Parallelism: From Parameter Server to Ring All-Reduce" §8: the
+    gradient dtype of the communication changes both bandwidth and numerical
+    behaviour.  Reading: each hop adds the received bf16 partial sum to the
+    rank's own bf16 value in fp32 and rounds the result to bf16 (round to
+    nearest even) before sending it on; the owner's final sum is widened and
+    divided by P in fp32.  Returns fp32.
+    """
+    P = len(contribs)
+    if not 0 <= r < P:
+        raise ValueError("owner rank out of range")
+    acc = np.asarray(contribs[(r + 1) % P], dtype=np.uint16).copy()
+    for k in range(2, P + 1):
+        acc = narrow(widen(acc) + widen(contribs[(r + k) % P]))
+    return (widen(acc) / np.float32(P)).astype(np.float32)

@@ -85,3 +85,18 @@ def compact_contribs(plan, w, r):
         fill_pieces(t, pieces, w, W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16)
         out.append(t)
     return out
+
+
+def full_state(plan, w):
+    """master, m, v over the whole bucket-major flat buffer (the replicated
+    DDP state), pads zero, placed with the library plan's tensor offsets."""
+    pre = prefix(w.numel)
+    out = []
+    for kind, std, mode in STATE_KINDS:
+        t = torch.zeros(plan.flat_len, dtype=torch.float32, device="cuda")
+        for ti, n in enumerate(w.numel):
+            if n:
+                off = plan.tensor(ti)[0]
+                gen.dev_fill(t[off:off + n], w.cfg_id, kind, 0, pre[ti], std, mode)
+        out.append(t)
+    return out

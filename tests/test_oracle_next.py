@@ -1,0 +1,80 @@
+"""Pins for the oracle's gradient accumulation and bf16-wire ring."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import pack as opack
+from oracle.bf16 import narrow, widen
+from oracle.plan import make_plan
+from oracle.reduce import reduce_mean, reduce_mean_bf16_wire, ring_allreduce_sim
+
+
+def bf16_torch_add(a, b):
+    ta = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    tb = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    return (ta + tb).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_accumulate_matches_torch_bf16_addition():
+    """A bf16 .grad += g in torch (the library routine the training loop runs)."""
+    rng = np.random.default_rng(1)
+    numel = [1000, 37, 4096, 0, 5]
+    plan = make_plan(numel, 4000, 4, align=8)
+    g1 = [narrow(rng.normal(0, 1e-3, n).astype(np.float32)) for n in numel]
+    g2 = [narrow(rng.normal(0, 1e-3, n).astype(np.float32)) for n in numel]
+    flat = opack.pack(plan, g1)
+    acc = opack.accumulate(plan, flat, g2)
+    for t, n in enumerate(numel):
+        off = plan.tensor_offset[t]
+        assert np.array_equal(acc[off:off + n], bf16_torch_add(g1[t], g2[t]))
+    pad = np.ones(plan.flat_len, bool)
+    for t, n in enumerate(numel):
+        pad[plan.tensor_offset[t]:plan.tensor_offset[t] + n] = False
+    assert not acc[pad].any()
+    # accumulating into zeros is packing
+    assert np.array_equal(opack.accumulate(plan, np.zeros(plan.flat_len, np.uint16), g2),
+                          opack.pack(plan, g2))
+
+
+def test_accumulate_is_exact_on_small_integers():
+    numel = [64, 64]
+    plan = make_plan(numel, 1 << 20, 2)
+    rng = np.random.default_rng(2)
+    ints = [rng.integers(-60, 61, (4, n)) for n in numel]         # sums of 4 stay below 2^8
+    flat = np.zeros(plan.flat_len, np.uint16)
+    for k in range(4):
+        flat = opack.accumulate(plan, flat, [narrow(x[k].astype(np.float32)) for x in ints])
+    for t, n in enumerate(numel):
+        off = plan.tensor_offset[t]
+        assert np.array_equal(widen(flat[off:off + n]), ints[t].sum(axis=0).astype(np.float32))
+
+
+def test_bf16_wire_equals_message_passing_ring():
+    rng = np.random.default_rng(3)
+    for P in (2, 3, 8):
+        numel = [int(x) for x in rng.integers(1, 2000, 5)]
+        plan = make_plan(numel, 3000, P, align=4)
+        flats = [opack.pack(plan, [narrow((rng.normal(size=n) * np.exp2(rng.integers(-8, 9, n)))
+                                          .astype(np.float32)) for n in numel]) for _ in range(P)]
+        res, _, _ = ring_allreduce_sim(plan, flats, bf16_partials=True)
+        for r in range(P):
+            g = reduce_mean_bf16_wire([opack.owner_view(plan, f, r) for f in flats], r)
+            assert np.array_equal(g.view(np.uint32), opack.owner_view(plan, res[0], r).view(np.uint32))
+
+
+def test_bf16_wire_drifts_from_fp32_but_not_on_exact_inputs():
+    rng = np.random.default_rng(4)
+    P, n = 8, 100000
+    c = [narrow(rng.normal(0, 1e-3, n).astype(np.float32)) for _ in range(P)]
+    a, b = reduce_mean(c, 0), reduce_mean_bf16_wire(c, 0)
+    assert (a != b).mean() > 0.3                      # per-hop rounding changes most sums
+    # each of the P-1 hops rounds a partial sum to bf16 (8 significant bits: a
+    # relative error of at most u = 2^-8); the rounded partial sums are at most
+    # sum|c| * (1+u)^(P-1); the division by P (a power of two) is exact
+    u = 2.0 ** -8
+    bound = (P - 1) * u * (1 + u) ** (P - 1) * np.sum([np.abs(widen(x)) for x in c], axis=0) / P
+    assert (np.abs(a.astype(np.float64) - b) <= bound * (1 + 1e-6) + 1e-12).all()
+    ints = [narrow(rng.integers(-15, 16, n).astype(np.float32)) for _ in range(P)]
+    assert np.array_equal(reduce_mean(ints, 3), reduce_mean_bf16_wire(ints, 3))
+    one = [c[0]]
+    assert np.array_equal(reduce_mean_bf16_wire(one, 0), widen(c[0]))
