@@ -480,11 +480,16 @@ def main():
     a = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
-    sink = torch.empty(dev.multi_processor_count * 8 * 256, dtype=torch.int32, device="cuda")
+    sink = torch.empty(dev.multi_processor_count * 16 * 256, dtype=torch.int32, device="cuda")
     ceil = {}
+    # the reduce's own pattern without arithmetic: the first 2*S bytes of each
+    # of the P contribution buffers, read at the same offsets
+    nbs = 2 * S // 16 * 16
     for name, fn, nbytes in (("copy", lambda: gen.dev_copy(a, b, nb), 2 * nb),
                              ("read", lambda: gen.dev_read(a, sink, nb), nb),
-                             ("write", lambda: gen.dev_write(b, nb), nb)):
+                             ("write", lambda: gen.dev_write(b, nb), nb),
+                             (f"read_{P}_streams",
+                              lambda: gen.dev_read_streams(contribs, nbs, sink), P * nbs)):
         for _ in range(2):
             fn()
         ms = time_call(fn, reps=10)

@@ -74,6 +74,9 @@ def _load_dev():
         lib.synth_write_dev.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_void_p]
         lib.synth_write_dev.restype = ctypes.c_int
+        lib.synth_read_streams_dev.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                               ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        lib.synth_read_streams_dev.restype = ctypes.c_int
         _dev = lib
     return _dev
 
@@ -156,3 +159,14 @@ def dev_write(dst, nbytes, grid=0, stream=None):
     rc = _load_dev().synth_write_dev(dst.data_ptr(), nbytes, grid, s)
     if rc != 0:
         raise RuntimeError(f"synth_write_dev failed ({rc})")
+
+
+def dev_read_streams(srcs, nbytes, out, grid=0, stream=None):
+    """Reads nbytes from each device tensor in srcs at the same offsets; out must
+    hold grid*256 uint32 (grid 0 = 16 per CU)."""
+    import torch
+    s = torch.cuda.current_stream().cuda_stream if stream is None else stream
+    arr = (ctypes.c_void_p * len(srcs))(*[t.data_ptr() for t in srcs])
+    rc = _load_dev().synth_read_streams_dev(arr, len(srcs), nbytes, out.data_ptr(), grid, s)
+    if rc != 0:
+        raise RuntimeError(f"synth_read_streams_dev failed ({rc})")

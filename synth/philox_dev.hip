@@ -110,6 +110,30 @@ __global__ __launch_bounds__(256) void synth_write_kernel(u32x4* __restrict__ ds
     }
 }
 
+// Read-only stream over ns buffers at the same offsets (the access pattern of
+// a reduction over ns contributions): n16 vectors of 16 bytes from each.
+struct StreamPtrs { const u32x4* p[256]; };
+__global__ __launch_bounds__(256) void synth_read_streams_kernel(StreamPtrs ps, int ns, int64_t n16,
+                                                                 unsigned* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    unsigned acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+        int k = 0;
+        for (; k + 8 <= ns; k += 8) {
+            u32x4 w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = ps.p[k + j][i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc ^= w[j].x ^ w[j].y ^ w[j].z ^ w[j].w;
+        }
+        for (; k < ns; ++k) {
+            const u32x4 w = ps.p[k][i];
+            acc ^= w.x ^ w.y ^ w.z ^ w.w;
+        }
+    }
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 int grid_for(int64_t n, int block) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -161,6 +185,27 @@ int synth_read_dev(const void* src, void* out, int64_t nbytes, int grid, hipStre
     const int g = grid > 0 ? grid : cus * 8;
     hipLaunchKernelGGL(synth_read_kernel, dim3(g), dim3(256), 0, stream, (const u32x4*)src,
                        (unsigned*)out, nbytes / 16);
+    return (int)hipGetLastError();
+}
+
+// Multi-buffer read probe: reads nbytes (a multiple of 16) from each of the ns
+// buffers in srcs (host array of device pointers, 16-byte aligned, ns <= 256).
+// `out` must hold grid * 256 words; grid <= 0 picks 16 blocks per CU.
+int synth_read_streams_dev(const void* const* srcs, int ns, int64_t nbytes, void* out, int grid,
+                           hipStream_t stream) {
+    if (ns < 1 || ns > 256 || nbytes <= 0 || (nbytes & 15) || !out || !srcs) return -1;
+    StreamPtrs ps{};
+    for (int k = 0; k < ns; ++k) {
+        if (!srcs[k] || ((uintptr_t)srcs[k] & 15)) return -1;
+        ps.p[k] = (const u32x4*)srcs[k];
+    }
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const int g = grid > 0 ? grid : cus * 16;
+    hipLaunchKernelGGL(synth_read_streams_kernel, dim3(g), dim3(256), 0, stream, ps, ns, nbytes / 16,
+                       (unsigned*)out);
     return (int)hipGetLastError();
 }
 

@@ -46,3 +46,18 @@ def test_read_and_write_probes():
     # every loaded word is folded into some lane's xor: the lanes' xor is the xor of all words
     assert int(np.bitwise_xor.reduce(sink.cpu().numpy())) == \
         int(np.bitwise_xor.reduce(np.arange(n, dtype=np.int32)))
+
+
+def test_read_streams_probe():
+    g = torch.Generator().manual_seed(5)
+    host_bufs = [torch.randint(-2**31, 2**31 - 1, (1 << 16,), generator=g, dtype=torch.int32)
+                 for _ in range(9)]
+    bufs = [b.cuda() for b in host_bufs]
+    sink = torch.zeros(torch.cuda.get_device_properties(0).multi_processor_count * 16 * 256,
+                       dtype=torch.int32, device="cuda")
+    gen.dev_read_streams(bufs, 4 * (1 << 16), sink)
+    torch.cuda.synchronize()
+    want = 0
+    for b in host_bufs:
+        want ^= int(np.bitwise_xor.reduce(b.numpy()))
+    assert int(np.bitwise_xor.reduce(sink.cpu().numpy())) == want
