@@ -50,6 +50,8 @@ def parse():
                     help="zero: the ZeRO-1/2 shard step (default); ddp: the unsharded step "
                          "(all-reduce, replicated AdamW, unpack)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured as one HIP graph (graph_ms_per_step)")
     ap.add_argument("--copy-gib", type=float, default=4.0,
                     help="size of the plain copy used as the measured HBM ceiling")
     return ap.parse_args()
@@ -413,6 +415,26 @@ def main():
     per = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
            for i, n in enumerate(names)}
 
+    graph_ms = None
+    if args.graph:
+        # The same step captured once into a HIP graph and replayed: the launch
+        # gaps between the calls disappear (this matters for small workloads).
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        log(f"[gpu] captured step: {graph_ms:.3f} ms/step over {args.steps} replays")
+
     # Algorithmic bytes (what the method must move), per call.
     byts = {"bucket_pack": 4 * w.n_params + 2 * (L - w.n_params),
             "shard_reduce_mean": (2 * P + 4) * S,
@@ -519,6 +541,7 @@ def main():
                    "precision": "bf16 grads/params, fp32 accumulation and master/m/v",
                    "step": " + ".join(names) + (" (all-gather layout)" if flat_mode
                                                  else " (shard-layout bf16)")},
+        "graph_ms_per_step": graph_ms,
         "reduce_adamw_ms": fused_ms,
         "reduce_adamw_GBps": fused_gbps,
         "reduce_adamw_frac_of_peak": fused_gbps / HBM_PEAK_GBPS,

@@ -1,0 +1,81 @@
+"""The shard step captured into a HIP graph (torch.cuda.graph) gives, replay
+after replay, the bits of the same steps run eagerly: the library allocates
+nothing, syncs nothing and records no memset inside a step.  Each replay is
+followed by eager work and a synchronisation, and checked."""
+import pytest
+import torch
+
+import gradient_sync_zero_amd as G
+from synth import workloads as W
+from tests import gpu_inputs as GI
+from tests.parity import assert_bits, host
+
+pytestmark = pytest.mark.gpu
+
+
+def make_state(w, plan, owners):
+    flats = []
+    for q in range(w.world_size):
+        f = torch.empty(plan.flat_len, dtype=torch.uint16, device="cuda")
+        G.bucket_pack(plan, GI.rank_grads_separate(w, q), f)
+        flats.append(f)
+    states = {r: GI.owner_state(plan, w, r) for r in owners}
+    return flats, states
+
+
+@pytest.mark.parametrize("cfg,owners", [(0, (0, 1, 2, 3)), (1, (0,))])
+def test_graph_replays_equal_eager_steps(cfg, owners):
+    w = W.by_id(cfg)
+    P = w.world_size
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    my_grads = GI.rank_grads_separate(w, 0)
+    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+
+    def buffers():
+        flats, states = make_state(w, plan, owners)
+        return dict(flats=flats, states=states,
+                    g={r: torch.empty(plan.shard_len, device="cuda") for r in owners},
+                    partials=torch.full((P,), 0.5, dtype=torch.float64, device="cuda"),
+                    coef=torch.empty(1, device="cuda"),
+                    gathered=torch.zeros(plan.flat_len, dtype=torch.uint16, device="cuda"))
+
+    def step(b):
+        G.bucket_pack(plan, my_grads, b["flats"][0])
+        for r in owners:
+            G.shard_reduce_mean(plan, r, b["flats"], G.LAYOUT_BUCKET_FLAT, b["g"][r],
+                                b["partials"][r:r + 1], ws)
+        G.clip_coef(b["partials"], w.hp.max_norm, b["coef"])
+        for r in owners:
+            th, m, v = b["states"][r]
+            G.shard_adamw_step(plan, r, th, m, v, b["g"][r], b["coef"], w.hp, b["gathered"], None)
+
+    def snapshot(b):
+        torch.cuda.synchronize()
+        out = [host(b["gathered"]), host(b["coef"])]
+        for r in owners:
+            out += [host(x) for x in b["states"][r]] + [host(b["g"][r])]
+        return out
+
+    eager = buffers()
+    want = []
+    for _ in range(3):
+        step(eager)
+        want.append(snapshot(eager))
+
+    b = buffers()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(b)
+    torch.cuda.synchronize()
+    # capture recorded the work without running it: the state is still the initial one
+    for k in range(3):
+        graph.replay()
+        junk = torch.randn(1 << 20, device="cuda").sum()        # eager work between replays
+        torch.cuda.synchronize()
+        got = snapshot(b)
+        for i, (x, y) in enumerate(zip(got, want[k])):
+            assert_bits(x, y, f"replay {k}, buffer {i}")
+        del junk
