@@ -83,3 +83,47 @@ def test_central_gather_traffic_grows_with_N():
         res, primary = central_gather_sim(plan, flats)
         assert np.all(res == 1.0)
         assert primary == 2 * (P - 1) * plan.flat_len * 4
+
+
+def _ring_with_fault(plan, flats, fault):
+    """A copy of the message-passing ring with one planted fault (CPU only):
+    'drop' loses the first reduce-scatter message of bucket 0; 'dup' delivers it
+    twice."""
+    P = plan.world_size
+    results = [np.zeros(plan.flat_len, dtype=np.float32) for _ in range(P)]
+    sent = [0] * P
+    for bi, bk in enumerate(plan.buckets):
+        C = bk.chunk
+        buf = [[widen(flats[k][bk.base + c * C: bk.base + (c + 1) * C]).copy()
+                for c in range(P)] for k in range(P)]
+        for s in range(P - 1):
+            msgs = [(k, (k - 1 - s) % P, buf[k][(k - 1 - s) % P].copy()) for k in range(P)]
+            for idx, (k, c, m) in enumerate(msgs):
+                first = bi == 0 and s == 0 and idx == 0
+                if fault == "drop" and first:
+                    continue
+                sent[k] += C * 4
+                buf[(k + 1) % P][c] = m + buf[(k + 1) % P][c]
+                if fault == "dup" and first:
+                    sent[k] += C * 4
+                    buf[(k + 1) % P][c] = m + buf[(k + 1) % P][c]
+        for c in range(P):
+            buf[c][c] = (buf[c][c] / np.float32(P)).astype(np.float32)
+            results[c][bk.base + c * C: bk.base + (c + 1) * C] = buf[c][c]
+    return results, sent
+
+
+@pytest.mark.parametrize("fault", ["drop", "dup"])
+def test_a_lost_or_repeated_message_is_caught(fault):
+    rng = np.random.default_rng(9)
+    P = 4
+    numel = [700, 300, 1200]
+    plan = make_plan(numel, 2000, P, align=4)
+    flats = [opack.pack(plan, [wide_range_bf16(rng, n) for n in numel]) for _ in range(P)]
+    res, sent = _ring_with_fault(plan, flats, fault)
+    M = plan.flat_len * 4
+    traffic_ok = all(s * P == (P - 1) * M for s in sent)
+    mean_ok = all(np.array_equal(
+        opack.owner_view(plan, res[r], r),
+        reduce_mean([opack.owner_view(plan, f, r) for f in flats], r)) for r in range(P))
+    assert not traffic_ok and not mean_ok
