@@ -69,10 +69,22 @@ def ensure_built():
 SHORT = {"k_pack": "k_pack", "k_reduce_mean": "k_reduce_mean", "k_adamw": "k_adamw",
          "k_clip": "k_clip", "k_finalize": "k_finalize", "k_zero_pads": "k_zero_pads",
          "synth_copy_kernel": "copy", "synth_fill_kernel": "synth_fill", "k_ag_write": "k_ag_write",
-         "k_sqnorm": "k_sqnorm"}
+         "k_sqnorm": "k_sqnorm", "synth_read_streams_kernel": "read_streams_probe",
+         "synth_read_kernel": "read_probe", "synth_write_kernel": "write_probe"}
 
 
 def short_name(full):
+    # template instances that move different bytes get their own names
+    if "k_pack<1>" in full:
+        return "k_unpack"
+    if "k_pack<2>" in full:
+        return "k_accumulate"
+    if "k_reduce_mean<" in full:
+        args = [a.strip() for a in full.split("k_reduce_mean<")[1].split(">")[0].split(",")]
+        if len(args) == 5 and args[4] == "true":
+            return "k_reduce_mean_bf16_wire"
+        if len(args) >= 4 and args[3] == "true":
+            return "k_allreduce_mean"
     for k, v in SHORT.items():
         if k in full:
             return v
@@ -80,7 +92,8 @@ def short_name(full):
         return "torch_fill"
     if "rocclr" in full:
         return "hip_runtime_copy"
-    return full.split("(")[0][-40:]
+    name = full.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].split("<")[0][-40:]
 
 
 def summarize_trace(csv_path, workload, command):
