@@ -80,9 +80,16 @@ _lib = None
 
 
 def load():
-    """Loads libgsz.so (raises if it is not built)."""
+    """Loads libgsz.so (raises if it is not built).
+
+    torch is imported first, on purpose: torch ships its own HIP runtime with
+    the same soname (libamdhip64.so.7) but asks for it as libamdhip64.so, so if
+    libgsz pulled in /opt/rocm's copy first, the process would hold two HIP
+    runtimes and torch's would find no GPU.  With torch loaded first, libgsz's
+    dependency resolves to the runtime torch already loaded."""
     global _lib
     if _lib is None:
+        import torch  # noqa: F401  (load order; see above)
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: the HIP library is not built "
                               "(run __graft_entry__.build()); there is no fallback")

@@ -58,6 +58,7 @@ def _load_host():
 def _load_dev():
     global _dev
     if _dev is None:
+        import torch  # noqa: F401  (torch's HIP runtime must be the one loaded first)
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"{DEV_LIB} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(DEV_LIB)

@@ -147,3 +147,18 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         G.shard_reduce_mean(p, 0, [torch.zeros(p.shard_len, dtype=torch.bfloat16)] * 4,
                             G.LAYOUT_SHARD_COMPACT, torch.zeros(p.shard_len))
+
+
+def test_torch_hip_runtime_is_loaded_before_the_library():
+    """Loading the library in a fresh process must leave one HIP runtime
+    mapped: torch's (the binding imports torch before loading libgsz)."""
+    import subprocess
+    import sys
+    code = ("import gradient_sync_zero_amd, synth.gen as g; g._load_dev(); "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"
