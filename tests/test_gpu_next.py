@@ -86,7 +86,8 @@ def test_bf16_wire_reduce_all_owners(cfg):
         assert abs(host(part)[0] - sqnorm_partial(ref)) <= 1e-12 * sqnorm_partial(ref)
         fp32 = reduce_mean(cs, r).astype(np.float64)
         u = 2.0 ** -8       # bf16 unit roundoff; see the oracle pin for the bound
-        bound = (P - 1) * u * (1 + u) ** (P - 1) * np.sum([np.abs(widen(c)) for c in cs], axis=0) / P
+        abs_sum = np.sum([np.abs(widen(c)).astype(np.float64) for c in cs], axis=0)
+        bound = (P - 1) * u * (1 + u) ** (P - 1) * abs_sum / P
         err = np.abs(fp32 - ref)
         assert (err <= bound * (1 + 1e-6) + 1e-12).all()
         worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))

@@ -72,7 +72,8 @@ def test_bf16_wire_drifts_from_fp32_but_not_on_exact_inputs():
     # relative error of at most u = 2^-8); the rounded partial sums are at most
     # sum|c| * (1+u)^(P-1); the division by P (a power of two) is exact
     u = 2.0 ** -8
-    bound = (P - 1) * u * (1 + u) ** (P - 1) * np.sum([np.abs(widen(x)) for x in c], axis=0) / P
+    abs_sum = np.sum([np.abs(widen(x)).astype(np.float64) for x in c], axis=0)
+    bound = (P - 1) * u * (1 + u) ** (P - 1) * abs_sum / P
     assert (np.abs(a.astype(np.float64) - b) <= bound * (1 + 1e-6) + 1e-12).all()
     ints = [narrow(rng.integers(-15, 16, n).astype(np.float32)) for _ in range(P)]
     assert np.array_equal(reduce_mean(ints, 3), reduce_mean_bf16_wire(ints, 3))
