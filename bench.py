@@ -268,7 +268,7 @@ def bench_ddp(args):
     pflat = torch.empty(L, dtype=torch.uint16, device="cuda")
     pbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
     params = [pbuf[s0:s0 + n] for s0, n in zip(GI.prefix(w.numel), w.numel)]
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.flat_len) // 8, dtype=torch.float64, device="cuda")
     part = torch.zeros(1, dtype=torch.float64, device="cuda")
     coef = torch.empty(1, dtype=torch.float32, device="cuda")
     names = ["bucket_pack", "allreduce_mean", "shard_grad_sqnorm", "clip_coef", "adamw_step",
@@ -376,7 +376,7 @@ def main():
         gathered, shard_out = None, torch.zeros(S, dtype=torch.uint16, device="cuda")
     master, m, v = GI.owner_state(plan, w, r)
     g = torch.empty(S, dtype=torch.float32, device="cuda")
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     partials = torch.zeros(P, dtype=torch.float64, device="cuda")
     coef = torch.empty(1, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()

@@ -62,7 +62,7 @@ _SIGS = {
     "gsz_plan_check": [_P, ctypes.c_uint64],
     "gsz_plan_upload": [_P],
     "gsz_ledger_bytes_per_param": [_I32, _I32, ctypes.POINTER(ctypes.c_double)],
-    "gsz_workspace_bytes": [ctypes.POINTER(ctypes.c_size_t)],
+    "gsz_workspace_bytes": [ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
     "gsz_bucket_pack": [_P, _P, _P, _P],
     "gsz_shard_reduce_mean": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_shard_grad_sqnorm": [_P, _I64, _P, _P, ctypes.c_size_t, _P],
@@ -212,9 +212,11 @@ def ledger_bytes_per_param(world_size, zero_stage):
     return out.value
 
 
-def workspace_bytes():
+def workspace_bytes(n):
+    """Device scratch bytes for a shard reduce over n elements (the plan's
+    shard_len) or a squared norm of n values."""
     out = ctypes.c_size_t()
-    _check(load().gsz_workspace_bytes(ctypes.byref(out)))
+    _check(load().gsz_workspace_bytes(int(n), ctypes.byref(out)))
     return out.value
 
 

@@ -10,12 +10,21 @@
 
 namespace gsz {
 
-// Elements per pack tile; a tile is the unit a block copies at a time.
-constexpr int64_t kPackTile = 8192;
+// Elements per pack tile: one block of 256 lanes moves one tile, 16 bytes a lane.
+constexpr int64_t kPackTile = 2048;
 // Tensor pointers per pack launch (they travel in the kernel argument block).
 constexpr int kPackBatch = 256;
-// Upper bound on blocks of the reduction kernels (sizes the caller's workspace).
-constexpr int kMaxRedBlocks = 4096;
+// Blocks of the reductions: one per kRedElems elements, at most kMaxRedGrid
+// (a launch's grid * 256 work-items stays below 2^32); their partials are summed
+// in kFinalBlocks fixed ranges when there are more than kFinalBlocks of them.
+constexpr int64_t kRedElems = 2048;
+constexpr int64_t kMaxRedGrid = (int64_t)1 << 23;
+constexpr int64_t kFinalBlocks = 1024;
+inline int64_t red_blocks(int64_t n) {
+    int64_t b = (n + kRedElems - 1) / kRedElems;
+    if (b > kMaxRedGrid) b = kMaxRedGrid;
+    return b < 1 ? 1 : b;
+}
 
 struct Bucket {
     int32_t first_tensor;  // forward index of the first tensor in bucket order

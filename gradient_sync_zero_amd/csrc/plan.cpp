@@ -209,9 +209,9 @@ extern "C" int gsz_ledger_bytes_per_param(int32_t P, int32_t zero_stage, double*
     return GSZ_OK;
 }
 
-extern "C" int gsz_workspace_bytes(size_t* out) {
-    if (!out) { set_error("gsz_workspace_bytes: NULL argument"); return GSZ_ERR_INVALID_ARG; }
-    *out = (size_t)gsz::kMaxRedBlocks * sizeof(double);
+extern "C" int gsz_workspace_bytes(int64_t n, size_t* out) {
+    if (!out || n < 0) { set_error("gsz_workspace_bytes: bad argument"); return GSZ_ERR_INVALID_ARG; }
+    *out = (size_t)(gsz::red_blocks(n) + gsz::kFinalBlocks) * sizeof(double);
     return GSZ_OK;
 }
 

@@ -152,9 +152,14 @@ int gsz_plan_upload(gsz_plan* plan);
  * 16, 1: 4 + 12/P, 2: 2 + 14/P, 3: 16/P. */
 int gsz_ledger_bytes_per_param(int32_t world_size, int32_t zero_stage, double* out);
 
-/* Bytes of device scratch that gsz_shard_reduce_mean and
- * gsz_shard_grad_sqnorm need (per call in flight).  Needs no initialisation. */
-int gsz_workspace_bytes(size_t* out);
+/* *out = bytes of device scratch that gsz_shard_reduce_mean (n = the plan's
+ * shard_len) or gsz_shard_grad_sqnorm (n = its element count) needs, per call
+ * in flight: one fp64 partial per 2048 elements (at most 2^23 of them) plus
+ * 1024 for the second stage of the fixed-order sum, i.e. 8 * (min(ceil(n /
+ * 2048), 2^23) + 1024) with ceil(0 / 2048) taken as 1.  About 0.4% of the
+ * bytes of the fp32 values it reduces.  Needs no initialisation.
+ * GSZ_ERR_INVALID_ARG if n < 0 or out is NULL. */
+int gsz_workspace_bytes(int64_t n, size_t* out);
 
 /* -------------------------------------------------------------- steps --- */
 

@@ -129,7 +129,13 @@ def test_argument_validation():
         p.bucket(1)
     with pytest.raises(G.GszError):
         p.tensor(-1)
-    assert G.workspace_bytes() >= 8 * 1024
+    # one fp64 partial per 2048 elements (at most 2^23 of them, at least one)
+    # plus 1024 second-stage sums
+    for n, blocks in ((0, 1), (1, 1), (2048, 1), (2049, 2), (842301952, 411281),
+                      (1077760128, 526251), (1 << 34, 1 << 23), ((1 << 34) + 1, 1 << 23)):
+        assert G.workspace_bytes(n) == 8 * (blocks + 1024), n
+    with pytest.raises(G.GszError):
+        G.workspace_bytes(-1)
     lib = G.load()
     assert lib.gsz_status_string(-5) == b"plan mismatch"
     assert lib.gsz_plan_destroy(None) == 0

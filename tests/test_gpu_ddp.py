@@ -37,7 +37,7 @@ def test_ddp_step_and_unpack(cfg):
         flats.append(flat)
     g_flat = torch.full((plan.flat_len,), float("nan"), dtype=torch.float32, device="cuda")
     G.allreduce_mean(plan, flats, g_flat)
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.flat_len) // 8, dtype=torch.float64, device="cuda")
     part = torch.zeros(1, dtype=torch.float64, device="cuda")
     G.shard_grad_sqnorm(g_flat, part, ws)
     coef = torch.empty(1, dtype=torch.float32, device="cuda")

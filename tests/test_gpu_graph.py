@@ -29,7 +29,7 @@ def test_graph_replays_equal_eager_steps(cfg, owners):
     P = w.world_size
     plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
     my_grads = GI.rank_grads_separate(w, 0)
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
 
     def buffers():
         flats, states = make_state(w, plan, owners)

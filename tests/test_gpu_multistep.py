@@ -48,7 +48,7 @@ def test_four_steps_with_checkpoint_resume():
     P = w.world_size
     plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
     oplan = make_plan(w.numel, w.bucket_cap_bytes, P)
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     states = {r: GI.owner_state(plan, w, r) for r in range(P)}
     th, m, v = OI.full_state(oplan, w)
     for k in range(4):

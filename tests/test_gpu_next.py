@@ -69,7 +69,7 @@ def test_bf16_wire_reduce_all_owners(cfg):
         G.bucket_pack(plan, GI.rank_grads_separate(w, q), f)
         flats.append(f)
     oflats = [OI.rank_flat(oplan, w, q) for q in range(P)]
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     part = torch.zeros(1, dtype=torch.float64, device="cuda")
     worst, changed, n_all = 0.0, 0, 0
     for r in range(P):

@@ -86,7 +86,7 @@ def test_full_size_sampled(cfg, layout, owners):
             ref = OI.values_at(w, W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16, pidx)
             assert_bits(gather_dev(flats[q], fpos), ref, f"pack rank {q} (sampled)")
 
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     for r in owners:
         contribs = flats if flats is not None else None
         if contribs is None:

@@ -29,7 +29,7 @@ def say(*a):
 def run_gpu_step(w, plan, flats_dev, layout=G.LAYOUT_BUCKET_FLAT, compacts=None):
     """All owners: reduce (+partial), clip, AdamW.  Returns host copies."""
     P = w.world_size
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     partials = torch.zeros(P, dtype=torch.float64, device="cuda")
     gs = []
     for r in range(P):
@@ -110,7 +110,7 @@ def test_full_step_all_owners(cfg):
     ag = torch.full((plan.flat_len,), 0x7777, dtype=torch.uint16, device="cuda")
     for r in range(w.world_size):
         G.allgather_layout_write(plan, r, out["shards_dev"][r], ag)
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     sq = torch.zeros(w.world_size, dtype=torch.float64, device="cuda")
     for r in range(w.world_size):
         G.shard_grad_sqnorm(out["gs_dev"][r], sq[r:r + 1], ws)
@@ -186,7 +186,7 @@ def test_reduce_every_rank_count(P):
         dev = [torch.from_numpy(gq.view(np.int16).copy()).view(torch.uint16).cuda() for gq in grads]
         G.bucket_pack(plan, dev, flat)
         flats_dev.append(flat)
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     part = torch.zeros(1, dtype=torch.float64, device="cuda")
     for r in sorted({0, P // 2, P - 1}):
         g = torch.empty(plan.shard_len, dtype=torch.float32, device="cuda")
@@ -197,10 +197,10 @@ def test_reduce_every_rank_count(P):
 
 
 def test_edge_plans_on_gpu():
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
     part = torch.full((1,), 7.0, dtype=torch.float64, device="cuda")
     # no tensors at all: every call is a no-op and the partial is zero
     plan = G.Plan([], 1 << 20, 4).upload()
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     dummy = torch.zeros(8, dtype=torch.uint16, device="cuda")
     G.shard_reduce_mean(plan, 2, [dummy] * 4, G.LAYOUT_SHARD_COMPACT,
                         torch.zeros(8, device="cuda"), part, ws)
@@ -275,6 +275,13 @@ def test_errors_are_reported_not_launched():
     with pytest.raises(G.GszError) as e:
         G.shard_reduce_mean(plan, 0, c, G.LAYOUT_SHARD_COMPACT, g, part, small_ws)
     assert e.value.name == "GSZ_ERR_SIZE"
+    short_ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8 - 1, dtype=torch.float64, device="cuda")
+    with pytest.raises(G.GszError) as e:
+        G.shard_reduce_mean(plan, 0, c, G.LAYOUT_SHARD_COMPACT, g, part, short_ws)
+    assert e.value.name == "GSZ_ERR_SIZE"
+    with pytest.raises(G.GszError) as e:
+        G.shard_grad_sqnorm(g, part, short_ws[:G.workspace_bytes(g.numel()) // 8 - 1])
+    assert e.value.name == "GSZ_ERR_SIZE"
     st = [torch.zeros(plan.shard_len, device="cuda") for _ in range(3)]
     coef = torch.ones(1, device="cuda")
     with pytest.raises(G.GszError):
@@ -289,7 +296,7 @@ def test_bitwise_deterministic_run_to_run():
     w = W.gpt2_small()
     plan = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size).upload()
     comp = GI.compact_contribs(plan, w, 3)
-    ws = torch.zeros(G.workspace_bytes() // 8, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     res = []
     for _ in range(3):
         g = torch.empty(plan.shard_len, dtype=torch.float32, device="cuda")
