@@ -85,6 +85,8 @@ def short_name(full):
             return "k_reduce_mean_bf16_wire"
         if len(args) >= 4 and args[3] == "true":
             return "k_allreduce_mean"
+    if "k_finalize_ranges" in full:
+        return "k_finalize_ranges"
     for k, v in SHORT.items():
         if k in full:
             return v

@@ -10,8 +10,9 @@
 
 namespace gsz {
 
-// Elements per pack tile: one block of 256 lanes moves one tile, 16 bytes a lane.
-constexpr int64_t kPackTile = 2048;
+// Elements per pack tile: one block of 64 lanes (one wave) moves one tile,
+// 16 bytes a lane.
+constexpr int64_t kPackTile = 512;
 // Tensor pointers per pack launch (they travel in the kernel argument block).
 constexpr int kPackBatch = 256;
 // Blocks of the reductions: one per kRedElems elements, at most kMaxRedGrid
