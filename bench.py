@@ -509,19 +509,20 @@ def main():
                                          for n, v in standalone.items()))
     del shard_bf16
 
-    # Plain streaming probes, run after the timed steps so that their
-    # allocations do not fragment the memory the working set was placed in:
-    # copy (the practical ceiling for half-read/half-write traffic and the
-    # calibration kernel of the counter runs), read-only and write-only.
+    # Plain streaming probes in the kernels' launch shape, run after the timed
+    # steps so that their allocations do not fragment the memory the working set
+    # was placed in: copy (the practical ceiling for half-read/half-write traffic
+    # and the calibration kernel of the counter runs), read-only and write-only.
     nb = int(args.copy_gib * (1 << 30)) // 16 * 16
     a = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
-    sink = torch.empty(dev.multi_processor_count * 16 * 256, dtype=torch.int32, device="cuda")
-    ceil = {}
     # the reduce's own pattern without arithmetic: the first 2*S bytes of each
     # of the P contribution buffers, read at the same offsets
     nbs = 2 * S // 16 * 16
+    sink = torch.empty(max(gen.probe_out_words(nb), gen.probe_out_words(nbs)), dtype=torch.int32,
+                       device="cuda")
+    ceil = {}
     for name, fn, nbytes in (("copy", lambda: gen.dev_copy(a, b, nb), 2 * nb),
                              ("read", lambda: gen.dev_read(a, sink, nb), nb),
                              ("write", lambda: gen.dev_write(b, nb), nb),

@@ -78,6 +78,8 @@ def _load_dev():
         lib.synth_read_streams_dev.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                                ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         lib.synth_read_streams_dev.restype = ctypes.c_int
+        lib.synth_probe_out_words.argtypes = [ctypes.c_int64]
+        lib.synth_probe_out_words.restype = ctypes.c_int64
         _dev = lib
     return _dev
 
@@ -145,9 +147,21 @@ def dev_copy(src, dst, nbytes, grid=0, stream=None):
         raise RuntimeError(f"synth_copy_dev failed ({rc})")
 
 
+def probe_out_words(nbytes, grid=0):
+    """uint32 words a read probe over nbytes (per buffer) writes: 4 per block."""
+    return 4 * grid if grid > 0 else int(_load_dev().synth_probe_out_words(nbytes))
+
+
+def _check_sink(out, nbytes, grid):
+    need = probe_out_words(nbytes, grid)
+    if out.element_size() != 4 or out.numel() < need:
+        raise ValueError(f"probe sink needs {need} 32-bit words, got {out.numel()}")
+
+
 def dev_read(src, out, nbytes, grid=0, stream=None):
-    """Read-only bandwidth probe; out must hold grid*256 uint32 (grid 0 = 8 per CU)."""
+    """Read-only bandwidth probe; out must hold probe_out_words(nbytes, grid) uint32."""
     import torch
+    _check_sink(out, nbytes, grid)
     s = torch.cuda.current_stream().cuda_stream if stream is None else stream
     rc = _load_dev().synth_read_dev(src.data_ptr(), out.data_ptr(), nbytes, grid, s)
     if rc != 0:
@@ -164,8 +178,9 @@ def dev_write(dst, nbytes, grid=0, stream=None):
 
 def dev_read_streams(srcs, nbytes, out, grid=0, stream=None):
     """Reads nbytes from each device tensor in srcs at the same offsets; out must
-    hold grid*256 uint32 (grid 0 = 16 per CU)."""
+    hold probe_out_words(nbytes, grid) uint32."""
     import torch
+    _check_sink(out, nbytes, grid)
     s = torch.cuda.current_stream().cuda_stream if stream is None else stream
     arr = (ctypes.c_void_p * len(srcs))(*[t.data_ptr() for t in srcs])
     rc = _load_dev().synth_read_streams_dev(arr, len(srcs), nbytes, out.data_ptr(), grid, s)

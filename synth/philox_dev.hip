@@ -1,5 +1,6 @@
-// Device (gfx950) side of the seeded input generator, plus a plain copy kernel
-// used as the measured HBM ceiling and as the byte-counter calibration.
+// Device (gfx950) side of the seeded input generator, plus plain streaming
+// probes (copy, read, write, multi-buffer read) that measure HBM ceilings; the
+// copy is also the byte-counter calibration kernel.
 //
 // Same generator as the host side: Philox4x32 with 10 rounds, from its
 // published definition (Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
@@ -53,32 +54,30 @@ __global__ void synth_fill_kernel(uint32_t seed, uint32_t key1, uint64_t start, 
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Plain copy of n16 16-byte vectors.  Each block copies runs of 8 * 256
-// vectors (8 loads in flight per lane, then 8 stores), with nontemporal hints:
-// the fastest of the simple copy variants measured on MI355X.
+// Streaming probes: one 16-byte vector per lane per tile of 256 vectors, one
+// short block per tile and a grid that covers the data (blocks stride over the
+// rest when the grid is capped) -- the launch shape that moves the most bytes
+// per second on MI355X.  The copy is also the byte-counter calibration kernel.
+constexpr int64_t kProbeMaxGrid = (int64_t)1 << 23;
+
 __global__ __launch_bounds__(256) void synth_copy_kernel(const u32x4* __restrict__ src,
                                                          u32x4* __restrict__ dst, int64_t n16) {
-    constexpr int U = 8;
-    const int64_t per_block = 256 * U;
-    const int64_t nblk = (n16 + per_block - 1) / per_block;
-    for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-        const int64_t base = blk * per_block + threadIdx.x;
-        u32x4 w[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int64_t i = base + (int64_t)k * 256;
-            if (i < n16) w[k] = __builtin_nontemporal_load(src + i);
-        }
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int64_t i = base + (int64_t)k * 256;
-            if (i < n16) __builtin_nontemporal_store(w[k], dst + i);
-        }
-    }
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
-// Read-only stream of n16 vectors (8 nontemporal loads in flight per lane); one
-// word per thread is written so the loads are not removed.
+// XOR of the 64 lanes' words, written by lane 0 to out[wave]: one word per
+// wave keeps every load live without a barrier.
+__device__ __forceinline__ void wave_xor_out(unsigned acc, unsigned* __restrict__ out) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc ^= (unsigned)__shfl_xor((int)acc, o, 64);
+    if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
+}
+
+// Read-only stream of n16 vectors; out[4 * block + wave] = XOR of the words
+// its wave loaded.  Reads alone go fastest as a grid-stride loop with 8
+// nontemporal loads in flight per lane and 8 blocks per CU (7.0 TB/s against
+// 6.6-6.7 for one short block per tile).
 __global__ __launch_bounds__(256) void synth_read_kernel(const u32x4* __restrict__ src,
                                                          unsigned* __restrict__ out, int64_t n16) {
     constexpr int U = 8;
@@ -94,24 +93,19 @@ __global__ __launch_bounds__(256) void synth_read_kernel(const u32x4* __restrict
             }
         }
     }
-    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+    wave_xor_out(acc, out);
 }
 
-// Write-only stream of n16 vectors (4 stores per lane per iteration).
+// Write-only stream of n16 vectors: dst[i] = {i, 1, 2, 3}.
 __global__ __launch_bounds__(256) void synth_write_kernel(u32x4* __restrict__ dst, int64_t n16) {
-    constexpr int U = 4;
     const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < n16; b += stride * U) {
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int64_t i = b + k * stride;
-            if (i < n16) dst[i] = u32x4{(unsigned)i, 1u, 2u, 3u};
-        }
-    }
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+        dst[i] = u32x4{(unsigned)i, 1u, 2u, 3u};
 }
 
 // Read-only stream over ns buffers at the same offsets (the access pattern of
-// a reduction over ns contributions): n16 vectors of 16 bytes from each.
+// a reduction over ns contributions): n16 vectors of 16 bytes from each; out
+// as for the single-buffer read.
 struct StreamPtrs { const u32x4* p[256]; };
 __global__ __launch_bounds__(256) void synth_read_streams_kernel(StreamPtrs ps, int ns, int64_t n16,
                                                                  unsigned* __restrict__ out) {
@@ -131,7 +125,22 @@ __global__ __launch_bounds__(256) void synth_read_streams_kernel(StreamPtrs ps, 
             acc ^= w.x ^ w.y ^ w.z ^ w.w;
         }
     }
-    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+    wave_xor_out(acc, out);
+}
+
+// Blocks of a probe over n16 vectors: one per 256 vectors, capped.
+int64_t probe_grid(int64_t n16) {
+    const int64_t g = (n16 + 255) / 256;
+    return g < 1 ? 1 : (g < kProbeMaxGrid ? g : kProbeMaxGrid);
+}
+
+// Blocks of the single-buffer read probe: 8 per CU.
+int64_t read_grid() {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    return (int64_t)cus * 8;
 }
 
 int grid_for(int64_t n, int block) {
@@ -162,35 +171,38 @@ int synth_fill_dev(uint32_t seed, uint32_t key1, uint64_t start, int64_t n, floa
     return (int)hipGetLastError();
 }
 
-// Copies nbytes (a multiple of 16; both pointers 16-byte aligned).
+// Copies nbytes (a multiple of 16; both pointers 16-byte aligned).  grid <= 0
+// covers the data (one block per 256 vectors).
 int synth_copy_dev(const void* src, void* dst, int64_t nbytes, int grid, hipStream_t stream) {
     if (nbytes < 0 || (nbytes & 15) || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return -1;
     if (nbytes == 0) return 0;
-    const int block = 256;
     const int64_t n16 = nbytes / 16;
-    const int g = grid > 0 ? grid : grid_for(n16, block);
-    hipLaunchKernelGGL(synth_copy_kernel, dim3(g), dim3(block), 0, stream,
+    const int64_t g = grid > 0 ? grid : probe_grid(n16);
+    hipLaunchKernelGGL(synth_copy_kernel, dim3((unsigned)g), dim3(256), 0, stream,
                        (const u32x4*)src, (u32x4*)dst, n16);
     return (int)hipGetLastError();
 }
 
+// Words of `out` that either read probe over nbytes (per buffer) may write
+// with grid <= 0: 4 per block (one per wave).
+int64_t synth_probe_out_words(int64_t nbytes) {
+    const int64_t a = probe_grid(nbytes / 16), b = read_grid();
+    return 4 * (a > b ? a : b);
+}
+
 // Read-only probe over nbytes of src (a multiple of 16, 16-byte aligned).
-// `out` must hold grid * 256 words; grid <= 0 picks 8 blocks per CU.
+// `out` must hold 4 * grid words (grid <= 0: 8 blocks per CU).
 int synth_read_dev(const void* src, void* out, int64_t nbytes, int grid, hipStream_t stream) {
     if (nbytes <= 0 || (nbytes & 15) || ((uintptr_t)src & 15) || !out) return -1;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    const int g = grid > 0 ? grid : cus * 8;
-    hipLaunchKernelGGL(synth_read_kernel, dim3(g), dim3(256), 0, stream, (const u32x4*)src,
+    const int64_t g = grid > 0 ? grid : read_grid();
+    hipLaunchKernelGGL(synth_read_kernel, dim3((unsigned)g), dim3(256), 0, stream, (const u32x4*)src,
                        (unsigned*)out, nbytes / 16);
     return (int)hipGetLastError();
 }
 
 // Multi-buffer read probe: reads nbytes (a multiple of 16) from each of the ns
 // buffers in srcs (host array of device pointers, 16-byte aligned, ns <= 256).
-// `out` must hold grid * 256 words; grid <= 0 picks 16 blocks per CU.
+// `out` as for synth_read_dev.
 int synth_read_streams_dev(const void* const* srcs, int ns, int64_t nbytes, void* out, int grid,
                            hipStream_t stream) {
     if (ns < 1 || ns > 256 || nbytes <= 0 || (nbytes & 15) || !out || !srcs) return -1;
@@ -199,25 +211,17 @@ int synth_read_streams_dev(const void* const* srcs, int ns, int64_t nbytes, void
         if (!srcs[k] || ((uintptr_t)srcs[k] & 15)) return -1;
         ps.p[k] = (const u32x4*)srcs[k];
     }
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    const int g = grid > 0 ? grid : cus * 16;
-    hipLaunchKernelGGL(synth_read_streams_kernel, dim3(g), dim3(256), 0, stream, ps, ns, nbytes / 16,
-                       (unsigned*)out);
+    const int64_t g = grid > 0 ? grid : probe_grid(nbytes / 16);
+    hipLaunchKernelGGL(synth_read_streams_kernel, dim3((unsigned)g), dim3(256), 0, stream, ps, ns,
+                       nbytes / 16, (unsigned*)out);
     return (int)hipGetLastError();
 }
 
-// Write-only probe over nbytes of dst; grid <= 0 picks 2 blocks per CU.
+// Write-only probe over nbytes of dst (a multiple of 16, 16-byte aligned).
 int synth_write_dev(void* dst, int64_t nbytes, int grid, hipStream_t stream) {
     if (nbytes <= 0 || (nbytes & 15) || ((uintptr_t)dst & 15)) return -1;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    const int g = grid > 0 ? grid : cus * 2;
-    hipLaunchKernelGGL(synth_write_kernel, dim3(g), dim3(256), 0, stream, (u32x4*)dst, nbytes / 16);
+    const int64_t g = grid > 0 ? grid : probe_grid(nbytes / 16);
+    hipLaunchKernelGGL(synth_write_kernel, dim3((unsigned)g), dim3(256), 0, stream, (u32x4*)dst, nbytes / 16);
     return (int)hipGetLastError();
 }
 

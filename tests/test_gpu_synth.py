@@ -34,8 +34,9 @@ def test_copy_probe():
 def test_read_and_write_probes():
     n = 1 << 22
     a = torch.arange(n, dtype=torch.int32, device="cuda")
-    sink = torch.zeros(torch.cuda.get_device_properties(0).multi_processor_count * 8 * 256,
-                       dtype=torch.int32, device="cuda")
+    sink = torch.zeros(gen.probe_out_words(n * 4), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):                       # a short sink is refused on the host
+        gen.dev_read(a, sink[:-1], n * 4)
     gen.dev_read(a, sink, n * 4)
     b = torch.zeros(n, dtype=torch.int32, device="cuda")
     gen.dev_write(b, n * 4)
@@ -53,8 +54,7 @@ def test_read_streams_probe():
     host_bufs = [torch.randint(-2**31, 2**31 - 1, (1 << 16,), generator=g, dtype=torch.int32)
                  for _ in range(9)]
     bufs = [b.cuda() for b in host_bufs]
-    sink = torch.zeros(torch.cuda.get_device_properties(0).multi_processor_count * 16 * 256,
-                       dtype=torch.int32, device="cuda")
+    sink = torch.zeros(gen.probe_out_words(4 * (1 << 16)), dtype=torch.int32, device="cuda")
     gen.dev_read_streams(bufs, 4 * (1 << 16), sink)
     torch.cuda.synchronize()
     want = 0
