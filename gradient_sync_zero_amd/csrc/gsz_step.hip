@@ -414,15 +414,14 @@ __global__ __launch_bounds__(kBlock) void k_ag_write(const uint16_t* __restrict_
 // ------------------------------------------------------------ host side --
 
 std::atomic<int> g_dev_state[64];   // 0 unknown, 1 gfx950, -1 other
-std::atomic<int> g_dev_cus[64];
 
 int hip_fail(const char* what, hipError_t e) {
     set_error("%s: %s", what, hipGetErrorString(e));
     return GSZ_ERR_HIP;
 }
 
-// Current device, checked to be gfx950; *cus receives its compute-unit count.
-int current_device(int* dev_out, int* cus) {
+// Current device, checked to be gfx950.
+int current_device(int* dev_out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail("hipGetDevice", e);
@@ -433,12 +432,10 @@ int current_device(int* dev_out, int* cus) {
         e = hipGetDeviceProperties(&prop, dev);
         if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
         st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
-        g_dev_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256);
         g_dev_state[dev].store(st);
     }
     if (st != 1) { set_error("device %d is not gfx950 (MI355X); this library targets gfx950 only", dev); return GSZ_ERR_DEVICE; }
     *dev_out = dev;
-    if (cus) *cus = g_dev_cus[dev].load();
     return GSZ_OK;
 }
 
@@ -486,10 +483,10 @@ AdamScalars adam_scalars(const gsz_adamw_hp& hp) {
 }
 
 // Checks a plan for a device call: uploaded to the current device, vector granule.
-int check_plan(const gsz_plan* p, const char* who, int* cus) {
+int check_plan(const gsz_plan* p, const char* who) {
     if (!p) { set_error("%s: NULL plan", who); return GSZ_ERR_INVALID_ARG; }
     int dev = 0;
-    int rc = current_device(&dev, cus);
+    int rc = current_device(&dev);
     if (rc) return rc;
     if (!p->dev_mem || p->device != dev) {
         set_error("%s: plan has no device tables on device %d (call gsz_plan_upload)", who, dev);
@@ -557,7 +554,7 @@ extern "C" int gsz_plan_destroy(gsz_plan* p) {
 extern "C" int gsz_plan_upload(gsz_plan* p) {
     if (!p) { set_error("gsz_plan_upload: NULL plan"); return GSZ_ERR_INVALID_ARG; }
     int dev = 0;
-    int rc = current_device(&dev, nullptr);
+    int rc = current_device(&dev);
     if (rc) return rc;
     std::lock_guard<std::mutex> lock(p->mu);
     if (p->dev_mem && p->device == dev) return GSZ_OK;
@@ -597,8 +594,7 @@ namespace {
 // the T tensor pointers (sources for kPack/kAccumulate, destinations for kUnpack).
 int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, uint16_t* flat, int mode,
              hipStream_t stream, const char* who) {
-    int cus = 0;
-    int rc = check_plan(p, who, &cus);
+    int rc = check_plan(p, who);
     if (rc) return rc;
     const int T = (int)p->numel.size();
     if (p->flat_len == 0) return GSZ_OK;
@@ -649,8 +645,7 @@ namespace {
 int reduce_impl(const gsz_plan* p, int32_t owner, const uint16_t* const* contrib, int32_t layout,
                 float* g, double* partial_out, void* ws, size_t ws_bytes, hipStream_t stream,
                 bool wire16, const char* who) {
-    int cus = 0;
-    int rc = check_plan(p, who, &cus);
+    int rc = check_plan(p, who);
     if (rc) return rc;
     if ((rc = check_owner(p, owner, who))) return rc;
     if (layout != GSZ_LAYOUT_BUCKET_FLAT && layout != GSZ_LAYOUT_SHARD_COMPACT) {
@@ -723,8 +718,8 @@ extern "C" int gsz_shard_reduce_mean_bf16_wire(const gsz_plan* p, int32_t owner,
 extern "C" int gsz_shard_grad_sqnorm(const float* g, int64_t n, double* partial_out, void* ws,
                                      size_t ws_bytes, hipStream_t stream) {
     const char* who = "gsz_shard_grad_sqnorm";
-    int dev = 0, cus = 0;
-    int rc = current_device(&dev, &cus);
+    int dev = 0;
+    int rc = current_device(&dev);
     if (rc) return rc;
     if (n < 0 || !partial_out || (n > 0 && !g)) { set_error("%s: bad arguments", who); return GSZ_ERR_INVALID_ARG; }
     size_t need = 0;
@@ -746,7 +741,7 @@ extern "C" int gsz_clip_coef(const double* partials, int32_t n_partials, float m
                              hipStream_t stream) {
     const char* who = "gsz_clip_coef";
     int dev = 0;
-    int rc = current_device(&dev, nullptr);
+    int rc = current_device(&dev);
     if (rc) return rc;
     if (n_partials < 0 || (n_partials > 0 && !partials) || !coef_out) {
         set_error("%s: bad arguments", who); return GSZ_ERR_INVALID_ARG;
@@ -761,8 +756,7 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
                                     const gsz_adamw_hp* hp, uint16_t* gathered,
                                     uint16_t* shard_bf16, hipStream_t stream) {
     const char* who = "gsz_shard_adamw_step";
-    int cus = 0;
-    int rc = check_plan(p, who, &cus);
+    int rc = check_plan(p, who);
     if (rc) return rc;
     if ((rc = check_owner(p, owner, who))) return rc;
     if (!hp || !coef) { set_error("%s: NULL hyperparameters or coefficient", who); return GSZ_ERR_INVALID_ARG; }
@@ -794,8 +788,7 @@ extern "C" int gsz_allgather_layout_write(const gsz_plan* p, int32_t owner,
                                           const uint16_t* shard_bf16, uint16_t* gathered,
                                           hipStream_t stream) {
     const char* who = "gsz_allgather_layout_write";
-    int cus = 0;
-    int rc = check_plan(p, who, &cus);
+    int rc = check_plan(p, who);
     if (rc) return rc;
     if ((rc = check_owner(p, owner, who))) return rc;
     const int64_t S = p->shard_len;
@@ -817,8 +810,7 @@ extern "C" int gsz_bucket_unpack(const gsz_plan* p, const uint16_t* flat, uint16
 extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* contrib, float* g_flat,
                                   hipStream_t stream) {
     const char* who = "gsz_allreduce_mean";
-    int cus = 0;
-    int rc = check_plan(p, who, &cus);
+    int rc = check_plan(p, who);
     if (rc) return rc;
     const int P = p->P;
     const int64_t S = p->shard_len;
@@ -855,8 +847,8 @@ extern "C" int gsz_adamw_step(float* master, float* m, float* v, const float* g,
                               const float* coef, const gsz_adamw_hp* hp, uint16_t* out_bf16,
                               hipStream_t stream) {
     const char* who = "gsz_adamw_step";
-    int dev = 0, cus = 0;
-    int rc = current_device(&dev, &cus);
+    int dev = 0;
+    int rc = current_device(&dev);
     if (rc) return rc;
     if (!hp || !coef || n < 0) { set_error("%s: bad arguments", who); return GSZ_ERR_INVALID_ARG; }
     if (hp->step < 1) { set_error("%s: step must be >= 1", who); return GSZ_ERR_INVALID_ARG; }
