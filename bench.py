@@ -98,6 +98,14 @@ def short_name(full):
     return name.split("(")[0].split("<")[0][-40:]
 
 
+def gpu_step_stats(ev):
+    """Mean, median and min over the timed steps of the GPU time from each
+    step's first event to its last."""
+    import numpy as np
+    t = [e[0].elapsed_time(e[-1]) for e in ev]
+    return dict(mean=float(np.mean(t)), median=float(np.median(t)), min=float(np.min(t)))
+
+
 def summarize_trace(csv_path, workload, command):
     import csv
     rows = list(csv.DictReader(open(csv_path)))
@@ -297,12 +305,15 @@ def bench_ddp(args):
         step(ev[k])
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) / args.steps * 1e3
-    per = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
-           for i, n in enumerate(names)}
+    samples = {n: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]
+               for i, n in enumerate(names)}
+    per = {n: float(np.mean(v)) for n, v in samples.items()}
+    step_gpu = gpu_step_stats(ev)
     byts = {"bucket_pack": 4 * w.n_params + 2 * (L - w.n_params),
             "allreduce_mean": (2 * P + 4) * L, "shard_grad_sqnorm": 4 * L, "clip_coef": 20,
             "adamw_step": 30 * L, "bucket_unpack": 4 * w.n_params}
-    kern = {n: dict(ms=per[n], bytes=byts[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9) for n in names}
+    kern = {n: dict(ms=per[n], ms_median=float(np.median(samples[n])), ms_min=float(np.min(samples[n])),
+                    bytes=byts[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9) for n in names}
     step_gbps = sum(byts.values()) / (ms_step * 1e-3) / 1e9
     log(f"[gpu] DDP {w.name}: {ms_step:.3f} ms/step; " + "; ".join(
         f"{n} {kern[n]['ms']:.3f} ms {kern[n]['GBps']:.0f} GB/s" for n in names))
@@ -314,7 +325,8 @@ def bench_ddp(args):
         "data": "synthetic",
         "config": {"workload": w.name, "variant": "ddp", "world_size_P": P,
                    "model_params": w.n_params, "step": " + ".join(names)},
-        "hbm_GBps": step_gbps, "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS, "kernels": kern}),
+        "hbm_GBps": step_gbps, "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "step_ms_gpu": step_gpu, "kernels": kern}),
         flush=True)
 
 
@@ -427,8 +439,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    per = {n: float(np.mean([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]))
-           for i, n in enumerate(names)}
+    samples = {n: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]
+               for i, n in enumerate(names)}
+    per = {n: float(np.mean(v)) for n, v in samples.items()}
+    step_gpu = gpu_step_stats(ev)
 
     graph_ms = None
     if args.graph:
@@ -457,8 +471,9 @@ def main():
             "shard_adamw_step": 30 * S}
     byts = {n: byts[n] for n in names}
     step_bytes = sum(byts.values())
-    kern = {n: dict(ms=per[n], launches=launches[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9,
-                    bytes=byts[n]) for n in names}
+    kern = {n: dict(ms=per[n], ms_median=float(np.median(samples[n])),
+                    ms_min=float(np.min(samples[n])), launches=launches[n],
+                    GBps=byts[n] / (per[n] * 1e-3) / 1e9, bytes=byts[n]) for n in names}
     for n in names:
         kern[n]["frac"] = kern[n]["GBps"] / HBM_PEAK_GBPS
     dom = max(names, key=lambda n: per[n])
@@ -558,6 +573,7 @@ def main():
                    "step": " + ".join(names) + (" (all-gather layout)" if flat_mode
                                                  else " (shard-layout bf16)")},
         "graph_ms_per_step": graph_ms,
+        "step_ms_gpu": step_gpu,
         "reduce_adamw_ms": fused_ms,
         "reduce_adamw_GBps": fused_gbps,
         "reduce_adamw_frac_of_peak": fused_gbps / HBM_PEAK_GBPS,

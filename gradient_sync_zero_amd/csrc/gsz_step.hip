@@ -36,8 +36,16 @@ constexpr int kAdamBlock = 512;
 // Largest grid: grid * block work-items must stay below 2^32 per dispatch.
 // Bigger inputs make blocks stride over the remaining tiles.
 constexpr int64_t kMaxFlatGrid = (int64_t)1 << 23;
-// Elements per block of the reductions (8 per lane) and blocks of the first
-// finalize stage.
+// MI355X dispatches block b of a grid to XCD b mod 8.  xcd_remap gives XCD x one
+// contiguous range of logical blocks instead (a bijection on [0, G)): the
+// reduce, which reads P buffers at the same offsets, runs 1.7-1.9% faster that
+// way on the 7B and 70B shares; pack and AdamW run slower and keep the plain order.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t G) {
+    const int64_t q = G / kXcds, rem = G % kXcds, x = b % kXcds;
+    return x * q + (x < rem ? x : rem) + b / kXcds;
+}
+// Elements per block of the reductions (8 per lane).
 constexpr int64_t kRedTile = 8 * kBlock;
 static_assert(kRedTile == gsz::kRedElems && kMaxFlatGrid == gsz::kMaxRedGrid,
               "the workspace size assumes these grids");
@@ -214,10 +222,11 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
                                                         float* __restrict__ g,
                                                         double* __restrict__ ws) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);      // logical block: tile bx
+    int64_t v = bx * kBlock + threadIdx.x;
     double sq = 0.0;
     SegCursor cur{seg, owner, 0, 0, 0};
-    if (FLAT && v < nvec) cur.seek((int64_t)blockIdx.x * kRedTile, nseg);   // uniform: scalar loads
+    if (FLAT && v < nvec) cur.seek(bx * kRedTile, nseg);      // uniform: scalar loads
     const float fP = (float)P;
     for (; v < nvec; v += stride) {
         const int64_t i = v * 8;
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
     }
     if (NORM) {
         const double s = block_sum(sq);
-        if (threadIdx.x == 0) ws[blockIdx.x] = s;
+        if (threadIdx.x == 0) ws[bx] = s;
     }
 }
 
