@@ -196,6 +196,22 @@ def test_reduce_every_rank_count(P):
         assert abs(host(part)[0] - sqnorm_partial(ref)) <= 1e-12 * sqnorm_partial(ref)
 
 
+@pytest.mark.parametrize("n", [0, 1, 3, 4, 5, 2047, 2048, 2049, 4099, (1 << 20) + 5, 2048 * 1025 + 7])
+def test_standalone_norm_any_length(n):
+    """Full 2048-element tiles, a ragged last tile (also not a multiple of 4),
+    and enough tiles (> 1024) for the two-stage fixed-order sum."""
+    from synth import gen
+    x = gen.host_fill(W.tiny().cfg_id, W.KIND_MASTER, 900, 0, n, 0.02, gen.MODE_F32)
+    g = torch.from_numpy(np.ascontiguousarray(x)).cuda() if n else torch.empty(0, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(n) // 8, dtype=torch.float64, device="cuda")
+    part = torch.full((1,), 7.0, dtype=torch.float64, device="cuda")
+    G.shard_grad_sqnorm(g, part, ws)
+    torch.cuda.synchronize()
+    want = sqnorm_partial(x)
+    got = host(part)[0]
+    assert abs(got - want) <= 1e-12 * want if n else got == 0.0, (n, got, want)
+
+
 def test_edge_plans_on_gpu():
     part = torch.full((1,), 7.0, dtype=torch.float64, device="cuda")
     # no tensors at all: every call is a no-op and the partial is zero
