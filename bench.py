@@ -226,22 +226,40 @@ def cpu_baseline(w, owner):
         state.append(gen.host_fill(w.cfg_id, kind, 0, pre, S, std, mode))
     hp = w.hp
     log(f"[cpu] timing the oracle step on S = {S} shard elements")
-    t0 = time.perf_counter()
-    mine = opack.pack(plan, grads[owner])
-    flats = others[:owner] + [mine] + others[owner:]
-    g = reduce_mean([opack.owner_view(plan, f, owner) for f in flats], owner)
-    part = sqnorm_partial(g)
-    _, coef = clip_coef(total([part] * P), hp.max_norm)
-    th, m1, v1, p = adamw(state[0], state[1], state[2], g, coef, hp.lr, hp.beta1, hp.beta2,
-                          hp.eps, hp.weight_decay, hp.step)
-    gathered = np.zeros(plan.flat_len, dtype=np.uint16)
-    ag_write(plan, owner, p, gathered)
+
+    def one_step():
+        mine = opack.pack(plan, grads[owner])
+        flats = others[:owner] + [mine] + others[owner:]
+        g = reduce_mean([opack.owner_view(plan, f, owner) for f in flats], owner)
+        part = sqnorm_partial(g)
+        _, coef = clip_coef(total([part] * P), hp.max_norm)
+        th, m1, v1, p = adamw(state[0], state[1], state[2], g, coef, hp.lr, hp.beta1, hp.beta2,
+                              hp.eps, hp.weight_decay, hp.step)
+        gathered = np.zeros(plan.flat_len, dtype=np.uint16)
+        ag_write(plan, owner, p, gathered)
+
+    # the same step on the same inputs, repeated until about 10 s of CPU work
+    reps, t0 = 0, time.perf_counter()
+    while reps < 3 or time.perf_counter() - t0 < 10.0:
+        one_step()
+        reps += 1
     dt = time.perf_counter() - t0
-    return dict(value=S / dt, unit="params/s", cores=1, kind="oracle",
+    return dict(value=S * reps / dt, unit="params/s", cores=1, kind="oracle",
+                host=_cpu_model(),
                 sample=(f"{w.name}: the first {len(plan.buckets)} buckets of the plan "
                         f"({m} trailing tensors, {s} params, owner {owner} shard of {S}); "
                         f"pack + reduce-mean + norm + clip + AdamW + all-gather layout, "
-                        f"{dt:.2f} s single-threaded NumPy"))
+                        f"{reps} repetitions in {dt:.1f} s of single-threaded NumPy"))
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return f"{line.split(':', 1)[1].strip()} ({os.cpu_count()} logical CPUs)"
+    except OSError:
+        pass
+    return f"unknown ({os.cpu_count()} logical CPUs)"
 
 
 def bench_ddp(args):
