@@ -66,6 +66,10 @@ def _load_dev():
                                        ctypes.c_int64, ctypes.c_float, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_void_p]
         lib.synth_fill_dev.restype = ctypes.c_int
+        lib.synth_fill_dev_pieces.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_fill_dev_pieces.restype = ctypes.c_int
         lib.synth_copy_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int, ctypes.c_void_p]
         lib.synth_copy_dev.restype = ctypes.c_int
@@ -136,6 +140,35 @@ def dev_fill(out, cfg_id, kind, rank, start, std, mode, seed=None, stream=None):
                                     scale_for(std), mode, out.data_ptr(), s)
     if rc != 0:
         raise RuntimeError(f"synth_fill_dev failed ({rc})")
+    return out
+
+
+def dev_fill_pieces(out, pieces, cfg_id, kind, rank, std, mode, seed=None):
+    """out[dst + j] = value(param + j), j < n, for every (dst, param, n) in pieces,
+    in one launch on the current stream; elements no piece covers are left as
+    they are.  The piece table is a device tensor on the same stream, so the
+    caching allocator reuses its memory only after the launch."""
+    import torch
+    from .workloads import SEED
+    seed = SEED if seed is None else seed
+    want = torch.uint16 if mode == MODE_BF16 else torch.float32
+    if out.dtype != want or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("dev_fill_pieces needs a contiguous device tensor of the mode's dtype")
+    rows, cum = [], 0
+    for dst, param, n in pieces:
+        if n < 0 or dst < 0 or param < 0 or dst + n > out.numel():
+            raise ValueError(f"piece ({dst}, {param}, {n}) does not fit a tensor of {out.numel()}")
+        rows += [cum, dst, param]
+        cum += n
+    if cum == 0:
+        return out
+    rows += [cum, 0, 0]
+    tab = torch.tensor(rows, dtype=torch.int64).to(out.device)
+    rc = _load_dev().synth_fill_dev_pieces(seed, key1(cfg_id, kind, rank), tab.data_ptr(),
+                                           len(pieces), cum, scale_for(std), mode,
+                                           out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_fill_dev_pieces failed ({rc})")
     return out
 
 

@@ -33,22 +33,46 @@ __device__ __forceinline__ float synth_value(uint32_t seed, uint32_t key1, uint6
     return (float)z * scale;
 }
 
+// out[i] <- x in the mode's type: fp32, |fp32|, or bf16 bits (round to nearest even).
+__device__ __forceinline__ void synth_store(void* out, int64_t i, float x, int mode) {
+    if (mode == 0) {
+        ((float*)out)[i] = x;
+    } else if (mode == 1) {
+        ((float*)out)[i] = __uint_as_float(__float_as_uint(x) & 0x7FFFFFFFu);
+    } else {
+        const uint32_t u = __float_as_uint(x);
+        uint16_t b;
+        if ((u & 0x7FFFFFFFu) > 0x7F800000u) b = (uint16_t)((u >> 16) | 0x0040u);
+        else b = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+        ((uint16_t*)out)[i] = b;
+    }
+}
+
 __global__ void synth_fill_kernel(uint32_t seed, uint32_t key1, uint64_t start, int64_t n,
                                   float scale, int mode, void* out) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const float x = synth_value(seed, key1, start + (uint64_t)i, scale);
-        if (mode == 0) {
-            ((float*)out)[i] = x;
-        } else if (mode == 1) {
-            ((float*)out)[i] = __uint_as_float(__float_as_uint(x) & 0x7FFFFFFFu);
-        } else {
-            const uint32_t u = __float_as_uint(x);
-            uint16_t b;
-            if ((u & 0x7FFFFFFFu) > 0x7F800000u) b = (uint16_t)((u >> 16) | 0x0040u);
-            else b = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-            ((uint16_t*)out)[i] = b;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        synth_store(out, i, synth_value(seed, key1, start + (uint64_t)i, scale), mode);
+}
+
+// Pieces: out[dst_k + j] = value(param_k + j) for j < len_k.  tab holds np + 1
+// rows {cum_k, dst_k, param_k} with cum_k = len_0 + ... + len_{k-1}; the last
+// row is {total, 0, 0}.  Virtual index v in [0, total) belongs to the largest k
+// with cum_k <= v (empty pieces are skipped that way).
+__global__ void synth_fill_pieces_kernel(uint32_t seed, uint32_t key1,
+                                         const int64_t* __restrict__ tab, int np, float scale,
+                                         int mode, void* out) {
+    const int64_t total = tab[3 * np];
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total; v += stride) {
+        int lo = 0, hi = np - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tab[3 * mid] <= v) lo = mid; else hi = mid - 1;
         }
+        const int64_t j = v - tab[3 * lo];
+        synth_store(out, tab[3 * lo + 1] + j,
+                    synth_value(seed, key1, (uint64_t)(tab[3 * lo + 2] + j), scale), mode);
     }
 }
 
@@ -168,6 +192,20 @@ int synth_fill_dev(uint32_t seed, uint32_t key1, uint64_t start, int64_t n, floa
     const int block = 256;
     hipLaunchKernelGGL(synth_fill_kernel, dim3(grid_for(n, block)), dim3(block), 0, stream,
                        seed, key1, start, n, scale, mode, out);
+    return (int)hipGetLastError();
+}
+
+// The pieces form of synth_fill_dev (see synth_fill_pieces_kernel): tab is a
+// device array of np + 1 rows; the caller guarantees every dst_k + len_k fits
+// in out.  One launch for any number of pieces.
+int synth_fill_dev_pieces(uint32_t seed, uint32_t key1, const int64_t* tab, int np, int64_t total,
+                          float scale, int mode, void* out, hipStream_t stream) {
+    if (np < 0 || total < 0 || mode < 0 || mode > 2) return -1;
+    if (np == 0 || total == 0) return 0;
+    if (!tab || !out) return -1;
+    const int block = 256;
+    hipLaunchKernelGGL(synth_fill_pieces_kernel, dim3(grid_for(total, block)), dim3(block), 0,
+                       stream, seed, key1, tab, np, scale, mode, out);
     return (int)hipGetLastError();
 }
 

@@ -61,8 +61,7 @@ def owner_pieces(plan, w, r):
 
 
 def fill_pieces(out, pieces, w, kind, rank, std, mode):
-    for so, pi, n in pieces:
-        gen.dev_fill(out[so:so + n], w.cfg_id, kind, rank, pi, std, mode)
+    gen.dev_fill_pieces(out, pieces, w.cfg_id, kind, rank, std, mode)
 
 
 def owner_state(plan, w, r):

@@ -61,3 +61,21 @@ def test_read_streams_probe():
     for b in host_bufs:
         want ^= int(np.bitwise_xor.reduce(b.numpy()))
     assert int(np.bitwise_xor.reduce(sink.cpu().numpy())) == want
+
+
+@pytest.mark.parametrize("mode,std", [(gen.MODE_F32, 0.02), (gen.MODE_BF16, 1e-3)])
+def test_pieces_fill_equals_per_piece_fills(mode, std):
+    dt = torch.uint16 if mode == gen.MODE_BF16 else torch.float32
+    n = 50000
+    pieces = [(0, 1000, 300), (300, 7, 0), (300, 2 ** 32 - 50, 100), (1000, 0, 4096),
+              (9000, 123456, 40000), (49990, 5, 10)]
+    a = torch.full((n,), 7, dtype=dt, device="cuda")
+    gen.dev_fill_pieces(a, pieces, 3, 2, 9, std, mode)
+    b = torch.full((n,), 7, dtype=dt, device="cuda")
+    for dst, param, k in pieces:
+        if k:
+            gen.dev_fill(b[dst:dst + k], 3, 2, 9, param, std, mode)
+    torch.cuda.synchronize()
+    assert_bits(host(a), host(b), "pieces fill")                  # covered and uncovered alike
+    with pytest.raises(ValueError):                               # out of range: refused on the host
+        gen.dev_fill_pieces(a, [(n - 5, 0, 6)], 3, 2, 9, std, mode)
