@@ -62,3 +62,39 @@ def accumulate(plan: Plan, flat: np.ndarray, grads) -> np.ndarray:
         off = plan.tensor_offset[t]
         out[off:off + g.size] = narrow(widen(out[off:off + g.size]) + widen(g))
     return out
+
+
+def pack_f32(plan: Plan, grads) -> np.ndarray:
+    """First micro-batch of an fp32 accumulation: the bf16 gradients widened
+    (exactly) into an fp32 bucket-major buffer, pads zero.
+
+    Gradient accumulation between synchronisations ("Distributed Training: Data
+    Parallel, Model Parallel and FSDP Strategies", section "Selecting and Tuning
+    Your Strategy", the no_sync loop) with the reduction dtype fp32 (same page,
+    section "FSDP1 vs FSDP2 and DTensor", reduce_dtype = fp32): the buckets hold
+    fp32 sums of the micro-batches' bf16 gradients.
+    """
+    from .bf16 import widen
+    flat = np.zeros(plan.flat_len, dtype=np.float32)
+    for t, g in enumerate(grads):
+        g = np.asarray(g, dtype=np.uint16).reshape(-1)
+        if g.size != plan.numel[t]:
+            raise ValueError(f"tensor {t}: {g.size} elements, plan says {plan.numel[t]}")
+        off = plan.tensor_offset[t]
+        flat[off:off + g.size] = widen(g)
+    return flat
+
+
+def accumulate_f32(plan: Plan, flat32: np.ndarray, grads) -> np.ndarray:
+    """Later micro-batches of the fp32 accumulation (passages as for pack_f32):
+    flat32 = flat32 + f32(grad), one fp32 addition (round to nearest even) per
+    element; pads untouched.  Returns a new array."""
+    from .bf16 import widen
+    out = np.array(flat32, dtype=np.float32, copy=True)
+    for t, g in enumerate(grads):
+        g = np.asarray(g, dtype=np.uint16).reshape(-1)
+        if g.size != plan.numel[t]:
+            raise ValueError(f"tensor {t}: {g.size} elements, plan says {plan.numel[t]}")
+        off = plan.tensor_offset[t]
+        out[off:off + g.size] = out[off:off + g.size] + widen(g)
+    return out

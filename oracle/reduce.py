@@ -28,17 +28,29 @@ import numpy as np
 from .bf16 import narrow, widen
 
 
+def as_f32(c) -> np.ndarray:
+    """A contribution as fp32: bf16 bits (uint16) are widened exactly; fp32
+    contributions (fp32 accumulation buckets) are taken as they are."""
+    c = np.asarray(c)
+    if c.dtype == np.uint16:
+        return widen(c)
+    if c.dtype != np.float32:
+        raise ValueError(f"contribution dtype {c.dtype}: need bf16 bits (uint16) or float32")
+    return c
+
+
 def reduce_mean(contribs, r: int) -> np.ndarray:
-    """contribs[q]: rank q's bf16 values (uint16) for owner r's elements.
+    """contribs[q]: rank q's values for owner r's elements, bf16 bits (uint16)
+    or fp32.
 
     Returns the fp32 mean in ring order ((c[r+1] + c[r+2]) + ...) + c[r], / P.
     """
     P = len(contribs)
     if not 0 <= r < P:
         raise ValueError("owner rank out of range")
-    acc = widen(contribs[(r + 1) % P]).copy()
+    acc = as_f32(contribs[(r + 1) % P]).copy()
     for k in range(2, P + 1):
-        acc = acc + widen(contribs[(r + k) % P])
+        acc = acc + as_f32(contribs[(r + k) % P])
     return (acc / np.float32(P)).astype(np.float32)
 
 
@@ -46,7 +58,7 @@ def ring_allreduce_sim(plan, flats, rs_wire_bytes: int = 4, ag_wire_bytes: int =
                       bf16_partials: bool = False):
     """Message-passing simulation of ring reduce-scatter then all-gather.
 
-    flats[k]: rank k's bucket-major flat bf16 buffer.  Returns
+    flats[k]: rank k's bucket-major flat buffer (bf16 bits or fp32).  Returns
     (results, rs_sent, ag_sent): results[k] is rank k's fp32 flat buffer after
     the all-reduce (mean); rs_sent[k] / ag_sent[k] count the bytes rank k sent
     in each phase (elements times the wire dtype's size).  With bf16_partials
@@ -62,7 +74,7 @@ def ring_allreduce_sim(plan, flats, rs_wire_bytes: int = 4, ag_wire_bytes: int =
     for bk in plan.buckets:
         C = bk.chunk
         # buf[k][c]: rank k's current fp32 values of chunk c of this bucket.
-        buf = [[widen(flats[k][bk.base + c * C: bk.base + (c + 1) * C]).copy()
+        buf = [[as_f32(flats[k][bk.base + c * C: bk.base + (c + 1) * C]).copy()
                 for c in range(P)] for k in range(P)]
         for s in range(P - 1):                       # reduce-scatter
             msgs = []

@@ -79,3 +79,68 @@ def test_bf16_wire_drifts_from_fp32_but_not_on_exact_inputs():
     assert np.array_equal(reduce_mean(ints, 3), reduce_mean_bf16_wire(ints, 3))
     one = [c[0]]
     assert np.array_equal(reduce_mean_bf16_wire(one, 0), widen(c[0]))
+
+
+def test_fp32_accumulation_matches_torch():
+    """An fp32 accumulation buffer fed bf16 gradients in torch (acc += g.float())."""
+    rng = np.random.default_rng(11)
+    numel = [1000, 37, 4096, 0, 5]
+    plan = make_plan(numel, 4000, 4, align=8)
+    micro = [[narrow(rng.normal(0, 1e-3, n).astype(np.float32)) for n in numel] for _ in range(4)]
+    flat = opack.pack_f32(plan, micro[0])
+    for k in range(1, 4):
+        flat = opack.accumulate_f32(plan, flat, micro[k])
+    for t, n in enumerate(numel):
+        acc = torch.from_numpy(micro[0][t].view(np.int16)).view(torch.bfloat16).float()
+        for k in range(1, 4):
+            acc += torch.from_numpy(micro[k][t].view(np.int16)).view(torch.bfloat16).float()
+        off = plan.tensor_offset[t]
+        assert np.array_equal(flat[off:off + n].view(np.uint32), acc.numpy().view(np.uint32))
+    pad = np.ones(plan.flat_len, bool)
+    for t, n in enumerate(numel):
+        pad[plan.tensor_offset[t]:plan.tensor_offset[t] + n] = False
+    assert not flat[pad].any()
+
+
+def test_fp32_accumulation_is_exact_where_bf16_rounds():
+    """Integers up to 2^10 in magnitude: four of them sum exactly in fp32, while
+    bf16 (8 significant bits) must round some partial sums."""
+    numel = [512]
+    plan = make_plan(numel, 1 << 20, 2)
+    rng = np.random.default_rng(12)
+    ints = rng.integers(-1000, 1001, (4, 512))
+    micro = [[narrow(x.astype(np.float32))] for x in ints]
+    exact_in = [widen(m[0]).astype(np.float64) for m in micro]   # the bf16-rounded inputs
+    f32 = opack.pack_f32(plan, micro[0])
+    b16 = opack.pack(plan, micro[0])
+    for k in range(1, 4):
+        f32 = opack.accumulate_f32(plan, f32, micro[k])
+        b16 = opack.accumulate(plan, b16, micro[k])
+    want = np.sum(exact_in, axis=0)
+    off = plan.tensor_offset[0]
+    assert np.array_equal(f32[off:off + 512].astype(np.float64), want)
+    assert (widen(b16[off:off + 512]).astype(np.float64) != want).any()
+
+
+@pytest.mark.parametrize("P", [2, 3, 4, 8])
+def test_fp32_contributions_equal_message_passing_ring(P):
+    rng = np.random.default_rng(20 + P)
+    numel = [int(rng.integers(1, 3000)) for _ in range(6)]
+    plan = make_plan(numel, 4000, P, align=8)
+    flats = []
+    for q in range(P):
+        f = opack.pack_f32(plan, [narrow(rng.normal(0, 1e-3, n).astype(np.float32)) for n in numel])
+        f = opack.accumulate_f32(plan, f, [narrow(rng.normal(0, 1e-3, n).astype(np.float32))
+                                           for n in numel])
+        flats.append(f)
+    results, rs_sent, _ = ring_allreduce_sim(plan, flats)
+    M = plan.flat_len * 4
+    for r in range(P):
+        g = reduce_mean([opack.owner_view(plan, f, r) for f in flats], r)
+        assert np.array_equal(g.view(np.uint32), opack.owner_view(plan, results[0], r).view(np.uint32))
+        assert rs_sent[r] * P == (P - 1) * M
+
+
+def test_reduce_takes_only_bf16_bits_or_fp32():
+    with pytest.raises(ValueError):
+        reduce_mean([np.zeros(4, np.float64)] * 2, 0)
