@@ -87,6 +87,14 @@ def short_name(full):
             return "k_allreduce_mean"
     if "k_finalize_ranges" in full:
         return "k_finalize_ranges"
+    if "k_pack_f32<false>" in full:
+        return "k_pack_f32"
+    if "k_pack_f32<true>" in full:
+        return "k_accumulate_f32"
+    if "k_reduce_mean_f32" in full:
+        return "k_reduce_mean_f32"
+    if "k_zero_pads_f32" in full:
+        return "k_zero_pads_f32"
     for k, v in SHORT.items():
         if k in full:
             return v
@@ -538,6 +546,29 @@ def main():
         ms = time_call(fn)
         standalone[name] = dict(ms=ms, bytes=nbytes, GBps=nbytes / (ms * 1e-3) / 1e9,
                                 frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+    # fp32 accumulation buckets and the reduce over fp32 contributions, when
+    # their buffers fit beside the working set: one fp32 flat buffer for the
+    # accumulation (10 bytes per parameter: bf16 gradient in, fp32 bucket in and
+    # out) and P shard-compact fp32 contributions for the reduce (4P + 4 bytes
+    # per shard element).
+    if flat_mode and 4 * L < 0.8 * torch.cuda.mem_get_info()[0]:
+        f32 = torch.zeros(L, dtype=torch.float32, device="cuda")
+        G.bucket_pack_f32(plan, my_grads, f32)
+        ms = time_call(lambda: G.bucket_accumulate_f32(plan, my_grads, f32))
+        nbytes = 10 * w.n_params
+        standalone["bucket_accumulate_f32"] = dict(ms=ms, bytes=nbytes,
+                                                   GBps=nbytes / (ms * 1e-3) / 1e9,
+                                                   frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+        del f32
+    if 4 * P * S < 0.8 * torch.cuda.mem_get_info()[0]:
+        c32 = [g.clone() for _ in range(P)]      # values do not change the timing
+        ms = time_call(lambda: G.shard_reduce_mean_f32(plan, r, c32, G.LAYOUT_SHARD_COMPACT, g,
+                                                       part1, ws))
+        nbytes = (4 * P + 4) * S
+        standalone["shard_reduce_mean_f32"] = dict(ms=ms, bytes=nbytes,
+                                                   GBps=nbytes / (ms * 1e-3) / 1e9,
+                                                   frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
+        del c32
     log("[gpu] standalone: " + "; ".join(f"{n} {v['ms']:.3f} ms {v['GBps']:.0f} GB/s"
                                          for n, v in standalone.items()))
     del shard_bf16

@@ -71,6 +71,9 @@ _SIGS = {
     "gsz_allgather_layout_write": [_P, _I32, _P, _P, _P],
     "gsz_bucket_unpack": [_P, _P, _P, _P],
     "gsz_bucket_accumulate": [_P, _P, _P, _P],
+    "gsz_bucket_pack_f32": [_P, _P, _P, _P],
+    "gsz_bucket_accumulate_f32": [_P, _P, _P, _P],
+    "gsz_shard_reduce_mean_f32": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_shard_reduce_mean_bf16_wire": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_allreduce_mean": [_P, _P, _P, _P],
     "gsz_adamw_step": [_P, _P, _P, _P, _I64, _P, ctypes.POINTER(AdamWHP), _P, _P],
@@ -237,6 +240,38 @@ def bucket_accumulate(plan, grads, flat, stream=None):
                                        for i, t in enumerate(grads)])
     _check(load().gsz_bucket_accumulate(plan.handle, ptrs, _ptr(flat, "flat", bt),
                                         _stream(stream)))
+
+
+def _grad_ptrs(plan, grads):
+    bt = _bf16_types()
+    if len(grads) != plan.n_tensors:
+        raise ValueError("need one gradient per plan tensor")
+    return (_P * max(len(grads), 1))(*[_ptr(t, f"grads[{i}]", bt) if t.numel() else None
+                                       for i, t in enumerate(grads)])
+
+
+def bucket_pack_f32(plan, grads, flat32, stream=None):
+    """First micro-batch of an fp32 accumulation window: flat32 = f32(grads), pads 0."""
+    _check(load().gsz_bucket_pack_f32(plan.handle, _grad_ptrs(plan, grads),
+                                      _ptr(flat32, "flat32", _f32()), _stream(stream)))
+
+
+def bucket_accumulate_f32(plan, grads, flat32, stream=None):
+    """Later micro-batches: flat32 += f32(grads) (fp32 adds)."""
+    _check(load().gsz_bucket_accumulate_f32(plan.handle, _grad_ptrs(plan, grads),
+                                            _ptr(flat32, "flat32", _f32()), _stream(stream)))
+
+
+def shard_reduce_mean_f32(plan, owner, contribs, layout, g, partial_out=None, ws=None, stream=None):
+    """gsz_shard_reduce_mean_f32: the ring-order mean of P fp32 contributions."""
+    if len(contribs) != plan.world_size:
+        raise ValueError("need one contribution per rank")
+    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", _f32()) for i, t in enumerate(contribs)])
+    wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(load().gsz_shard_reduce_mean_f32(plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32()),
+                                            _ptr(partial_out, "partial_out", _f64(), allow_none=True),
+                                            wsp, nbytes, _stream(stream)))
 
 
 def shard_reduce_mean(plan, owner, contribs, layout, g, partial_out=None, ws=None, stream=None,

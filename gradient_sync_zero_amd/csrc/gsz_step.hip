@@ -51,6 +51,7 @@ static_assert(kRedTile == gsz::kRedElems && kMaxFlatGrid == gsz::kMaxRedGrid,
               "the workspace size assumes these grids");
 
 struct RankPtrs { const uint16_t* p[GSZ_MAX_RANKS]; };
+struct RankPtrsF { const float* p[GSZ_MAX_RANKS]; };
 struct PackPtrs { const uint16_t* p[gsz::kPackBatch]; };
 
 // fp32 constants of the AdamW update, each rounded once from double on the host.
@@ -204,6 +205,83 @@ __global__ __launch_bounds__(kBlock) void k_zero_pads(const int64_t* __restrict_
     for (int64_t j = threadIdx.x; j < n; j += kBlock) flat[s + j] = 0;
 }
 
+// fp32 accumulation buckets (gradient accumulation with an fp32 reduction
+// dtype): ACC = false widens the tensors of one batch into flat32 (the first
+// micro-batch), ACC = true adds them: flat32[off_t + j] = flat32[off_t + j] +
+// f32(grad_t[j]), one IEEE fp32 addition.  Tiles and grid as k_pack.  In a full
+// tile lane l takes elements 4l..4l+3 and 256+4l..256+4l+3 (two 8-byte bf16
+// loads), so each 16-byte fp32 load and store of the wave covers whole lines;
+// with nontemporal hints on every access this runs 5-6% faster than one 16-byte
+// bf16 load per lane widened into two half-line fp32 stores.
+__device__ __forceinline__ void stf8(float* p, const float a[8]) {
+    stf4(p, f32x4{a[0], a[1], a[2], a[3]});
+    stf4(p + 4, f32x4{a[4], a[5], a[6], a[7]});
+}
+template <bool ACC>
+__global__ __launch_bounds__(kPackBlock) void k_pack_f32(PackPtrs pp, const int64_t* __restrict__ tab,
+                                                     int k0, int nk, int64_t t_begin, int64_t t_end,
+                                                     float* __restrict__ flat) {
+    const int tid = threadIdx.x;
+    for (int64_t tile = t_begin + blockIdx.x; tile < t_end; tile += gridDim.x) {
+        int lo = k0, hi = k0 + nk - 1;          // largest k with first_tile[k] <= tile
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (tab[3 * mid + 2] <= tile) lo = mid; else hi = mid - 1;
+        }
+        const int k = lo;
+        const int64_t n = tab[3 * k + 1];
+        const int64_t j0 = (tile - tab[3 * k + 2]) * gsz::kPackTile;
+        const int64_t j1 = j0 + gsz::kPackTile < n ? j0 + gsz::kPackTile : n;
+        const uint16_t* __restrict__ src = pp.p[k - k0];
+        float* __restrict__ dst = flat + tab[3 * k];
+        const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+        if (vec && j1 - j0 == gsz::kPackTile) {
+            static_assert(gsz::kPackTile == 8 * kPackBlock, "two groups of 4 elements per lane");
+            const int64_t ja = j0 + 4 * tid, jb = ja + 4 * kPackBlock;
+            const u32x2 wa = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src + ja));
+            const u32x2 wb = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src + jb));
+            f32x4 xa = f32x4{bf16_lo(wa.x), bf16_hi(wa.x), bf16_lo(wa.y), bf16_hi(wa.y)};
+            f32x4 xb = f32x4{bf16_lo(wb.x), bf16_hi(wb.x), bf16_lo(wb.y), bf16_hi(wb.y)};
+            if (ACC) {
+                const f32x4 da = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dst + ja));
+                const f32x4 db = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dst + jb));
+                xa = f32x4{da.x + xa.x, da.y + xa.y, da.z + xa.z, da.w + xa.w};
+                xb = f32x4{db.x + xb.x, db.y + xb.y, db.z + xb.z, db.w + xb.w};
+            }
+            __builtin_nontemporal_store(xa, reinterpret_cast<f32x4*>(dst + ja));
+            __builtin_nontemporal_store(xb, reinterpret_cast<f32x4*>(dst + jb));
+        } else if (vec) {
+            const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
+            for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kPackBlock) {
+                float a[8];
+                widen8(ld16(src + j), a);
+                if (ACC) {
+                    const f32x4 d0 = ldf4(dst + j), d1 = ldf4(dst + j + 4);
+                    a[0] = d0.x + a[0]; a[1] = d0.y + a[1]; a[2] = d0.z + a[2]; a[3] = d0.w + a[3];
+                    a[4] = d1.x + a[4]; a[5] = d1.y + a[5]; a[6] = d1.z + a[6]; a[7] = d1.w + a[7];
+                }
+                stf8(dst + j, a);
+            }
+            for (int64_t j = jv + tid; j < j1; j += kPackBlock) {
+                const float x = __uint_as_float((uint32_t)src[j] << 16);
+                dst[j] = ACC ? dst[j] + x : x;
+            }
+        } else {
+            for (int64_t j = j0 + tid; j < j1; j += kPackBlock) {
+                const float x = __uint_as_float((uint32_t)src[j] << 16);
+                dst[j] = ACC ? dst[j] + x : x;
+            }
+        }
+    }
+}
+
+// Zeroes the padding of each padded bucket of an fp32 buffer; one block per bucket.
+__global__ __launch_bounds__(kBlock) void k_zero_pads_f32(const int64_t* __restrict__ pads,
+                                                          float* __restrict__ flat) {
+    const int64_t s = pads[2 * blockIdx.x], n = pads[2 * blockIdx.x + 1];
+    for (int64_t j = threadIdx.x; j < n; j += kBlock) flat[s + j] = 0.0f;
+}
+
 // ---------------------------------------------------------- reduce-mean --
 
 // g[i] = (((c0 + c1) + c2) + ... + c_{P-1}) / P with rp.p[k] = contribution of
@@ -273,6 +351,82 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
                 const double d = (double)a[j];
                 sq = __fma_rn(d, d, sq);                        // d*d is exact in fp64
             }
+        }
+    }
+    if (NORM) {
+        const double s = block_sum(sq);
+        if (threadIdx.x == 0) ws[bx] = s;
+    }
+}
+
+// The reduce over fp32 contributions (fp32 accumulation buckets, fp32 on the
+// ring's wire): the same ring order and division as k_reduce_mean, inputs
+// taken as they are.  A wave owns 512 shard elements of its block's tile as two
+// groups of 256; lane l handles elements 4l..4l+3 of each, so every 16-byte
+// load and store of a wave covers whole lines.  Blocks, XCD order and norm
+// partials as k_reduce_mean.
+template <int PS, bool NORM, bool FLAT>
+__global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P, float invP, int pow2,
+                                                            const int64_t* __restrict__ seg, int nseg,
+                                                            int64_t owner, int64_t S,
+                                                            float* __restrict__ g,
+                                                            double* __restrict__ ws) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);
+    double sq = 0.0;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    int64_t t = bx * kRedTile;
+    if (FLAT && t < S) cur.seek(t, nseg);                     // uniform: scalar loads
+    const float fP = (float)P;
+    for (; t < S; t += (int64_t)gridDim.x * kRedTile) {
+        const int64_t i0 = t + 512 * wave + 4 * lane, i1 = i0 + 256;
+        const bool ok0 = i0 < S, ok1 = i1 < S;               // S and i are multiples of 4
+        const int64_t off0 = ok0 ? (FLAT ? cur.map(i0) : i0) : 0;
+        const int64_t off1 = ok1 ? (FLAT ? cur.map(i1) : i1) : 0;
+        const f32x4 zero = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 a = zero, b = zero;
+        if constexpr (PS > 0) {
+            constexpr int G = PS < 16 ? PS : 16;
+#pragma unroll
+            for (int k0 = 0; k0 < PS; k0 += G) {
+                f32x4 w0[G], w1[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    w0[j] = ok0 ? ldf4(rp.p[k0 + j] + off0) : zero;
+                    w1[j] = ok1 ? ldf4(rp.p[k0 + j] + off1) : zero;
+                }
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if (k0 + j == 0) { a = w0[j]; b = w1[j]; }
+                    else {
+                        a.x = a.x + w0[j].x; a.y = a.y + w0[j].y; a.z = a.z + w0[j].z; a.w = a.w + w0[j].w;
+                        b.x = b.x + w1[j].x; b.y = b.y + w1[j].y; b.z = b.z + w1[j].z; b.w = b.w + w1[j].w;
+                    }
+                }
+            }
+        } else {
+            a = ok0 ? ldf4(rp.p[0] + off0) : zero;
+            b = ok1 ? ldf4(rp.p[0] + off1) : zero;
+            for (int k = 1; k < P; ++k) {
+                const f32x4 w0 = ok0 ? ldf4(rp.p[k] + off0) : zero;
+                const f32x4 w1 = ok1 ? ldf4(rp.p[k] + off1) : zero;
+                a.x = a.x + w0.x; a.y = a.y + w0.y; a.z = a.z + w0.z; a.w = a.w + w0.w;
+                b.x = b.x + w1.x; b.y = b.y + w1.y; b.z = b.z + w1.z; b.w = b.w + w1.w;
+            }
+        }
+        if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
+            a = f32x4{a.x * invP, a.y * invP, a.z * invP, a.w * invP};   // exact: a power of two
+            b = f32x4{b.x * invP, b.y * invP, b.z * invP, b.w * invP};
+        } else {
+            a = f32x4{a.x / fP, a.y / fP, a.z / fP, a.w / fP};
+            b = f32x4{b.x / fP, b.y / fP, b.z / fP, b.w / fP};
+        }
+        if (ok0) stf4(g + i0, a);
+        if (ok1) stf4(g + i1, b);
+        if (NORM) {
+            const double d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sq = __fma_rn(d[j], d[j], sq);   // zeros where !ok
         }
     }
     if (NORM) {
@@ -544,6 +698,20 @@ void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPt
         hipLaunchKernelGGL((k_reduce_mean<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
 }
 
+template <int PS>
+void launch_reduce_f32(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPtrsF& rp, int P,
+                       float invP, int pow2, const int64_t* seg, int nseg, int64_t owner, int64_t S,
+                       float* g, double* ws) {
+    if (norm && flat)
+        hipLaunchKernelGGL((k_reduce_mean_f32<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, S, g, ws);
+    else if (norm)
+        hipLaunchKernelGGL((k_reduce_mean_f32<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, S, g, ws);
+    else if (flat)
+        hipLaunchKernelGGL((k_reduce_mean_f32<PS, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, S, g, ws);
+    else
+        hipLaunchKernelGGL((k_reduce_mean_f32<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, S, g, ws);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI --
@@ -600,9 +768,14 @@ extern "C" int gsz_plan_upload(gsz_plan* p) {
 
 namespace {
 
-// Launches the pack kernel in MODE over every tensor: ptrs is the host array of
-// the T tensor pointers (sources for kPack/kAccumulate, destinations for kUnpack).
-int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, uint16_t* flat, int mode,
+// Modes of run_pack beyond PackMode: the fp32 bucket buffer's first micro-batch
+// (widen) and later ones (add).
+constexpr int kPackF32 = 3, kAccumulateF32 = 4;
+
+// Launches the pack kernel in `mode` over every tensor: ptrs is the host array of
+// the T tensor pointers (sources for kPack/kAccumulate and the fp32 modes,
+// destinations for kUnpack); flat is bf16 (uint16) or, in the fp32 modes, float.
+int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, void* flat, int mode,
              hipStream_t stream, const char* who) {
     int rc = check_plan(p, who);
     if (rc) return rc;
@@ -622,17 +795,29 @@ int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, uint16_t* flat, int
         if (te == tb) continue;
         constexpr int64_t kMaxPackGrid = ((int64_t)1 << 31) / kPackBlock;   // work-items < 2^32
         const int grid = (int)(te - tb < kMaxPackGrid ? te - tb : kMaxPackGrid);
+        uint16_t* f16 = static_cast<uint16_t*>(flat);
+        float* f32 = static_cast<float*>(flat);
         if (mode == kPack)
-            hipLaunchKernelGGL(k_pack<kPack>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, flat);
+            hipLaunchKernelGGL(k_pack<kPack>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f16);
         else if (mode == kUnpack)
-            hipLaunchKernelGGL(k_pack<kUnpack>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, flat);
+            hipLaunchKernelGGL(k_pack<kUnpack>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f16);
+        else if (mode == kAccumulate)
+            hipLaunchKernelGGL(k_pack<kAccumulate>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f16);
+        else if (mode == kPackF32)
+            hipLaunchKernelGGL(k_pack_f32<false>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f32);
         else
-            hipLaunchKernelGGL(k_pack<kAccumulate>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, flat);
+            hipLaunchKernelGGL(k_pack_f32<true>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f32);
         if ((rc = launched(who))) return rc;
     }
     const int npad = (int)(p->pads.size() / 2);
     if (mode == kPack && npad > 0) {
-        hipLaunchKernelGGL(k_zero_pads, dim3(npad), dim3(kBlock), 0, stream, p->d_pads, flat);
+        hipLaunchKernelGGL(k_zero_pads, dim3(npad), dim3(kBlock), 0, stream, p->d_pads,
+                           static_cast<uint16_t*>(flat));
+        if ((rc = launched(who))) return rc;
+    }
+    if (mode == kPackF32 && npad > 0) {
+        hipLaunchKernelGGL(k_zero_pads_f32, dim3(npad), dim3(kBlock), 0, stream, p->d_pads,
+                           static_cast<float*>(flat));
         if ((rc = launched(who))) return rc;
     }
     return GSZ_OK;
@@ -650,11 +835,24 @@ extern "C" int gsz_bucket_accumulate(const gsz_plan* p, const uint16_t* const* g
     return run_pack(p, grads, flat, kAccumulate, stream, "gsz_bucket_accumulate");
 }
 
+extern "C" int gsz_bucket_pack_f32(const gsz_plan* p, const uint16_t* const* grads, float* flat32,
+                                   hipStream_t stream) {
+    return run_pack(p, grads, flat32, kPackF32, stream, "gsz_bucket_pack_f32");
+}
+
+extern "C" int gsz_bucket_accumulate_f32(const gsz_plan* p, const uint16_t* const* grads,
+                                         float* flat32, hipStream_t stream) {
+    return run_pack(p, grads, flat32, kAccumulateF32, stream, "gsz_bucket_accumulate_f32");
+}
+
 namespace {
 
-int reduce_impl(const gsz_plan* p, int32_t owner, const uint16_t* const* contrib, int32_t layout,
+// The shard reduce over bf16 contributions (wire16: rounding the partial sums
+// to bf16) or, with f32in, over fp32 contributions; contrib holds P device
+// pointers of the matching type.
+int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, int32_t layout,
                 float* g, double* partial_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                bool wire16, const char* who) {
+                bool wire16, bool f32in, const char* who) {
     int rc = check_plan(p, who);
     if (rc) return rc;
     if ((rc = check_owner(p, owner, who))) return rc;
@@ -679,9 +877,29 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const uint16_t* const* contrib
     }
     const int64_t nvec = S / 8;
     const int grid = flat_grid((S + kRedTile - 1) / kRedTile);
-    if (S > 0) {
+    if (S > 0 && f32in) {
+        RankPtrsF rp{};
+        for (int k = 0; k < P; ++k) rp.p[k] = static_cast<const float*>(contrib[(owner + 1 + k) % P]);
+        const int pow2 = (P & (P - 1)) == 0;
+        const float invP = pow2 ? 1.0f / (float)P : 0.0f;
+        const bool norm = partial_out != nullptr;
+        const bool flat = layout == GSZ_LAYOUT_BUCKET_FLAT;
+        const int nseg = (int)p->buckets.size();
+        double* wsd = static_cast<double*>(ws);
+        const dim3 gr(grid);
+        switch (P) {
+            case 2: launch_reduce_f32<2>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
+            case 4: launch_reduce_f32<4>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
+            case 8: launch_reduce_f32<8>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
+            case 16: launch_reduce_f32<16>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
+            case 32: launch_reduce_f32<32>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
+            case 64: launch_reduce_f32<64>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
+            default: launch_reduce_f32<0>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
+        }
+        if ((rc = launched(who))) return rc;
+    } else if (S > 0) {
         RankPtrs rp{};
-        for (int k = 0; k < P; ++k) rp.p[k] = contrib[(owner + 1 + k) % P];
+        for (int k = 0; k < P; ++k) rp.p[k] = static_cast<const uint16_t*>(contrib[(owner + 1 + k) % P]);
         const int pow2 = (P & (P - 1)) == 0;
         const float invP = pow2 ? 1.0f / (float)P : 0.0f;
         const bool norm = partial_out != nullptr;
@@ -713,15 +931,24 @@ extern "C" int gsz_shard_reduce_mean(const gsz_plan* p, int32_t owner,
                                      const uint16_t* const* contrib, int32_t layout, float* g,
                                      double* partial_out, void* ws, size_t ws_bytes,
                                      hipStream_t stream) {
-    return reduce_impl(p, owner, contrib, layout, g, partial_out, ws, ws_bytes, stream, false,
-                       "gsz_shard_reduce_mean");
+    return reduce_impl(p, owner, reinterpret_cast<const void* const*>(contrib), layout, g,
+                       partial_out, ws, ws_bytes, stream, false, false, "gsz_shard_reduce_mean");
+}
+
+extern "C" int gsz_shard_reduce_mean_f32(const gsz_plan* p, int32_t owner,
+                                         const float* const* contrib, int32_t layout, float* g,
+                                         double* partial_out, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+    return reduce_impl(p, owner, reinterpret_cast<const void* const*>(contrib), layout, g,
+                       partial_out, ws, ws_bytes, stream, false, true, "gsz_shard_reduce_mean_f32");
 }
 
 extern "C" int gsz_shard_reduce_mean_bf16_wire(const gsz_plan* p, int32_t owner,
                                                const uint16_t* const* contrib, int32_t layout,
                                                float* g, double* partial_out, void* ws,
                                                size_t ws_bytes, hipStream_t stream) {
-    return reduce_impl(p, owner, contrib, layout, g, partial_out, ws, ws_bytes, stream, true,
+    return reduce_impl(p, owner, reinterpret_cast<const void* const*>(contrib), layout, g,
+                       partial_out, ws, ws_bytes, stream, true, false,
                        "gsz_shard_reduce_mean_bf16_wire");
 }
 

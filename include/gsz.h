@@ -244,6 +244,19 @@ int gsz_allgather_layout_write(const gsz_plan* plan, int32_t owner, const uint16
 int gsz_bucket_accumulate(const gsz_plan* plan, const uint16_t* const* grads, uint16_t* flat,
                           hipStream_t stream);
 
+/* The same accumulation into fp32 buckets (reduce_dtype = fp32: "Distributed
+ * Training ...", section FSDP1 vs FSDP2 and DTensor).  flat32 (device,
+ * flat_len fp32, 16-byte aligned) is the bucket-major buffer in fp32.
+ *   gsz_bucket_pack_f32:        flat32[off_t + j] = f32(grads[t][j]) (exact), pads 0
+ *                               (the first micro-batch of a window);
+ *   gsz_bucket_accumulate_f32:  flat32[off_t + j] = flat32[off_t + j] + f32(grads[t][j])
+ *                               (one fp32 add, nearest even); pads not touched.
+ * grads as for gsz_bucket_pack.  The buffers then feed gsz_shard_reduce_mean_f32. */
+int gsz_bucket_pack_f32(const gsz_plan* plan, const uint16_t* const* grads, float* flat32,
+                        hipStream_t stream);
+int gsz_bucket_accumulate_f32(const gsz_plan* plan, const uint16_t* const* grads, float* flat32,
+                              hipStream_t stream);
+
 /* --------------------------------------------- reduce-dtype variant --- */
 
 /* gsz_shard_reduce_mean with bf16 partial sums on the wire ("Data Parallelism:
@@ -255,6 +268,17 @@ int gsz_shard_reduce_mean_bf16_wire(const gsz_plan* plan, int32_t owner,
                                     const uint16_t* const* contrib, int32_t layout, float* g,
                                     double* partial_out, void* ws, size_t ws_bytes,
                                     hipStream_t stream);
+
+/* gsz_shard_reduce_mean over fp32 contributions (fp32 accumulation buckets,
+ * fp32 on the wire; reduce_dtype = fp32, "Distributed Training ...", section
+ * FSDP1 vs FSDP2 and DTensor): the same ring order
+ * ((c_{r+1} + c_{r+2}) + ...) + c_r and division by P, the inputs taken as they
+ * are.  contrib: P device pointers to fp32 buffers (flat_len for
+ * GSZ_LAYOUT_BUCKET_FLAT, S for GSZ_LAYOUT_SHARD_COMPACT), 16-byte aligned.
+ * Other arguments, outputs and errors as gsz_shard_reduce_mean. */
+int gsz_shard_reduce_mean_f32(const gsz_plan* plan, int32_t owner, const float* const* contrib,
+                              int32_t layout, float* g, double* partial_out, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------- unshard side and DDP --- */
 

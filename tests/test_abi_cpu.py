@@ -153,6 +153,13 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         G.shard_reduce_mean(p, 0, [torch.zeros(p.shard_len, dtype=torch.bfloat16)] * 4,
                             G.LAYOUT_SHARD_COMPACT, torch.zeros(p.shard_len))
+    with pytest.raises(ValueError):
+        G.bucket_pack_f32(p, grads, torch.zeros(p.flat_len))
+    with pytest.raises(ValueError):
+        G.bucket_accumulate_f32(p, grads, torch.zeros(p.flat_len))
+    with pytest.raises(ValueError):
+        G.shard_reduce_mean_f32(p, 0, [torch.zeros(p.shard_len)] * 4, G.LAYOUT_SHARD_COMPACT,
+                                torch.zeros(p.shard_len))
 
 
 def test_torch_hip_runtime_is_loaded_before_the_library():

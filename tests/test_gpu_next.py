@@ -95,3 +95,102 @@ def test_bf16_wire_reduce_all_owners(cfg):
         n_all += err.size
     print(f"[{w.name}] bf16 wire vs fp32 accumulation: {changed / n_all:.1%} of elements differ; "
           f"largest difference {worst:.2f} of the rounding bound", flush=True)
+
+
+# --- fp32 accumulation buckets and the fp32-contribution reduce -------------
+
+MICRO_F32 = 1100    # generator rank field of rank q's micro-batch k: MICRO_F32 + 8q + k
+
+
+def rank_micro_dev(w, q, k):
+    out = []
+    for s0, n in zip(GI.prefix(w.numel), w.numel):
+        t = torch.empty(n, dtype=torch.uint16, device="cuda")
+        if n:
+            gen.dev_fill(t, w.cfg_id, W.KIND_GRAD, MICRO_F32 + 8 * q + k, s0, w.grad_std,
+                         gen.MODE_BF16)
+        out.append(t)
+    return out
+
+
+def rank_micro_host(w, q, k):
+    flat = gen.host_fill(w.cfg_id, W.KIND_GRAD, MICRO_F32 + 8 * q + k, 0, w.n_params,
+                         w.grad_std, gen.MODE_BF16)
+    return [flat[s0:s0 + n] for s0, n in zip(OI.prefix(w.numel), w.numel)]
+
+
+def compact_from_flat(plan, flat, r):
+    """Owner r's chunks of a device flat buffer, in shard order (library plan)."""
+    return torch.cat([flat[b["base"] + r * b["chunk"]:b["base"] + (r + 1) * b["chunk"]]
+                      for b in plan.buckets()]).contiguous()
+
+
+@pytest.mark.parametrize("cfg,micro,owners", [(0, 4, None), (1, 2, (0, 7))])
+def test_fp32_accumulation_then_fp32_reduce(cfg, micro, owners):
+    w = W.by_id(cfg)
+    P = w.world_size
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    oplan = make_plan(w.numel, w.bucket_cap_bytes, P)
+    dev, ref = [], []
+    for q in range(P):
+        f = torch.full((plan.flat_len,), float("nan"), dtype=torch.float32, device="cuda")
+        G.bucket_pack_f32(plan, rank_micro_dev(w, q, 0), f)      # also writes the pads
+        for k in range(1, micro):
+            G.bucket_accumulate_f32(plan, rank_micro_dev(w, q, k), f)
+        o = opack.pack_f32(oplan, rank_micro_host(w, q, 0))
+        for k in range(1, micro):
+            o = opack.accumulate_f32(oplan, o, rank_micro_host(w, q, k))
+        dev.append(f)
+        ref.append(o)
+    torch.cuda.synchronize()
+    for q in range(P):
+        assert_bits(host(dev[q]), ref[q], f"{w.name}: fp32 buckets of rank {q}")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+    part = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for r in (owners or range(P)):
+        g = torch.empty(plan.shard_len, dtype=torch.float32, device="cuda")
+        G.shard_reduce_mean_f32(plan, r, dev, G.LAYOUT_BUCKET_FLAT, g, part, ws)
+        gc = torch.empty_like(g)
+        G.shard_reduce_mean_f32(plan, r, [compact_from_flat(plan, f, r) for f in dev],
+                                G.LAYOUT_SHARD_COMPACT, gc)
+        torch.cuda.synchronize()
+        want = reduce_mean([opack.owner_view(oplan, o, r) for o in ref], r)
+        assert_bits(host(g), want, f"{w.name}: fp32-contribution mean, owner {r}")
+        assert_bits(host(gc), want, f"{w.name}: fp32-contribution mean, owner {r} (shard-compact)")
+        sq = sqnorm_partial(want)
+        assert abs(host(part)[0] - sq) <= 1e-12 * sq
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 6, 7, 8, 16])
+def test_fp32_reduce_every_rank_count(P):
+    """Fixed-P kernels (1, 2, 8, 16) and the generic loop with true division."""
+    rng = np.random.default_rng(300 + P)
+    numel = [int(x) for x in rng.integers(1, 5000, 9)]
+    plan = G.Plan(numel, 6000, P, 8).upload()
+    oplan = make_plan(numel, 6000, P, align=8)
+    host_flats = [opack.pack_f32(oplan, [np.asarray(rng.integers(0, 65536, n), np.uint16) & 0xBFFF
+                                         for n in numel]) for _ in range(P)]
+    flats = [torch.from_numpy(f).cuda() for f in host_flats]
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+    part = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for r in sorted({0, P // 2, P - 1}):
+        g = torch.empty(plan.shard_len, dtype=torch.float32, device="cuda")
+        G.shard_reduce_mean_f32(plan, r, flats, G.LAYOUT_BUCKET_FLAT, g, part, ws)
+        torch.cuda.synchronize()
+        want = reduce_mean([opack.owner_view(oplan, f, r) for f in host_flats], r)
+        assert_bits(host(g), want, f"P={P} owner {r}")
+
+
+def test_fp32_accumulation_unaligned_sources():
+    numel = [1001, 17, 4096]
+    plan = G.Plan(numel, 1 << 20, 2).upload()
+    oplan = make_plan(numel, 1 << 20, 2)
+    base = torch.arange(1, 8000, dtype=torch.int16, device="cuda").view(torch.uint16)
+    grads = [base[1:1 + 1001], base[1003:1003 + 17], base[1021:1021 + 4096]]   # odd offsets
+    flat = torch.full((plan.flat_len,), 3.0, dtype=torch.float32, device="cuda")
+    G.bucket_pack_f32(plan, grads, flat)
+    G.bucket_accumulate_f32(plan, grads, flat)
+    torch.cuda.synchronize()
+    hg = [host(t) for t in grads]
+    want = opack.accumulate_f32(oplan, opack.pack_f32(oplan, hg), hg)
+    assert_bits(host(flat), want, "unaligned fp32 accumulation")
