@@ -161,9 +161,10 @@ def test_fp32_accumulation_then_fp32_reduce(cfg, micro, owners):
         assert abs(host(part)[0] - sq) <= 1e-12 * sq
 
 
-@pytest.mark.parametrize("P", [1, 2, 3, 5, 6, 7, 8, 16])
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 6, 7, 8, 16, 100, 256])
 def test_fp32_reduce_every_rank_count(P):
-    """Fixed-P kernels (1, 2, 8, 16) and the generic loop with true division."""
+    """Fixed-P kernels (2, 8, 16) and the generic loop (1, 3, 5, 6, 7, 100, 256)
+    with true division where P is not a power of two."""
     rng = np.random.default_rng(300 + P)
     numel = [int(x) for x in rng.integers(1, 5000, 9)]
     plan = G.Plan(numel, 6000, P, 8).upload()

@@ -165,10 +165,11 @@ def test_clip_kernel_against_oracle_on_given_partials():
         assert gn == n32 and gc == c32, (parts, gn, n32, gc, c32)
 
 
-@pytest.mark.parametrize("P", [1, 2, 3, 5, 6, 12, 16, 32, 64])
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 6, 12, 16, 32, 64, 100, 256])
 def test_reduce_every_rank_count(P):
-    """Static-P kernels (2..64) and the dynamic-P kernel (1, 3, 5, 6, 12),
-    power-of-two and true-division paths, ragged tensor sizes."""
+    """Static-P kernels (2..64) and the dynamic-P kernel (1, 3, 5, 6, 12, 100,
+    and 256 = the largest world size, a full pointer table), power-of-two and
+    true-division paths, ragged tensor sizes."""
     rng = np.random.default_rng(P)
     numel = [int(x) for x in rng.integers(1, 3000, 9)]
     numel[0] = 0
