@@ -304,24 +304,24 @@ def bench_ddp(args):
     pflat = torch.empty(L, dtype=torch.uint16, device="cuda")
     pbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
     params = [pbuf[s0:s0 + n] for s0, n in zip(GI.prefix(w.numel), w.numel)]
-    ws = torch.zeros(G.workspace_bytes(plan.flat_len) // 8, dtype=torch.float64, device="cuda")
-    part = torch.zeros(1, dtype=torch.float64, device="cuda")
+    # the all-reduce writes the P chunk owners' norm partials in the same pass
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+    parts = torch.zeros(P, dtype=torch.float64, device="cuda")
     coef = torch.empty(1, dtype=torch.float32, device="cuda")
-    names = ["bucket_pack", "allreduce_mean", "shard_grad_sqnorm", "clip_coef", "adamw_step",
-             "bucket_unpack"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    names = ["bucket_pack", "allreduce_mean", "clip_coef", "adamw_step", "bucket_unpack"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
 
     def step(e=None):
         calls = [lambda: G.bucket_pack(plan, my_grads, flats[r]),
-                 lambda: G.allreduce_mean(plan, flats, g),
-                 lambda: G.shard_grad_sqnorm(g, part, ws),
-                 lambda: G.clip_coef(part, w.hp.max_norm, coef),
+                 lambda: G.allreduce_mean(plan, flats, g, parts, ws),
+                 lambda: G.clip_coef(parts, w.hp.max_norm, coef),
                  lambda: G.adamw_step(master, m, v, g, coef, w.hp, pflat),
                  lambda: G.bucket_unpack(plan, pflat, params)]
         for i, c in enumerate(calls):
             if e: e[i].record()
             c()
-        if e: e[6].record()
+        if e: e[len(calls)].record()
 
     for _ in range(args.warmup):
         step()
@@ -336,7 +336,7 @@ def bench_ddp(args):
     per = {n: float(np.mean(v)) for n, v in samples.items()}
     step_gpu = gpu_step_stats(ev)
     byts = {"bucket_pack": 4 * w.n_params + 2 * (L - w.n_params),
-            "allreduce_mean": (2 * P + 4) * L, "shard_grad_sqnorm": 4 * L, "clip_coef": 20,
+            "allreduce_mean": (2 * P + 4) * L, "clip_coef": 8 * P + 12,
             "adamw_step": 30 * L, "bucket_unpack": 4 * w.n_params}
     kern = {n: dict(ms=per[n], ms_median=float(np.median(samples[n])), ms_min=float(np.min(samples[n])),
                     bytes=byts[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9) for n in names}

@@ -75,7 +75,7 @@ _SIGS = {
     "gsz_bucket_accumulate_f32": [_P, _P, _P, _P],
     "gsz_shard_reduce_mean_f32": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_shard_reduce_mean_bf16_wire": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
-    "gsz_allreduce_mean": [_P, _P, _P, _P],
+    "gsz_allreduce_mean": [_P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_adamw_step": [_P, _P, _P, _P, _I64, _P, ctypes.POINTER(AdamWHP), _P, _P],
 }
 
@@ -338,13 +338,18 @@ def bucket_unpack(plan, flat, params, stream=None):
     _check(load().gsz_bucket_unpack(plan.handle, _ptr(flat, "flat", bt), ptrs, _stream(stream)))
 
 
-def allreduce_mean(plan, contribs, g_flat, stream=None):
+def allreduce_mean(plan, contribs, g_flat, partials=None, ws=None, stream=None):
+    """gsz_allreduce_mean; with partials (P doubles) and ws, the per-chunk-owner
+    squared-norm partials are written in the same pass."""
     bt = _bf16_types()
     if len(contribs) != plan.world_size:
         raise ValueError("need one contribution per rank")
     ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", bt) for i, t in enumerate(contribs)])
+    wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load().gsz_allreduce_mean(plan.handle, ptrs, _ptr(g_flat, "g_flat", _f32()),
-                                     _stream(stream)))
+                                     _ptr(partials, "partials", _f64(), allow_none=True),
+                                     wsp, nbytes, _stream(stream)))
 
 
 def adamw_step(master, m, v, g, coef, hp, out_bf16, stream=None):

@@ -686,7 +686,9 @@ void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPt
             hipLaunchKernelGGL((k_reduce_mean<PS, false, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
         return;
     }
-    if (outflat)
+    if (outflat && norm)
+        hipLaunchKernelGGL((k_reduce_mean<PS, true, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+    else if (outflat)
         hipLaunchKernelGGL((k_reduce_mean<PS, false, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
     else if (norm && flat)
         hipLaunchKernelGGL((k_reduce_mean<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
@@ -1045,13 +1047,26 @@ extern "C" int gsz_bucket_unpack(const gsz_plan* p, const uint16_t* flat, uint16
 }
 
 extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* contrib, float* g_flat,
-                                  hipStream_t stream) {
+                                  double* partials, void* ws, size_t ws_bytes, hipStream_t stream) {
     const char* who = "gsz_allreduce_mean";
     int rc = check_plan(p, who);
     if (rc) return rc;
     const int P = p->P;
     const int64_t S = p->shard_len;
-    if (S == 0) return GSZ_OK;
+    if (partials) {
+        size_t need = 0;
+        gsz_workspace_bytes(S, &need);
+        if (!ws || ws_bytes < need) { set_error("%s: workspace of %zu bytes required", who, need); return GSZ_ERR_SIZE; }
+        if (misaligned(ws)) { set_error("%s: workspace is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED; }
+    }
+    if (S == 0) {
+        if (partials)
+            for (int c = 0; c < P; ++c) {
+                launch_finalize(static_cast<double*>(ws), 0, partials + c, stream);
+                if ((rc = launched(who))) return rc;
+            }
+        return GSZ_OK;
+    }
     if (!g_flat || !contrib) { set_error("%s: NULL buffer", who); return GSZ_ERR_INVALID_ARG; }
     if (misaligned(g_flat)) { set_error("%s: g_flat is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED; }
     for (int q = 0; q < P; ++q) {
@@ -1059,23 +1074,32 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
         if (misaligned(contrib[q])) { set_error("%s: contribution %d is not 16-byte aligned", who, q); return GSZ_ERR_MISALIGNED; }
     }
     const int64_t nvec = S / 8;
-    const dim3 gr(flat_grid((nvec + kBlock - 1) / kBlock));
+    const int grid = flat_grid((S + kRedTile - 1) / kRedTile);
+    const dim3 gr(grid);
     const int pow2 = (P & (P - 1)) == 0;
     const float invP = pow2 ? 1.0f / (float)P : 0.0f;
     const int nseg = (int)p->buckets.size();
-    for (int c = 0; c < P; ++c) {      // chunk c of every bucket, summed in ring order ending at rank c
+    const bool norm = partials != nullptr;
+    double* wsd = static_cast<double*>(ws);
+    // chunk c of every bucket, summed in ring order ending at rank c; its norm
+    // partial is finalized before the next launch reuses the workspace (stream order)
+    for (int c = 0; c < P; ++c) {
         RankPtrs rp{};
         for (int k = 0; k < P; ++k) rp.p[k] = contrib[(c + 1 + k) % P];
         switch (P) {
-            case 2: launch_reduce<2>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
-            case 4: launch_reduce<4>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
-            case 8: launch_reduce<8>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
-            case 16: launch_reduce<16>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
-            case 32: launch_reduce<32>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
-            case 64: launch_reduce<64>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
-            default: launch_reduce<0>(false, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, nullptr, true); break;
+            case 2: launch_reduce<2>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
+            case 4: launch_reduce<4>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
+            case 8: launch_reduce<8>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
+            case 16: launch_reduce<16>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
+            case 32: launch_reduce<32>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
+            case 64: launch_reduce<64>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
+            default: launch_reduce<0>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
         }
         if ((rc = launched(who))) return rc;
+        if (norm) {
+            launch_finalize(wsd, grid, partials + c, stream);
+            if ((rc = launched(who))) return rc;
+        }
     }
     return GSZ_OK;
 }

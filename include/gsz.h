@@ -297,9 +297,14 @@ int gsz_bucket_unpack(const gsz_plan* plan, const uint16_t* flat, uint16_t* cons
  * mean of the P bucket-flat contributions at flat position p, where the ring
  * of chunk c ends at rank c -- so chunk c of g_flat is bit-identical to what
  * gsz_shard_reduce_mean gives owner c.  contrib (host array of P device
- * pointers, each flat_len bf16); g_flat (device, flat_len fp32). */
+ * pointers, each flat_len bf16); g_flat (device, flat_len fp32).
+ * partials (device, P doubles, may be NULL): partials[c] = the squared norm of
+ * chunk-owner c's part of g_flat (fp64, as gsz_shard_reduce_mean's partial for
+ * owner c), fused into the same pass, so gsz_clip_coef over them gives the
+ * global clip coefficient with no separate norm pass.  ws/ws_bytes as for
+ * gsz_shard_reduce_mean (gsz_workspace_bytes(shard_len)); required if partials. */
 int gsz_allreduce_mean(const gsz_plan* plan, const uint16_t* const* contrib, float* g_flat,
-                       hipStream_t stream);
+                       double* partials, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* The replicated (DDP) optimizer update: the AdamW of gsz_shard_adamw_step on
  * n contiguous elements, bf16 result written contiguously to out_bf16.

@@ -9,6 +9,7 @@ import torch
 
 import gradient_sync_zero_amd as G
 from oracle import pack as opack
+from oracle.norm import sqnorm_partial
 from oracle.plan import make_plan
 from oracle.step import ddp_step
 from synth import workloads as W
@@ -62,6 +63,23 @@ def test_ddp_step_and_unpack(cfg):
     assert_bits(host(params_flat), d["p"], "bf16 params (flat)")
     for t, (a, b) in enumerate(zip(params, opack.unpack(oplan, d["p"]))):
         assert_bits(host(a), b, f"unpacked parameter {t}")
+
+    say(f"[{w.name}] all-reduce with the norm partials fused in")
+    g2 = torch.full((plan.flat_len,), float("nan"), dtype=torch.float32, device="cuda")
+    parts = torch.full((P,), 7.0, dtype=torch.float64, device="cuda")
+    ws2 = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+    G.allreduce_mean(plan, flats, g2, parts, ws2)
+    coef2 = torch.empty(1, dtype=torch.float32, device="cuda")
+    tot2 = torch.empty(1, dtype=torch.float64, device="cuda")
+    G.clip_coef(parts, w.hp.max_norm, coef2, None, tot2)
+    torch.cuda.synchronize()
+    assert_bits(host(g2), d["g"], "all-reduce mean with fused norm")
+    hp_ = host(parts)
+    for c in range(P):                # partial c is owner c's part of the norm
+        want = sqnorm_partial(opack.owner_view(oplan, d["g"], c))
+        assert abs(hp_[c] - want) <= 1e-12 * max(want, 1e-300)
+    assert abs(float(host(tot2)[0]) - d["total"]) <= 1e-12 * d["total"]
+    assert host(coef2)[0] == d["coef"]
 
     say(f"[{w.name}] DDP chunks equal the ZeRO owners' reduce")
     gf = host(g_flat)
