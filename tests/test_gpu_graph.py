@@ -79,3 +79,63 @@ def test_graph_replays_equal_eager_steps(cfg, owners):
         for i, (x, y) in enumerate(zip(got, want[k])):
             assert_bits(x, y, f"replay {k}, buffer {i}")
         del junk
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_graph_replays_equal_eager_ddp_steps(cfg):
+    """The unsharded step (pack, all-reduce with fused norm partials, clip,
+    replicated AdamW, unpack) captured once and replayed."""
+    w = W.by_id(cfg)
+    P = w.world_size
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    my_grads = GI.rank_grads_separate(w, 0)
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+
+    def buffers():
+        flats = []
+        for q in range(P):
+            f = torch.empty(plan.flat_len, dtype=torch.uint16, device="cuda")
+            G.bucket_pack(plan, GI.rank_grads_separate(w, q), f)
+            flats.append(f)
+        th, m, v = GI.full_state(plan, w)
+        return dict(flats=flats, th=th, m=m, v=v,
+                    g=torch.empty(plan.flat_len, device="cuda"),
+                    parts=torch.full((P,), 0.5, dtype=torch.float64, device="cuda"),
+                    coef=torch.empty(1, device="cuda"),
+                    pflat=torch.zeros(plan.flat_len, dtype=torch.uint16, device="cuda"),
+                    params=[torch.zeros(n, dtype=torch.uint16, device="cuda") for n in w.numel])
+
+    def step(b):
+        G.bucket_pack(plan, my_grads, b["flats"][0])
+        G.allreduce_mean(plan, b["flats"], b["g"], b["parts"], ws)
+        G.clip_coef(b["parts"], w.hp.max_norm, b["coef"])
+        G.adamw_step(b["th"], b["m"], b["v"], b["g"], b["coef"], w.hp, b["pflat"])
+        G.bucket_unpack(plan, b["pflat"], b["params"])
+
+    def snapshot(b):
+        torch.cuda.synchronize()
+        return [host(b[k]) for k in ("g", "parts", "coef", "th", "m", "v", "pflat")] + \
+               [host(t) for t in b["params"]]
+
+    eager = buffers()
+    want = []
+    for _ in range(3):
+        step(eager)
+        want.append(snapshot(eager))
+
+    b = buffers()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(b)
+    torch.cuda.synchronize()
+    for k in range(3):
+        graph.replay()
+        junk = torch.randn(1 << 20, device="cuda").sum()        # eager work between replays
+        torch.cuda.synchronize()
+        got = snapshot(b)
+        for i, (x, y) in enumerate(zip(got, want[k])):
+            assert_bits(x, y, f"DDP replay {k}, buffer {i}")
+        del junk
