@@ -144,23 +144,37 @@ def _pmc_per_dispatch(csv_path, counter):
     return by
 
 
+KERNEL_SOURCES = ("gsz_device.h", "gsz_internal.h", "gsz_kernels_adamw.h", "gsz_kernels_pack.h",
+                  "gsz_kernels_reduce.h", "gsz_step.hip")
+
+
+def kernel_source_digest():
+    """SHA-256 over the library's kernel sources (names and contents), the key
+    that ties a counter summary to the kernels it measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(name.encode() + b"\0")
+        h.update(open(os.path.join(ROOT, "gradient_sync_zero_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def summarize_pmc(fetch_csv, write_csv, workload, command, copy_bytes):
     """FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by the ratio
     of known bytes to what it reads for the plain copy of copy_bytes."""
-    import hashlib
     import numpy as np
     f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
     w = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
     cf = float(np.median(f["copy"])) * 1024
     cw = float(np.median(w["copy"])) * 1024
     sf, sw = copy_bytes / cf, copy_bytes / cw
-    src = open(os.path.join(ROOT, "gradient_sync_zero_amd", "csrc", "gsz_step.hip"), "rb").read()
+    digest = kernel_source_digest()
     out = [f"# HBM traffic per launch from rocprofv3 counters: {workload}", "#",
            f"# command: {command}", "#",
            f"# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the copy kernel's",
            f"# known bytes ({copy_bytes} read, {copy_bytes} written): fetch x {sf:.4f}, "
            f"write x {sw:.4f}.", "# A kernel edited after this file was written gets traffic = null.",
-           f"source_sha256 = {hashlib.sha256(src).hexdigest()}",
+           f"source_sha256 = {digest}",
            f"copy.fetch_scale = {sf:.6f}", f"copy.write_scale = {sw:.6f}"]
     for name in sorted(set(f) & set(w)):
         if name in ("synth_fill", "torch_fill", "hip_runtime_copy"):
@@ -179,7 +193,6 @@ def summarize_pmc(fetch_csv, write_csv, workload, command, copy_bytes):
 def read_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summary, or None if it
     is missing or was taken on a different kernel source."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -188,8 +201,8 @@ def read_traffic(kernel, workload):
         m = re.match(r"^\s*([\w.]+)\s*=\s*(\S+)\s*$", line)
         if m:
             kv[m.group(1)] = m.group(2)
-    src = open(os.path.join(ROOT, "gradient_sync_zero_amd", "csrc", "gsz_step.hip"), "rb").read()
-    if kv.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    digest = kernel_source_digest()
+    if kv.get("source_sha256") != digest:
         return None
     key = f"{kernel}.hbm_bytes_per_launch"
     return float(kv[key]) if key in kv else None

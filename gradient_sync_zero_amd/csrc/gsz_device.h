@@ -1,0 +1,137 @@
+// Device-side building blocks shared by the kernels of the shard step: vector
+// types, launch constants, bf16 conversions, 16-byte loads and stores, the
+// fixed-order block sum, the bucket-segment cursor and the XCD-aware block order.
+//
+// Every kernel of the library is HBM-bound streaming work (no contraction, so no
+// MFMA): 16-byte loads and stores per lane, 64-wide wavefronts, and one short
+// block per tile with the grid covering the data.  Blocks are dispatched in
+// index order, so the lines in flight stay close together in the address space;
+// on MI355X that moves 10-20% more bytes per second than long-running
+// grid-stride blocks.  fp64 reductions run in a fixed order (wave shuffles, LDS,
+// one partial per block, then fixed ranges of partials) so results are
+// bit-reproducible.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gsz_internal.h"
+
+#pragma clang fp contract(off)
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr int kBlock = 256;
+// The pack kernels' block: one wave per 1 KiB tile copied 2.7% faster than
+// 256-lane blocks on 2 KiB tiles (7B share, MI355X).
+constexpr int kPackBlock = 64;
+// AdamW's block size (8 waves of 512 elements): measured faster than 256.
+constexpr int kAdamBlock = 512;
+// Largest grid: grid * block work-items must stay below 2^32 per dispatch.
+// Bigger inputs make blocks stride over the remaining tiles.
+constexpr int64_t kMaxFlatGrid = (int64_t)1 << 23;
+// MI355X dispatches block b of a grid to XCD b mod 8.  xcd_remap gives XCD x one
+// contiguous range of logical blocks instead (a bijection on [0, G)): the
+// reduce, which reads P buffers at the same offsets, runs 1.7-1.9% faster that
+// way on the 7B and 70B shares; pack and AdamW run slower and keep the plain order.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t G) {
+    const int64_t q = G / kXcds, rem = G % kXcds, x = b % kXcds;
+    return x * q + (x < rem ? x : rem) + b / kXcds;
+}
+// Elements per block of the reductions (8 per lane).
+constexpr int64_t kRedTile = 8 * kBlock;
+static_assert(kRedTile == gsz::kRedElems && kMaxFlatGrid == gsz::kMaxRedGrid,
+              "the workspace size assumes these grids");
+
+struct RankPtrs { const uint16_t* p[GSZ_MAX_RANKS]; };
+struct RankPtrsF { const float* p[GSZ_MAX_RANKS]; };
+struct PackPtrs { const uint16_t* p[gsz::kPackBatch]; };
+
+// fp32 constants of the AdamW update, each rounded once from double on the host.
+struct AdamScalars { float b1, omb1, b2, omb2, bc1, bc2, lr, eps, decay; };
+
+// ----------------------------------------------------------- device utils --
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ f32x4 ldf4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void stf4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+__device__ __forceinline__ void widen8(u32x4 w, float a[8]) {
+    a[0] = bf16_lo(w.x); a[1] = bf16_hi(w.x); a[2] = bf16_lo(w.y); a[3] = bf16_hi(w.y);
+    a[4] = bf16_lo(w.z); a[5] = bf16_hi(w.z); a[6] = bf16_lo(w.w); a[7] = bf16_hi(w.w);
+}
+
+// a[j] = a[j] + widen(w)[j]: one IEEE fp32 add per element, partial sum on the left.
+__device__ __forceinline__ void add8(u32x4 w, float a[8]) {
+    a[0] = a[0] + bf16_lo(w.x); a[1] = a[1] + bf16_hi(w.x);
+    a[2] = a[2] + bf16_lo(w.y); a[3] = a[3] + bf16_hi(w.y);
+    a[4] = a[4] + bf16_lo(w.z); a[5] = a[5] + bf16_hi(w.z);
+    a[6] = a[6] + bf16_lo(w.w); a[7] = a[7] + bf16_hi(w.w);
+}
+
+// a[j] <- bf16(a[j]) (round to nearest even), kept as fp32.
+__device__ __forceinline__ void round8_bf16(float a[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = __uint_as_float(bf16_rne(a[j]) << 16);
+}
+
+// Sum over the block in a fixed order; the result is valid in thread 0.
+__device__ double block_sum(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = x + __shfl_xor(x, o, 64);
+    __shared__ double part[kBlock / 64];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < kBlock / 64; ++k) s = s + part[k];
+    }
+    return s;
+}
+
+// Walks the bucket segments of a shard in increasing order.  seg rows are
+// {shard_off, base, chunk}; row nseg is {S, 0, 0}.  For shard index i in bucket
+// b, the all-gather / flat position is i + delta with
+// delta = base_b + owner*C_b - shard_off_b.
+struct SegCursor {
+    const int64_t* seg;
+    int64_t owner, end, delta;
+    int b;
+    __device__ void seek(int64_t i, int nseg) {
+        int lo = 0, hi = nseg - 1;          // largest b with shard_off[b] <= i
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seg[3 * mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+        load();
+    }
+    __device__ void load() {
+        end = seg[3 * (b + 1)];
+        delta = seg[3 * b + 1] + owner * seg[3 * b + 2] - seg[3 * b];
+    }
+    __device__ __forceinline__ int64_t map(int64_t i) {
+        while (i >= end) { ++b; load(); }
+        return i + delta;
+    }
+};
+
+}  // namespace

@@ -1,0 +1,88 @@
+// The fused AdamW update with its bf16 output in all-gather or shard layout, and
+// the standalone all-gather layout writer.  Pages cited (title, section): see gsz.h.
+#pragma once
+
+#include "gsz_device.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+// ----------------------------------------------------------------- AdamW --
+
+__device__ __forceinline__ void adamw1(float& th, float& mm, float& vv, float gg, float coef,
+                                       const AdamScalars& s) {
+    const float gc = gg * coef;
+    const float m1 = (s.b1 * mm) + (s.omb1 * gc);
+    const float v1 = (s.b2 * vv) + (s.omb2 * (gc * gc));
+    const float mh = m1 / s.bc1;
+    const float vh = v1 / s.bc2;
+    const float u = mh / (sqrtf(vh) + s.eps);
+    th = (th * s.decay) - (s.lr * u);
+    mm = m1;
+    vv = v1;
+}
+
+// A wave owns 512 consecutive shard elements per iteration, as two groups of
+// 256; lane l updates elements 4l..4l+3 of each group, so every 16-byte load
+// and store instruction of the wave covers 1 KiB of whole 128-byte lines (a
+// lane that loads 32 contiguous bytes as two 16-byte halves makes each
+// instruction touch half of every line, and half-line misses to the same line
+// are fetched twice).  The bf16 result goes out as 8 bytes per lane.
+template <bool GATH, bool SHARD>
+__global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master, float* __restrict__ m,
+                                                      float* __restrict__ v, const float* __restrict__ g,
+                                                      const float* __restrict__ coefp, AdamScalars s,
+                                                      const int64_t* __restrict__ seg, int nseg,
+                                                      int64_t owner, int64_t S,
+                                                      uint16_t* __restrict__ gathered,
+                                                      uint16_t* __restrict__ shard_bf16) {
+    constexpr int kWaves = kAdamBlock / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
+    int64_t wv = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t ntile = (S + 511) / 512;
+    const float coef = *coefp;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    if (GATH && wv < ntile) cur.seek(wv * 512, nseg);        // wave-uniform: scalar loads
+    for (; wv < ntile; wv += nwaves) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t i = wv * 512 + h * 256 + 4 * lane;
+            if (i < S) {                       // S and i are multiples of 4
+                const f32x4 g4 = ldf4(g + i);
+                const f32x4 t4 = ldf4(master + i), m4 = ldf4(m + i), v4 = ldf4(v + i);
+                float th[4] = {t4.x, t4.y, t4.z, t4.w};
+                float mm[4] = {m4.x, m4.y, m4.z, m4.w};
+                float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+                const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) adamw1(th[j], mm[j], vv[j], gg[j], coef, s);
+                stf4(master + i, f32x4{th[0], th[1], th[2], th[3]});
+                stf4(m + i, f32x4{mm[0], mm[1], mm[2], mm[3]});
+                stf4(v + i, f32x4{vv[0], vv[1], vv[2], vv[3]});
+                const u32x2 p = u32x2{bf16_rne(th[0]) | (bf16_rne(th[1]) << 16),
+                                      bf16_rne(th[2]) | (bf16_rne(th[3]) << 16)};
+                if (GATH) *reinterpret_cast<u32x2*>(gathered + cur.map(i)) = p;
+                if (SHARD) *reinterpret_cast<u32x2*>(shard_bf16 + i) = p;
+            }
+        }
+    }
+}
+
+// gathered[i + delta_b] = shard[i] for shard index i of bucket b.
+__global__ __launch_bounds__(kBlock) void k_ag_write(const uint16_t* __restrict__ shard,
+                                                     const int64_t* __restrict__ seg, int nseg,
+                                                     int64_t owner, int64_t nvec,
+                                                     uint16_t* __restrict__ gathered) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    if (v < nvec) cur.seek((int64_t)blockIdx.x * kBlock * 8, nseg);   // the block's first element
+    for (; v < nvec; v += stride) {
+        const int64_t i = v * 8;
+        st16(gathered + cur.map(i), ld16(shard + i));
+    }
+}
+
+}  // namespace

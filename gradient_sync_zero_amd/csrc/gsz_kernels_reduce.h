@@ -1,0 +1,228 @@
+// Reduction kernels: the ring-order mean of P contributions (bf16 or fp32, with
+// the fused norm partial), the standalone squared norm, the fixed-order
+// finalize and the clip coefficient.  Pages cited (title, section): see gsz.h.
+#pragma once
+
+#include "gsz_device.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+// ---------------------------------------------------------- reduce-mean --
+
+// g[i] = (((c0 + c1) + c2) + ... + c_{P-1}) / P with rp.p[k] = contribution of
+// rank (owner+1+k) mod P, so the owner's own value is added last.  Each lane
+// handles 8 consecutive shard elements per iteration (one 16-byte load per
+// rank).  PS > 0 fixes P at compile time; loads are issued in groups of up to
+// 16 ranks before their adds so many 16-byte requests are in flight.  With
+// OUTFLAT (bucket-flat input only) g is indexed by flat position instead of
+// shard index: P launches, one per chunk owner, give the all-reduce result.
+// W16: the partial sum is rounded to bf16 after every addition (a ring whose
+// wire carries bf16 partial sums); the final division stays fp32.
+template <int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
+__global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
+                                                        const int64_t* __restrict__ seg, int nseg,
+                                                        int64_t owner, int64_t nvec,
+                                                        float* __restrict__ g,
+                                                        double* __restrict__ ws) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);      // logical block: tile bx
+    int64_t v = bx * kBlock + threadIdx.x;
+    double sq = 0.0;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    if (FLAT && v < nvec) cur.seek(bx * kRedTile, nseg);      // uniform: scalar loads
+    const float fP = (float)P;
+    for (; v < nvec; v += stride) {
+        const int64_t i = v * 8;
+        const int64_t off = FLAT ? cur.map(i) : i;
+        float a[8];
+        if constexpr (PS > 0) {
+            constexpr int G = PS < 16 ? PS : 16;
+#pragma unroll
+            for (int k0 = 0; k0 < PS; k0 += G) {
+                u32x4 w[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) w[j] = ld16(rp.p[k0 + j] + off);
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if (k0 + j == 0) widen8(w[j], a);
+                    else { add8(w[j], a); if (W16) round8_bf16(a); }
+                }
+            }
+        } else {
+            widen8(ld16(rp.p[0] + off), a);
+            int k = 1;
+            for (; k + 8 <= P; k += 8) {
+                u32x4 w[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) w[j] = ld16(rp.p[k + j] + off);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) { add8(w[j], a); if (W16) round8_bf16(a); }
+            }
+            for (; k < P; ++k) { add8(ld16(rp.p[k] + off), a); if (W16) round8_bf16(a); }
+        }
+        if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = a[j] * invP;   // exact: invP is a power of two
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = a[j] / fP;
+        }
+        const int64_t o = OUTFLAT ? off : i;    // all-reduce output: the flat position
+        stf4(g + o, f32x4{a[0], a[1], a[2], a[3]});
+        stf4(g + o + 4, f32x4{a[4], a[5], a[6], a[7]});
+        if (NORM) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double d = (double)a[j];
+                sq = __fma_rn(d, d, sq);                        // d*d is exact in fp64
+            }
+        }
+    }
+    if (NORM) {
+        const double s = block_sum(sq);
+        if (threadIdx.x == 0) ws[bx] = s;
+    }
+}
+
+// The reduce over fp32 contributions (fp32 accumulation buckets, fp32 on the
+// ring's wire): the same ring order and division as k_reduce_mean, inputs
+// taken as they are.  A wave owns 512 shard elements of its block's tile as two
+// groups of 256; lane l handles elements 4l..4l+3 of each, so every 16-byte
+// load and store of a wave covers whole lines.  Blocks, XCD order and norm
+// partials as k_reduce_mean.
+template <int PS, bool NORM, bool FLAT>
+__global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P, float invP, int pow2,
+                                                            const int64_t* __restrict__ seg, int nseg,
+                                                            int64_t owner, int64_t S,
+                                                            float* __restrict__ g,
+                                                            double* __restrict__ ws) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);
+    double sq = 0.0;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    int64_t t = bx * kRedTile;
+    if (FLAT && t < S) cur.seek(t, nseg);                     // uniform: scalar loads
+    const float fP = (float)P;
+    for (; t < S; t += (int64_t)gridDim.x * kRedTile) {
+        const int64_t i0 = t + 512 * wave + 4 * lane, i1 = i0 + 256;
+        const bool ok0 = i0 < S, ok1 = i1 < S;               // S and i are multiples of 4
+        const int64_t off0 = ok0 ? (FLAT ? cur.map(i0) : i0) : 0;
+        const int64_t off1 = ok1 ? (FLAT ? cur.map(i1) : i1) : 0;
+        const f32x4 zero = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 a = zero, b = zero;
+        if constexpr (PS > 0) {
+            constexpr int G = PS < 16 ? PS : 16;
+#pragma unroll
+            for (int k0 = 0; k0 < PS; k0 += G) {
+                f32x4 w0[G], w1[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    w0[j] = ok0 ? ldf4(rp.p[k0 + j] + off0) : zero;
+                    w1[j] = ok1 ? ldf4(rp.p[k0 + j] + off1) : zero;
+                }
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if (k0 + j == 0) { a = w0[j]; b = w1[j]; }
+                    else {
+                        a.x = a.x + w0[j].x; a.y = a.y + w0[j].y; a.z = a.z + w0[j].z; a.w = a.w + w0[j].w;
+                        b.x = b.x + w1[j].x; b.y = b.y + w1[j].y; b.z = b.z + w1[j].z; b.w = b.w + w1[j].w;
+                    }
+                }
+            }
+        } else {
+            a = ok0 ? ldf4(rp.p[0] + off0) : zero;
+            b = ok1 ? ldf4(rp.p[0] + off1) : zero;
+            for (int k = 1; k < P; ++k) {
+                const f32x4 w0 = ok0 ? ldf4(rp.p[k] + off0) : zero;
+                const f32x4 w1 = ok1 ? ldf4(rp.p[k] + off1) : zero;
+                a.x = a.x + w0.x; a.y = a.y + w0.y; a.z = a.z + w0.z; a.w = a.w + w0.w;
+                b.x = b.x + w1.x; b.y = b.y + w1.y; b.z = b.z + w1.z; b.w = b.w + w1.w;
+            }
+        }
+        if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
+            a = f32x4{a.x * invP, a.y * invP, a.z * invP, a.w * invP};   // exact: a power of two
+            b = f32x4{b.x * invP, b.y * invP, b.z * invP, b.w * invP};
+        } else {
+            a = f32x4{a.x / fP, a.y / fP, a.z / fP, a.w / fP};
+            b = f32x4{b.x / fP, b.y / fP, b.z / fP, b.w / fP};
+        }
+        if (ok0) stf4(g + i0, a);
+        if (ok1) stf4(g + i1, b);
+        if (NORM) {
+            const double d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sq = __fma_rn(d[j], d[j], sq);   // zeros where !ok
+        }
+    }
+    if (NORM) {
+        const double s = block_sum(sq);
+        if (threadIdx.x == 0) ws[bx] = s;
+    }
+}
+
+// Standalone squared norm of n fp32 values (16-byte aligned): block b sums
+// elements [b * kRedTile, (b + 1) * kRedTile) (two lane-contiguous 16-byte
+// loads per lane) into ws[b].
+__global__ __launch_bounds__(kBlock) void k_sqnorm(const float* __restrict__ g, int64_t n,
+                                                   double* __restrict__ ws) {
+    const int tid = threadIdx.x;
+    double sq = 0.0;
+    for (int64_t base = (int64_t)blockIdx.x * kRedTile; base < n; base += (int64_t)gridDim.x * kRedTile) {
+        if (base + kRedTile <= n) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 x = ldf4(g + base + h * (4 * kBlock) + 4 * tid);
+                const double d0 = x.x, d1 = x.y, d2 = x.z, d3 = x.w;
+                sq = __fma_rn(d0, d0, sq); sq = __fma_rn(d1, d1, sq);
+                sq = __fma_rn(d2, d2, sq); sq = __fma_rn(d3, d3, sq);
+            }
+        } else {
+            for (int64_t i = base + tid; i < n; i += kBlock) {
+                const double d = g[i];
+                sq = __fma_rn(d, d, sq);
+            }
+        }
+    }
+    const double s = block_sum(sq);
+    if (threadIdx.x == 0) ws[blockIdx.x] = s;
+}
+
+// ws2[b] = sum, in order, of the partials in the b-th of gridDim.x contiguous
+// ranges of ws[0, n).
+__global__ __launch_bounds__(kBlock) void k_finalize_ranges(const double* __restrict__ ws, int64_t n,
+                                                            double* __restrict__ ws2) {
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t a = (int64_t)blockIdx.x * per, e = a + per < n ? a + per : n;
+    double s = 0.0;
+    for (int64_t k = a + threadIdx.x; k < e; k += kBlock) s = s + ws[k];
+    s = block_sum(s);
+    if (threadIdx.x == 0) ws2[blockIdx.x] = s;
+}
+
+// out = sum of the n block partials, in block order, one block.
+__global__ __launch_bounds__(kBlock) void k_finalize(const double* __restrict__ ws, int64_t n,
+                                                     double* __restrict__ out) {
+    double s = 0.0;
+    for (int64_t k = threadIdx.x; k < n; k += kBlock) s = s + ws[k];
+    s = block_sum(s);
+    if (threadIdx.x == 0) *out = s;
+}
+
+// total = partials[0] + ... + partials[n-1] (rank order); norm = fp32(sqrt(total));
+// coef = min(1, max_norm / (norm + 1e-6)); NaN propagates.
+__global__ void k_clip(const double* __restrict__ partials, int n, float max_norm,
+                       float* __restrict__ coef, float* __restrict__ norm,
+                       double* __restrict__ total) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    double t = 0.0;
+    for (int q = 0; q < n; ++q) t = t + partials[q];
+    const float nr = (float)sqrt(t);
+    const float c = max_norm / (nr + 1e-6f);
+    *coef = (c != c) ? c : (c < 1.0f ? c : 1.0f);
+    if (norm) *norm = nr;
+    if (total) *total = t;
+}
+
+}  // namespace

@@ -1,579 +1,26 @@
-// gfx950 kernels of the shard step and the device half of the C ABI.
-//
-// Every kernel here is HBM-bound streaming work (no contraction, so no MFMA):
-// 16-byte loads and stores per lane, 64-wide wavefronts, and one short block per
-// tile with the grid covering the data.  Blocks are dispatched in index order,
-// so the lines in flight stay close together in the address space; on MI355X
-// that moves 10-20% more bytes per second than long-running grid-stride blocks.
-// fp64 reductions run in a fixed order (wave shuffles, LDS, one partial per
-// block, then fixed ranges of partials) so results are bit-reproducible.
+// Host half of the C ABI: argument checks, launch shapes and the entry points of
+// include/gsz.h.  The kernels live in gsz_kernels_*.h (one header per part of
+// the step, shared pieces in gsz_device.h), all compiled in this one
+// translation unit.
 //
 // Pages cited (title, section): see gsz.h.
+#pragma clang fp contract(off)
+
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cmath>
 #include <cstring>
 
+#include "gsz_device.h"
 #include "gsz_internal.h"
-
-#pragma clang fp contract(off)
+#include "gsz_kernels_adamw.h"
+#include "gsz_kernels_pack.h"
+#include "gsz_kernels_reduce.h"
 
 using gsz::set_error;
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
 namespace {
-
-constexpr int kBlock = 256;
-// The pack kernels' block: one wave per 1 KiB tile copied 2.7% faster than
-// 256-lane blocks on 2 KiB tiles (7B share, MI355X).
-constexpr int kPackBlock = 64;
-// AdamW's block size (8 waves of 512 elements): measured faster than 256.
-constexpr int kAdamBlock = 512;
-// Largest grid: grid * block work-items must stay below 2^32 per dispatch.
-// Bigger inputs make blocks stride over the remaining tiles.
-constexpr int64_t kMaxFlatGrid = (int64_t)1 << 23;
-// MI355X dispatches block b of a grid to XCD b mod 8.  xcd_remap gives XCD x one
-// contiguous range of logical blocks instead (a bijection on [0, G)): the
-// reduce, which reads P buffers at the same offsets, runs 1.7-1.9% faster that
-// way on the 7B and 70B shares; pack and AdamW run slower and keep the plain order.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t G) {
-    const int64_t q = G / kXcds, rem = G % kXcds, x = b % kXcds;
-    return x * q + (x < rem ? x : rem) + b / kXcds;
-}
-// Elements per block of the reductions (8 per lane).
-constexpr int64_t kRedTile = 8 * kBlock;
-static_assert(kRedTile == gsz::kRedElems && kMaxFlatGrid == gsz::kMaxRedGrid,
-              "the workspace size assumes these grids");
-
-struct RankPtrs { const uint16_t* p[GSZ_MAX_RANKS]; };
-struct RankPtrsF { const float* p[GSZ_MAX_RANKS]; };
-struct PackPtrs { const uint16_t* p[gsz::kPackBatch]; };
-
-// fp32 constants of the AdamW update, each rounded once from double on the host.
-struct AdamScalars { float b1, omb1, b2, omb2, bc1, bc2, lr, eps, decay; };
-
-// ----------------------------------------------------------- device utils --
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-__device__ __forceinline__ f32x4 ldf4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ void stf4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-
-__device__ __forceinline__ void widen8(u32x4 w, float a[8]) {
-    a[0] = bf16_lo(w.x); a[1] = bf16_hi(w.x); a[2] = bf16_lo(w.y); a[3] = bf16_hi(w.y);
-    a[4] = bf16_lo(w.z); a[5] = bf16_hi(w.z); a[6] = bf16_lo(w.w); a[7] = bf16_hi(w.w);
-}
-
-// a[j] = a[j] + widen(w)[j]: one IEEE fp32 add per element, partial sum on the left.
-__device__ __forceinline__ void add8(u32x4 w, float a[8]) {
-    a[0] = a[0] + bf16_lo(w.x); a[1] = a[1] + bf16_hi(w.x);
-    a[2] = a[2] + bf16_lo(w.y); a[3] = a[3] + bf16_hi(w.y);
-    a[4] = a[4] + bf16_lo(w.z); a[5] = a[5] + bf16_hi(w.z);
-    a[6] = a[6] + bf16_lo(w.w); a[7] = a[7] + bf16_hi(w.w);
-}
-
-// a[j] <- bf16(a[j]) (round to nearest even), kept as fp32.
-__device__ __forceinline__ void round8_bf16(float a[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = __uint_as_float(bf16_rne(a[j]) << 16);
-}
-
-// Sum over the block in a fixed order; the result is valid in thread 0.
-__device__ double block_sum(double x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = x + __shfl_xor(x, o, 64);
-    __shared__ double part[kBlock / 64];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
-    __syncthreads();
-    double s = 0.0;
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int k = 0; k < kBlock / 64; ++k) s = s + part[k];
-    }
-    return s;
-}
-
-// Walks the bucket segments of a shard in increasing order.  seg rows are
-// {shard_off, base, chunk}; row nseg is {S, 0, 0}.  For shard index i in bucket
-// b, the all-gather / flat position is i + delta with
-// delta = base_b + owner*C_b - shard_off_b.
-struct SegCursor {
-    const int64_t* seg;
-    int64_t owner, end, delta;
-    int b;
-    __device__ void seek(int64_t i, int nseg) {
-        int lo = 0, hi = nseg - 1;          // largest b with shard_off[b] <= i
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (seg[3 * mid] <= i) lo = mid; else hi = mid - 1;
-        }
-        b = lo;
-        load();
-    }
-    __device__ void load() {
-        end = seg[3 * (b + 1)];
-        delta = seg[3 * b + 1] + owner * seg[3 * b + 2] - seg[3 * b];
-    }
-    __device__ __forceinline__ int64_t map(int64_t i) {
-        while (i >= end) { ++b; load(); }
-        return i + delta;
-    }
-};
-
-// ------------------------------------------------------------------ pack --
-
-// Pack modes: copy tensors into the flat buffer, copy flat ranges back into the
-// tensors, or add tensors into the flat buffer (bf16 += bf16 in fp32, rounded
-// to nearest even).
-enum PackMode { kPack = 0, kUnpack = 1, kAccumulate = 2 };
-
-__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
-    return bf16_rne(bf16_lo(a) + bf16_lo(b)) | (bf16_rne(bf16_hi(a) + bf16_hi(b)) << 16);
-}
-__device__ __forceinline__ u32x4 add_bf16x8(u32x4 a, u32x4 b) {
-    return u32x4{add_bf16x2(a.x, b.x), add_bf16x2(a.y, b.y), add_bf16x2(a.z, b.z),
-                 add_bf16x2(a.w, b.w)};
-}
-__device__ __forceinline__ uint16_t add_bf16(uint16_t a, uint16_t b) {
-    return (uint16_t)bf16_rne(__uint_as_float((uint32_t)a << 16) + __uint_as_float((uint32_t)b << 16));
-}
-
-// Moves the tensors of one batch (bucket-order positions [k0, k0+nk)) to or
-// from the flat buffer as MODE says.  tab rows: {flat offset, numel, first
-// tile}.  One block per tile of kPackTile = 8 * kPackBlock elements (one
-// 16-byte vector per lane), the grid covering the batch's tiles [t_begin, t_end): short
-// blocks dispatched in address order keep the lines in flight close together,
-// which MI355X's HBM rewards over long-running grid-stride blocks.  Grids are
-// capped below the dispatch limit; blocks then stride over the remaining tiles.
-template <int MODE>
-__global__ __launch_bounds__(kPackBlock) void k_pack(PackPtrs pp, const int64_t* __restrict__ tab,
-                                                 int k0, int nk, int64_t t_begin, int64_t t_end,
-                                                 uint16_t* __restrict__ flat) {
-    const int tid = threadIdx.x;
-    for (int64_t tile = t_begin + blockIdx.x; tile < t_end; tile += gridDim.x) {
-        int lo = k0, hi = k0 + nk - 1;          // largest k with first_tile[k] <= tile
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (tab[3 * mid + 2] <= tile) lo = mid; else hi = mid - 1;
-        }
-        const int k = lo;
-        const int64_t n = tab[3 * k + 1];
-        const int64_t j0 = (tile - tab[3 * k + 2]) * gsz::kPackTile;
-        const int64_t j1 = j0 + gsz::kPackTile < n ? j0 + gsz::kPackTile : n;
-        const uint16_t* __restrict__ src = MODE == kUnpack ? flat + tab[3 * k] : pp.p[k - k0];
-        uint16_t* __restrict__ dst = MODE == kUnpack ? const_cast<uint16_t*>(pp.p[k - k0]) : flat + tab[3 * k];
-        const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
-        if (vec && j1 - j0 == gsz::kPackTile) {
-            static_assert(gsz::kPackTile == 8 * kPackBlock, "one vector per lane");
-            // Nontemporal hints on both sides: the bytes are used once (2-3% faster).
-            const int64_t j = j0 + 8 * tid;
-            u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + j));
-            if (MODE == kAccumulate) w = add_bf16x8(ld16(dst + j), w);
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + j));
-        } else if (vec) {
-            const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
-            for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kPackBlock)
-                st16(dst + j, MODE == kAccumulate ? add_bf16x8(ld16(dst + j), ld16(src + j)) : ld16(src + j));
-            for (int64_t j = jv + tid; j < j1; j += kPackBlock)
-                dst[j] = MODE == kAccumulate ? add_bf16(dst[j], src[j]) : src[j];
-        } else {
-            for (int64_t j = j0 + tid; j < j1; j += kPackBlock)
-                dst[j] = MODE == kAccumulate ? add_bf16(dst[j], src[j]) : src[j];
-        }
-    }
-}
-
-// Zeroes the padding at the end of each padded bucket; one block per bucket.
-__global__ __launch_bounds__(kBlock) void k_zero_pads(const int64_t* __restrict__ pads,
-                                                      uint16_t* __restrict__ flat) {
-    const int64_t s = pads[2 * blockIdx.x], n = pads[2 * blockIdx.x + 1];
-    for (int64_t j = threadIdx.x; j < n; j += kBlock) flat[s + j] = 0;
-}
-
-// fp32 accumulation buckets (gradient accumulation with an fp32 reduction
-// dtype): ACC = false widens the tensors of one batch into flat32 (the first
-// micro-batch), ACC = true adds them: flat32[off_t + j] = flat32[off_t + j] +
-// f32(grad_t[j]), one IEEE fp32 addition.  Tiles and grid as k_pack.  In a full
-// tile lane l takes elements 4l..4l+3 and 256+4l..256+4l+3 (two 8-byte bf16
-// loads), so each 16-byte fp32 load and store of the wave covers whole lines;
-// with nontemporal hints on every access this runs 5-6% faster than one 16-byte
-// bf16 load per lane widened into two half-line fp32 stores.
-__device__ __forceinline__ void stf8(float* p, const float a[8]) {
-    stf4(p, f32x4{a[0], a[1], a[2], a[3]});
-    stf4(p + 4, f32x4{a[4], a[5], a[6], a[7]});
-}
-template <bool ACC>
-__global__ __launch_bounds__(kPackBlock) void k_pack_f32(PackPtrs pp, const int64_t* __restrict__ tab,
-                                                     int k0, int nk, int64_t t_begin, int64_t t_end,
-                                                     float* __restrict__ flat) {
-    const int tid = threadIdx.x;
-    for (int64_t tile = t_begin + blockIdx.x; tile < t_end; tile += gridDim.x) {
-        int lo = k0, hi = k0 + nk - 1;          // largest k with first_tile[k] <= tile
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (tab[3 * mid + 2] <= tile) lo = mid; else hi = mid - 1;
-        }
-        const int k = lo;
-        const int64_t n = tab[3 * k + 1];
-        const int64_t j0 = (tile - tab[3 * k + 2]) * gsz::kPackTile;
-        const int64_t j1 = j0 + gsz::kPackTile < n ? j0 + gsz::kPackTile : n;
-        const uint16_t* __restrict__ src = pp.p[k - k0];
-        float* __restrict__ dst = flat + tab[3 * k];
-        const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
-        if (vec && j1 - j0 == gsz::kPackTile) {
-            static_assert(gsz::kPackTile == 8 * kPackBlock, "two groups of 4 elements per lane");
-            const int64_t ja = j0 + 4 * tid, jb = ja + 4 * kPackBlock;
-            const u32x2 wa = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src + ja));
-            const u32x2 wb = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src + jb));
-            f32x4 xa = f32x4{bf16_lo(wa.x), bf16_hi(wa.x), bf16_lo(wa.y), bf16_hi(wa.y)};
-            f32x4 xb = f32x4{bf16_lo(wb.x), bf16_hi(wb.x), bf16_lo(wb.y), bf16_hi(wb.y)};
-            if (ACC) {
-                const f32x4 da = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dst + ja));
-                const f32x4 db = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dst + jb));
-                xa = f32x4{da.x + xa.x, da.y + xa.y, da.z + xa.z, da.w + xa.w};
-                xb = f32x4{db.x + xb.x, db.y + xb.y, db.z + xb.z, db.w + xb.w};
-            }
-            __builtin_nontemporal_store(xa, reinterpret_cast<f32x4*>(dst + ja));
-            __builtin_nontemporal_store(xb, reinterpret_cast<f32x4*>(dst + jb));
-        } else if (vec) {
-            const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
-            for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kPackBlock) {
-                float a[8];
-                widen8(ld16(src + j), a);
-                if (ACC) {
-                    const f32x4 d0 = ldf4(dst + j), d1 = ldf4(dst + j + 4);
-                    a[0] = d0.x + a[0]; a[1] = d0.y + a[1]; a[2] = d0.z + a[2]; a[3] = d0.w + a[3];
-                    a[4] = d1.x + a[4]; a[5] = d1.y + a[5]; a[6] = d1.z + a[6]; a[7] = d1.w + a[7];
-                }
-                stf8(dst + j, a);
-            }
-            for (int64_t j = jv + tid; j < j1; j += kPackBlock) {
-                const float x = __uint_as_float((uint32_t)src[j] << 16);
-                dst[j] = ACC ? dst[j] + x : x;
-            }
-        } else {
-            for (int64_t j = j0 + tid; j < j1; j += kPackBlock) {
-                const float x = __uint_as_float((uint32_t)src[j] << 16);
-                dst[j] = ACC ? dst[j] + x : x;
-            }
-        }
-    }
-}
-
-// Zeroes the padding of each padded bucket of an fp32 buffer; one block per bucket.
-__global__ __launch_bounds__(kBlock) void k_zero_pads_f32(const int64_t* __restrict__ pads,
-                                                          float* __restrict__ flat) {
-    const int64_t s = pads[2 * blockIdx.x], n = pads[2 * blockIdx.x + 1];
-    for (int64_t j = threadIdx.x; j < n; j += kBlock) flat[s + j] = 0.0f;
-}
-
-// ---------------------------------------------------------- reduce-mean --
-
-// g[i] = (((c0 + c1) + c2) + ... + c_{P-1}) / P with rp.p[k] = contribution of
-// rank (owner+1+k) mod P, so the owner's own value is added last.  Each lane
-// handles 8 consecutive shard elements per iteration (one 16-byte load per
-// rank).  PS > 0 fixes P at compile time; loads are issued in groups of up to
-// 16 ranks before their adds so many 16-byte requests are in flight.  With
-// OUTFLAT (bucket-flat input only) g is indexed by flat position instead of
-// shard index: P launches, one per chunk owner, give the all-reduce result.
-// W16: the partial sum is rounded to bf16 after every addition (a ring whose
-// wire carries bf16 partial sums); the final division stays fp32.
-template <int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
-__global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
-                                                        const int64_t* __restrict__ seg, int nseg,
-                                                        int64_t owner, int64_t nvec,
-                                                        float* __restrict__ g,
-                                                        double* __restrict__ ws) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);      // logical block: tile bx
-    int64_t v = bx * kBlock + threadIdx.x;
-    double sq = 0.0;
-    SegCursor cur{seg, owner, 0, 0, 0};
-    if (FLAT && v < nvec) cur.seek(bx * kRedTile, nseg);      // uniform: scalar loads
-    const float fP = (float)P;
-    for (; v < nvec; v += stride) {
-        const int64_t i = v * 8;
-        const int64_t off = FLAT ? cur.map(i) : i;
-        float a[8];
-        if constexpr (PS > 0) {
-            constexpr int G = PS < 16 ? PS : 16;
-#pragma unroll
-            for (int k0 = 0; k0 < PS; k0 += G) {
-                u32x4 w[G];
-#pragma unroll
-                for (int j = 0; j < G; ++j) w[j] = ld16(rp.p[k0 + j] + off);
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    if (k0 + j == 0) widen8(w[j], a);
-                    else { add8(w[j], a); if (W16) round8_bf16(a); }
-                }
-            }
-        } else {
-            widen8(ld16(rp.p[0] + off), a);
-            int k = 1;
-            for (; k + 8 <= P; k += 8) {
-                u32x4 w[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) w[j] = ld16(rp.p[k + j] + off);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) { add8(w[j], a); if (W16) round8_bf16(a); }
-            }
-            for (; k < P; ++k) { add8(ld16(rp.p[k] + off), a); if (W16) round8_bf16(a); }
-        }
-        if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a[j] = a[j] * invP;   // exact: invP is a power of two
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a[j] = a[j] / fP;
-        }
-        const int64_t o = OUTFLAT ? off : i;    // all-reduce output: the flat position
-        stf4(g + o, f32x4{a[0], a[1], a[2], a[3]});
-        stf4(g + o + 4, f32x4{a[4], a[5], a[6], a[7]});
-        if (NORM) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const double d = (double)a[j];
-                sq = __fma_rn(d, d, sq);                        // d*d is exact in fp64
-            }
-        }
-    }
-    if (NORM) {
-        const double s = block_sum(sq);
-        if (threadIdx.x == 0) ws[bx] = s;
-    }
-}
-
-// The reduce over fp32 contributions (fp32 accumulation buckets, fp32 on the
-// ring's wire): the same ring order and division as k_reduce_mean, inputs
-// taken as they are.  A wave owns 512 shard elements of its block's tile as two
-// groups of 256; lane l handles elements 4l..4l+3 of each, so every 16-byte
-// load and store of a wave covers whole lines.  Blocks, XCD order and norm
-// partials as k_reduce_mean.
-template <int PS, bool NORM, bool FLAT>
-__global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P, float invP, int pow2,
-                                                            const int64_t* __restrict__ seg, int nseg,
-                                                            int64_t owner, int64_t S,
-                                                            float* __restrict__ g,
-                                                            double* __restrict__ ws) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);
-    double sq = 0.0;
-    SegCursor cur{seg, owner, 0, 0, 0};
-    int64_t t = bx * kRedTile;
-    if (FLAT && t < S) cur.seek(t, nseg);                     // uniform: scalar loads
-    const float fP = (float)P;
-    for (; t < S; t += (int64_t)gridDim.x * kRedTile) {
-        const int64_t i0 = t + 512 * wave + 4 * lane, i1 = i0 + 256;
-        const bool ok0 = i0 < S, ok1 = i1 < S;               // S and i are multiples of 4
-        const int64_t off0 = ok0 ? (FLAT ? cur.map(i0) : i0) : 0;
-        const int64_t off1 = ok1 ? (FLAT ? cur.map(i1) : i1) : 0;
-        const f32x4 zero = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        f32x4 a = zero, b = zero;
-        if constexpr (PS > 0) {
-            constexpr int G = PS < 16 ? PS : 16;
-#pragma unroll
-            for (int k0 = 0; k0 < PS; k0 += G) {
-                f32x4 w0[G], w1[G];
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    w0[j] = ok0 ? ldf4(rp.p[k0 + j] + off0) : zero;
-                    w1[j] = ok1 ? ldf4(rp.p[k0 + j] + off1) : zero;
-                }
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    if (k0 + j == 0) { a = w0[j]; b = w1[j]; }
-                    else {
-                        a.x = a.x + w0[j].x; a.y = a.y + w0[j].y; a.z = a.z + w0[j].z; a.w = a.w + w0[j].w;
-                        b.x = b.x + w1[j].x; b.y = b.y + w1[j].y; b.z = b.z + w1[j].z; b.w = b.w + w1[j].w;
-                    }
-                }
-            }
-        } else {
-            a = ok0 ? ldf4(rp.p[0] + off0) : zero;
-            b = ok1 ? ldf4(rp.p[0] + off1) : zero;
-            for (int k = 1; k < P; ++k) {
-                const f32x4 w0 = ok0 ? ldf4(rp.p[k] + off0) : zero;
-                const f32x4 w1 = ok1 ? ldf4(rp.p[k] + off1) : zero;
-                a.x = a.x + w0.x; a.y = a.y + w0.y; a.z = a.z + w0.z; a.w = a.w + w0.w;
-                b.x = b.x + w1.x; b.y = b.y + w1.y; b.z = b.z + w1.z; b.w = b.w + w1.w;
-            }
-        }
-        if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
-            a = f32x4{a.x * invP, a.y * invP, a.z * invP, a.w * invP};   // exact: a power of two
-            b = f32x4{b.x * invP, b.y * invP, b.z * invP, b.w * invP};
-        } else {
-            a = f32x4{a.x / fP, a.y / fP, a.z / fP, a.w / fP};
-            b = f32x4{b.x / fP, b.y / fP, b.z / fP, b.w / fP};
-        }
-        if (ok0) stf4(g + i0, a);
-        if (ok1) stf4(g + i1, b);
-        if (NORM) {
-            const double d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sq = __fma_rn(d[j], d[j], sq);   // zeros where !ok
-        }
-    }
-    if (NORM) {
-        const double s = block_sum(sq);
-        if (threadIdx.x == 0) ws[bx] = s;
-    }
-}
-
-// Standalone squared norm of n fp32 values (16-byte aligned): block b sums
-// elements [b * kRedTile, (b + 1) * kRedTile) (two lane-contiguous 16-byte
-// loads per lane) into ws[b].
-__global__ __launch_bounds__(kBlock) void k_sqnorm(const float* __restrict__ g, int64_t n,
-                                                   double* __restrict__ ws) {
-    const int tid = threadIdx.x;
-    double sq = 0.0;
-    for (int64_t base = (int64_t)blockIdx.x * kRedTile; base < n; base += (int64_t)gridDim.x * kRedTile) {
-        if (base + kRedTile <= n) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const f32x4 x = ldf4(g + base + h * (4 * kBlock) + 4 * tid);
-                const double d0 = x.x, d1 = x.y, d2 = x.z, d3 = x.w;
-                sq = __fma_rn(d0, d0, sq); sq = __fma_rn(d1, d1, sq);
-                sq = __fma_rn(d2, d2, sq); sq = __fma_rn(d3, d3, sq);
-            }
-        } else {
-            for (int64_t i = base + tid; i < n; i += kBlock) {
-                const double d = g[i];
-                sq = __fma_rn(d, d, sq);
-            }
-        }
-    }
-    const double s = block_sum(sq);
-    if (threadIdx.x == 0) ws[blockIdx.x] = s;
-}
-
-// ws2[b] = sum, in order, of the partials in the b-th of gridDim.x contiguous
-// ranges of ws[0, n).
-__global__ __launch_bounds__(kBlock) void k_finalize_ranges(const double* __restrict__ ws, int64_t n,
-                                                            double* __restrict__ ws2) {
-    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
-    const int64_t a = (int64_t)blockIdx.x * per, e = a + per < n ? a + per : n;
-    double s = 0.0;
-    for (int64_t k = a + threadIdx.x; k < e; k += kBlock) s = s + ws[k];
-    s = block_sum(s);
-    if (threadIdx.x == 0) ws2[blockIdx.x] = s;
-}
-
-// out = sum of the n block partials, in block order, one block.
-__global__ __launch_bounds__(kBlock) void k_finalize(const double* __restrict__ ws, int64_t n,
-                                                     double* __restrict__ out) {
-    double s = 0.0;
-    for (int64_t k = threadIdx.x; k < n; k += kBlock) s = s + ws[k];
-    s = block_sum(s);
-    if (threadIdx.x == 0) *out = s;
-}
-
-// total = partials[0] + ... + partials[n-1] (rank order); norm = fp32(sqrt(total));
-// coef = min(1, max_norm / (norm + 1e-6)); NaN propagates.
-__global__ void k_clip(const double* __restrict__ partials, int n, float max_norm,
-                       float* __restrict__ coef, float* __restrict__ norm,
-                       double* __restrict__ total) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    double t = 0.0;
-    for (int q = 0; q < n; ++q) t = t + partials[q];
-    const float nr = (float)sqrt(t);
-    const float c = max_norm / (nr + 1e-6f);
-    *coef = (c != c) ? c : (c < 1.0f ? c : 1.0f);
-    if (norm) *norm = nr;
-    if (total) *total = t;
-}
-
-// ----------------------------------------------------------------- AdamW --
-
-__device__ __forceinline__ void adamw1(float& th, float& mm, float& vv, float gg, float coef,
-                                       const AdamScalars& s) {
-    const float gc = gg * coef;
-    const float m1 = (s.b1 * mm) + (s.omb1 * gc);
-    const float v1 = (s.b2 * vv) + (s.omb2 * (gc * gc));
-    const float mh = m1 / s.bc1;
-    const float vh = v1 / s.bc2;
-    const float u = mh / (sqrtf(vh) + s.eps);
-    th = (th * s.decay) - (s.lr * u);
-    mm = m1;
-    vv = v1;
-}
-
-// A wave owns 512 consecutive shard elements per iteration, as two groups of
-// 256; lane l updates elements 4l..4l+3 of each group, so every 16-byte load
-// and store instruction of the wave covers 1 KiB of whole 128-byte lines (a
-// lane that loads 32 contiguous bytes as two 16-byte halves makes each
-// instruction touch half of every line, and half-line misses to the same line
-// are fetched twice).  The bf16 result goes out as 8 bytes per lane.
-template <bool GATH, bool SHARD>
-__global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master, float* __restrict__ m,
-                                                      float* __restrict__ v, const float* __restrict__ g,
-                                                      const float* __restrict__ coefp, AdamScalars s,
-                                                      const int64_t* __restrict__ seg, int nseg,
-                                                      int64_t owner, int64_t S,
-                                                      uint16_t* __restrict__ gathered,
-                                                      uint16_t* __restrict__ shard_bf16) {
-    constexpr int kWaves = kAdamBlock / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
-    int64_t wv = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t ntile = (S + 511) / 512;
-    const float coef = *coefp;
-    SegCursor cur{seg, owner, 0, 0, 0};
-    if (GATH && wv < ntile) cur.seek(wv * 512, nseg);        // wave-uniform: scalar loads
-    for (; wv < ntile; wv += nwaves) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t i = wv * 512 + h * 256 + 4 * lane;
-            if (i < S) {                       // S and i are multiples of 4
-                const f32x4 g4 = ldf4(g + i);
-                const f32x4 t4 = ldf4(master + i), m4 = ldf4(m + i), v4 = ldf4(v + i);
-                float th[4] = {t4.x, t4.y, t4.z, t4.w};
-                float mm[4] = {m4.x, m4.y, m4.z, m4.w};
-                float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-                const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) adamw1(th[j], mm[j], vv[j], gg[j], coef, s);
-                stf4(master + i, f32x4{th[0], th[1], th[2], th[3]});
-                stf4(m + i, f32x4{mm[0], mm[1], mm[2], mm[3]});
-                stf4(v + i, f32x4{vv[0], vv[1], vv[2], vv[3]});
-                const u32x2 p = u32x2{bf16_rne(th[0]) | (bf16_rne(th[1]) << 16),
-                                      bf16_rne(th[2]) | (bf16_rne(th[3]) << 16)};
-                if (GATH) *reinterpret_cast<u32x2*>(gathered + cur.map(i)) = p;
-                if (SHARD) *reinterpret_cast<u32x2*>(shard_bf16 + i) = p;
-            }
-        }
-    }
-}
-
-// gathered[i + delta_b] = shard[i] for shard index i of bucket b.
-__global__ __launch_bounds__(kBlock) void k_ag_write(const uint16_t* __restrict__ shard,
-                                                     const int64_t* __restrict__ seg, int nseg,
-                                                     int64_t owner, int64_t nvec,
-                                                     uint16_t* __restrict__ gathered) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    SegCursor cur{seg, owner, 0, 0, 0};
-    if (v < nvec) cur.seek((int64_t)blockIdx.x * kBlock * 8, nseg);   // the block's first element
-    for (; v < nvec; v += stride) {
-        const int64_t i = v * 8;
-        st16(gathered + cur.map(i), ld16(shard + i));
-    }
-}
 
 // ------------------------------------------------------------ host side --
 

@@ -175,3 +175,13 @@ def test_torch_hip_runtime_is_loaded_before_the_library():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+def test_traffic_digest_covers_every_kernel_source():
+    """The counter summaries are keyed to the kernel sources; a new header or
+    HIP file under csrc/ must be part of that key."""
+    import bench
+    csrc = os.path.join(os.path.dirname(G.LIB_PATH), "csrc")
+    on_disk = sorted(f for f in os.listdir(csrc) if f.endswith((".h", ".hip")))
+    assert sorted(bench.KERNEL_SOURCES) == on_disk
+    assert len(bench.kernel_source_digest()) == 64
