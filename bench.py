@@ -114,7 +114,7 @@ def gpu_step_stats(ev):
     return dict(mean=float(np.mean(t)), median=float(np.median(t)), min=float(np.min(t)))
 
 
-def summarize_trace(csv_path, workload, command):
+def summarize_trace(csv_path, workload, command, out_dir=None):
     import csv
     rows = list(csv.DictReader(open(csv_path)))
     out = [f"# rocprofv3 kernel statistics: {workload}", "#", f"# command: {command}", "#",
@@ -123,7 +123,7 @@ def summarize_trace(csv_path, workload, command):
         out.append(f"  {short_name(r['Name']):<16} {int(r['Calls']):>6} "
                    f"{float(r['AverageNs']) / 1e3:>10.1f} {float(r['MinNs']) / 1e3:>10.1f} "
                    f"{float(r['MaxNs']) / 1e3:>10.1f} {float(r['TotalDurationNs']) / 1e6:>10.2f}")
-    path = os.path.join(ROOT, "profiles", f"kernel_stats_{workload}.txt")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"kernel_stats_{workload}.txt")
     open(path, "w").write("\n".join(out) + "\n")
     print(path)
 
@@ -159,7 +159,7 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def summarize_pmc(fetch_csv, write_csv, workload, command, copy_bytes):
+def summarize_pmc(fetch_csv, write_csv, workload, command, copy_bytes, out_dir=None):
     """FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by the ratio
     of known bytes to what it reads for the plain copy of copy_bytes."""
     import numpy as np
@@ -185,15 +185,15 @@ def summarize_pmc(fetch_csv, write_csv, workload, command, copy_bytes):
                 f"{name}.fetch_bytes_per_launch = {fb:.0f}",
                 f"{name}.write_bytes_per_launch = {wb:.0f}",
                 f"{name}.hbm_bytes_per_launch = {fb + wb:.0f}"]
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{workload}.txt")
     open(path, "w").write("\n".join(out) + "\n")
     print(path)
 
 
-def read_traffic(kernel, workload):
+def read_traffic(kernel, workload, profiles_dir=None):
     """HBM bytes per launch from the committed counter summary, or None if it
     is missing or was taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}

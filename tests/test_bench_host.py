@@ -1,0 +1,70 @@
+"""CPU tests of the benchmark's host logic: one GPU only, and the profile
+summaries it writes and reads (synthetic rocprofv3 CSVs in a temporary
+directory; the committed profiles are not touched)."""
+import csv
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 2
+    assert "only --gpus 1" in out.stderr
+
+
+def _write_csv(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_trace_summary_names_template_instances(tmp_path):
+    rows = [("void (anonymous namespace)::k_pack<0>(PackPtrs, long const*, int, int, long, long, unsigned short*)",
+             4, 2000000, 1000000, 3000000, 8000000),
+            ("void (anonymous namespace)::k_pack<2>(PackPtrs, long const*, int, int, long, long, unsigned short*)",
+             2, 3000000, 3000000, 3000000, 6000000),
+            ("void (anonymous namespace)::k_reduce_mean<8, true, true, false, true>(RankPtrs, int, float, int, long const*, int, long, long, float*, double*)",
+             1, 500, 500, 500, 500)]
+    src = tmp_path / "stats.csv"
+    _write_csv(src, ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "TotalDurationNs"], rows)
+    bench.summarize_trace(str(src), "w", "cmd", out_dir=str(tmp_path))
+    text = (tmp_path / "kernel_stats_w.txt").read_text()
+    assert "# command: cmd" in text
+    lines = [l.split() for l in text.splitlines() if not l.startswith("#")]
+    assert lines[0][:3] == ["k_pack", "4", "2000.0"]
+    assert lines[1][0] == "k_accumulate"
+    assert lines[2][0] == "k_reduce_mean_bf16_wire"
+
+
+def test_counter_summary_scales_by_the_copy_kernel_and_is_keyed(tmp_path):
+    # FETCH_SIZE / WRITE_SIZE arrive as several rows per dispatch (one per
+    # counter instance); the summary sums them per dispatch, averages per
+    # kernel and scales by what the copy kernel of known size read.
+    copy = "synth_copy_kernel(u32x4 const*, u32x4*, long)"
+    kern = "void (anonymous namespace)::k_adamw<true, false>(float*, float*, float*, float const*, float const*, AdamScalars, long const*, int, long, long, unsigned short*, unsigned short*)"
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    copy_bytes = 1 << 20
+    fetch = [(1, copy, "FETCH_SIZE", 1024), (1, copy, "FETCH_SIZE", 1024),     # 2048 KiB: x0.5
+             (2, kern, "FETCH_SIZE", 3000), (2, kern, "FETCH_SIZE", 1000),
+             (3, kern, "FETCH_SIZE", 2000), (3, kern, "FETCH_SIZE", 2000)]
+    write = [(1, copy, "WRITE_SIZE", 1024),                                       # 1024 KiB: x1
+             (2, kern, "WRITE_SIZE", 700), (3, kern, "WRITE_SIZE", 900)]
+    _write_csv(tmp_path / "f.csv", hdr, fetch)
+    _write_csv(tmp_path / "w.csv", hdr, write)
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "w", "cmd", copy_bytes,
+                        out_dir=str(tmp_path))
+    want = 4000 * 1024 * 0.5 + 800 * 1024 * 1.0
+    got = bench.read_traffic("k_adamw", "w", profiles_dir=str(tmp_path))
+    assert abs(got - want) < 1.0
+    assert bench.read_traffic("k_pack", "w", profiles_dir=str(tmp_path)) is None
+    # a summary taken on other kernel sources is not used
+    p = tmp_path / "traffic_w.txt"
+    p.write_text(p.read_text().replace(bench.kernel_source_digest(), "0" * 64))
+    assert bench.read_traffic("k_adamw", "w", profiles_dir=str(tmp_path)) is None
