@@ -15,7 +15,7 @@ namespace {
 // rank (owner+1+k) mod P, so the owner's own value is added last.  Each lane
 // handles 8 consecutive shard elements per iteration (one 16-byte load per
 // rank).  PS > 0 fixes P at compile time; loads are issued in groups of up to
-// 16 ranks before their adds so many 16-byte requests are in flight.  With
+// 32 ranks before their adds so many 16-byte requests are in flight.  With
 // OUTFLAT (bucket-flat input only) g is indexed by flat position instead of
 // shard index: P launches, one per chunk owner, give the all-reduce result.
 // W16: the partial sum is rounded to bf16 after every addition (a ring whose
@@ -38,7 +38,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
         const int64_t off = FLAT ? cur.map(i) : i;
         float a[8];
         if constexpr (PS > 0) {
-            constexpr int G = PS < 16 ? PS : 16;
+            // up to 32 loads before their adds (at P = 64 that measured 1.4% faster than 16)
+            constexpr int G = PS < 32 ? PS : 32;
 #pragma unroll
             for (int k0 = 0; k0 < PS; k0 += G) {
                 u32x4 w[G];
