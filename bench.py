@@ -42,7 +42,9 @@ def parse():
                          "WRITE_SIZE) into profiles/traffic_<workload>.txt")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50 for the workloads up to 1.3B, 20 for the "
+                         "7B and 70B shares)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload id (synth.workloads)")
     ap.add_argument("--owner", type=int, default=0)
@@ -54,7 +56,10 @@ def parse():
                     help="also time the step captured as one HIP graph (graph_ms_per_step)")
     ap.add_argument("--copy-gib", type=float, default=4.0,
                     help="size of the plain copy used as the measured HBM ceiling")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 50 if args.config <= 2 else 20
+    return args
 
 
 def ensure_built():
