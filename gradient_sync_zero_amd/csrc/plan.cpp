@@ -53,15 +53,21 @@ extern "C" int gsz_plan_create(const int64_t* numel, int32_t n_tensors, int64_t 
     if (!out) { set_error("gsz_plan_create: out is NULL"); return GSZ_ERR_INVALID_ARG; }
     *out = nullptr;
     if (n_tensors < 0 || (n_tensors > 0 && !numel)) {
-        set_error("gsz_plan_create: bad tensor list"); return GSZ_ERR_INVALID_ARG;
+        set_error("gsz_plan_create: bad tensor list (n_tensors %d, numel %s)", n_tensors,
+                  numel ? "given" : "NULL");
+        return GSZ_ERR_INVALID_ARG;
     }
     if (bucket_cap_bytes < 1 || world_size < 1 || world_size > GSZ_MAX_RANKS || align_elems < 1) {
-        set_error("gsz_plan_create: need bucket_cap_bytes >= 1, 1 <= world_size <= %d, align >= 1",
-                  GSZ_MAX_RANKS);
+        set_error("gsz_plan_create: got bucket_cap_bytes %lld, world_size %d, align %d; need "
+                  "bucket_cap_bytes >= 1, 1 <= world_size <= %d, align >= 1",
+                  (long long)bucket_cap_bytes, world_size, align_elems, GSZ_MAX_RANKS);
         return GSZ_ERR_INVALID_ARG;
     }
     for (int32_t t = 0; t < n_tensors; ++t)
-        if (numel[t] < 0) { set_error("gsz_plan_create: tensor %d has negative size", t); return GSZ_ERR_INVALID_ARG; }
+        if (numel[t] < 0) {
+            set_error("gsz_plan_create: tensor %d has negative size %lld", t, (long long)numel[t]);
+            return GSZ_ERR_INVALID_ARG;
+        }
 
     gsz_plan* p = new (std::nothrow) gsz_plan();
     if (!p) { set_error("gsz_plan_create: out of host memory"); return GSZ_ERR_NO_MEMORY; }

@@ -185,3 +185,35 @@ def test_traffic_digest_covers_every_kernel_source():
     on_disk = sorted(f for f in os.listdir(csrc) if f.endswith((".h", ".hip")))
     assert sorted(bench.KERNEL_SOURCES) == on_disk
     assert len(bench.kernel_source_digest()) == 64
+
+
+def test_planner_and_error_text_are_thread_safe():
+    """Eight threads create plans concurrently (each checked against the
+    oracle's planner) and provoke their own errors: the last-error text is per
+    thread, so each sees its own message."""
+    import threading
+    failures = []
+
+    def worker(k):
+        rng = np.random.default_rng(100 + k)
+        try:
+            for i in range(40):
+                T = int(rng.integers(1, 30))
+                numel = [int(x) for x in rng.integers(0, 5000, T)]
+                cap, P = int(rng.integers(1, 20000)), int(rng.integers(1, 9))
+                assert_same_plan(G.Plan(numel, cap, P, 8), make_plan(numel, cap, P, 8))
+                try:
+                    G.Plan([1], 100, G.MAX_RANKS + 1 + k)            # a bad world size of its own
+                except G.GszError:
+                    msg = G.load().gsz_last_error().decode()
+                    if str(G.MAX_RANKS + 1 + k) not in msg:
+                        failures.append((k, i, msg))
+        except Exception as e:                                        # noqa: BLE001
+            failures.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not failures, failures[:3]
