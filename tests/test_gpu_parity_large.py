@@ -138,3 +138,63 @@ def test_full_size_sampled(cfg, layout, owners):
             assert_bits(gather_dev(shard_out, idx), p1, f"bf16 shard owner {r}")
         del th, m, v, g, gathered, shard_out
         torch.cuda.empty_cache()
+
+
+MICRO32 = 3000      # generator rank fields: micro-batch k of rank 0, and fp32 contribution q
+
+
+def test_fp32_rows_full_size_sampled():
+    """The fp32 accumulation buckets and the reduce over fp32 contributions at
+    the 7B share's size, in the launch shapes the benchmark times: two
+    micro-batches widened and added into rank 0's fp32 buckets (sampled flat
+    positions), and the reduce over 8 shard-compact fp32 contributions for
+    owner 0 (sampled shard elements; the norm partial by its property)."""
+    from oracle.bf16 import widen
+    w = W.by_id(3)
+    P = w.world_size
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    oplan = make_plan(w.numel, w.bucket_cap_bytes, P)
+    S = plan.shard_len
+
+    say(f"[{w.name}] fp32 buckets: widen micro-batch 0, add micro-batch 1")
+    buf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+    flat32 = torch.empty(plan.flat_len, dtype=torch.float32, device="cuda")
+    views = [buf[s0:s0 + n] for s0, n in zip(GI.prefix(w.numel), w.numel)]
+    for k in (0, 1):
+        gen.dev_fill(buf, w.cfg_id, W.KIND_GRAD, MICRO32 + k, 0, w.grad_std, gen.MODE_BF16)
+        (G.bucket_pack_f32 if k == 0 else G.bucket_accumulate_f32)(plan, views, flat32)
+        torch.cuda.synchronize()                       # buf is refilled for the next micro-batch
+    del buf, views
+    rng = np.random.default_rng(33)
+    fpos = np.unique(np.concatenate([rng.integers(0, plan.flat_len, 1 << 18),
+                                     [0, plan.flat_len - 1]]))
+    pidx = OI.param_index_of_flat(oplan, fpos)
+    g0, g1 = (widen(OI.values_at(w, W.KIND_GRAD, MICRO32 + k, w.grad_std, gen.MODE_BF16, pidx))
+              for k in (0, 1))
+    assert_bits(gather_dev(flat32, fpos), (g0 + g1).astype(np.float32), "fp32 buckets (sampled)")
+    del flat32
+    torch.cuda.empty_cache()
+
+    say(f"[{w.name}] reduce over {P} fp32 shard-compact contributions, S={S}")
+    pieces = GI.owner_pieces(plan, w, 0)
+    contribs = []
+    for q in range(P):
+        t = torch.zeros(S, dtype=torch.float32, device="cuda")
+        GI.fill_pieces(t, pieces, w, W.KIND_GRAD, MICRO32 + 16 + q, w.grad_std, gen.MODE_F32)
+        contribs.append(t)
+    g = torch.empty(S, dtype=torch.float32, device="cuda")
+    part = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(S) // 8, dtype=torch.float64, device="cuda")
+    G.shard_reduce_mean_f32(plan, 0, contribs, G.LAYOUT_SHARD_COMPACT, g, part, ws)
+    torch.cuda.synchronize()
+    del contribs
+    idx = sample_indices(oplan, 1 << 20, 200)
+    pidx = OI.param_index_of_flat(oplan, OI.flat_pos_of_shard(oplan, 0, idx))
+    cs = [OI.values_at(w, W.KIND_GRAD, MICRO32 + 16 + q, w.grad_std, gen.MODE_F32, pidx)
+          for q in range(P)]
+    assert_bits(gather_dev(g, idx), o_reduce(cs, 0), "fp32-contribution mean (sampled)")
+    prop = 0.0
+    for c in torch.split(g, 1 << 28):
+        prop += float(torch.sum(c.double() * c.double()))
+    got = float(host(part)[0])
+    assert abs(got - prop) <= 1e-12 * prop, (got, prop)
