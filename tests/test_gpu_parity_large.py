@@ -143,13 +143,30 @@ def test_full_size_sampled(cfg, layout, owners):
 MICRO32 = 3000      # generator rank fields: micro-batch k of rank 0, and fp32 contribution q
 
 
+def sampled_accumulation(micro, fp32):
+    """The oracle's accumulation of the micro-batches' values at sampled
+    positions: a one-tensor plan whose elements are the samples (a pad sample
+    carries 0 in every micro-batch, which accumulates to the pad's 0)."""
+    from oracle import pack as opack
+    n = micro[0].size
+    plan1 = make_plan([n], 1 << 40, 1, align=1)
+    if fp32:
+        flat = opack.pack_f32(plan1, [micro[0]])
+        for mk in micro[1:]:
+            flat = opack.accumulate_f32(plan1, flat, [mk])
+    else:
+        flat = opack.pack(plan1, [micro[0]])
+        for mk in micro[1:]:
+            flat = opack.accumulate(plan1, flat, [mk])
+    return flat[:n]
+
+
 def test_fp32_rows_full_size_sampled():
     """The fp32 accumulation buckets and the reduce over fp32 contributions at
     the 7B share's size, in the launch shapes the benchmark times: two
     micro-batches widened and added into rank 0's fp32 buckets (sampled flat
     positions), and the reduce over 8 shard-compact fp32 contributions for
     owner 0 (sampled shard elements; the norm partial by its property)."""
-    from oracle.bf16 import widen
     w = W.by_id(3)
     P = w.world_size
     plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
@@ -169,9 +186,10 @@ def test_fp32_rows_full_size_sampled():
     fpos = np.unique(np.concatenate([rng.integers(0, plan.flat_len, 1 << 18),
                                      [0, plan.flat_len - 1]]))
     pidx = OI.param_index_of_flat(oplan, fpos)
-    g0, g1 = (widen(OI.values_at(w, W.KIND_GRAD, MICRO32 + k, w.grad_std, gen.MODE_BF16, pidx))
-              for k in (0, 1))
-    assert_bits(gather_dev(flat32, fpos), (g0 + g1).astype(np.float32), "fp32 buckets (sampled)")
+    mb = [OI.values_at(w, W.KIND_GRAD, MICRO32 + k, w.grad_std, gen.MODE_BF16, pidx)
+          for k in (0, 1)]
+    assert_bits(gather_dev(flat32, fpos), sampled_accumulation(mb, fp32=True),
+                "fp32 buckets (sampled)")
     del flat32
     torch.cuda.empty_cache()
 
@@ -198,3 +216,52 @@ def test_fp32_rows_full_size_sampled():
         prop += float(torch.sum(c.double() * c.double()))
     got = float(host(part)[0])
     assert abs(got - prop) <= 1e-12 * prop, (got, prop)
+
+
+def test_bf16_rows_full_size_sampled():
+    """The bf16 gradient accumulation and the bf16-wire reduce at the 7B share's
+    size, in the launch shapes the benchmark times: micro-batches 0 and 1 into
+    rank 0's bf16 buckets (sampled flat positions), and the bf16-wire reduce
+    over the 8 ranks' packed buckets for owner 0 (sampled shard elements)."""
+    from oracle.reduce import reduce_mean_bf16_wire
+    w = W.by_id(3)
+    P = w.world_size
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    oplan = make_plan(w.numel, w.bucket_cap_bytes, P)
+    S = plan.shard_len
+
+    say(f"[{w.name}] bf16 buckets: pack micro-batch 0, accumulate micro-batch 1")
+    buf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+    views = [buf[s0:s0 + n] for s0, n in zip(GI.prefix(w.numel), w.numel)]
+    acc = torch.empty(plan.flat_len, dtype=torch.uint16, device="cuda")
+    for k in (0, 1):
+        gen.dev_fill(buf, w.cfg_id, W.KIND_GRAD, MICRO32 + k, 0, w.grad_std, gen.MODE_BF16)
+        (G.bucket_pack if k == 0 else G.bucket_accumulate)(plan, views, acc)
+        torch.cuda.synchronize()
+    rng = np.random.default_rng(34)
+    fpos = np.unique(np.concatenate([rng.integers(0, plan.flat_len, 1 << 18),
+                                     [0, plan.flat_len - 1]]))
+    pidx = OI.param_index_of_flat(oplan, fpos)
+    mb = [OI.values_at(w, W.KIND_GRAD, MICRO32 + k, w.grad_std, gen.MODE_BF16, pidx)
+          for k in (0, 1)]
+    assert_bits(gather_dev(acc, fpos), sampled_accumulation(mb, fp32=False),
+                "bf16 buckets (sampled)")
+    del acc
+
+    say(f"[{w.name}] bf16-wire reduce over {P} ranks' buckets, S={S}")
+    flats = []
+    for q in range(P):
+        _, v2 = GI.rank_grads(w, q, buf)
+        f = torch.empty(plan.flat_len, dtype=torch.uint16, device="cuda")
+        G.bucket_pack(plan, v2, f)
+        flats.append(f)
+    torch.cuda.synchronize()
+    del buf, views
+    g = torch.empty(S, dtype=torch.float32, device="cuda")
+    G.shard_reduce_mean(plan, 0, flats, G.LAYOUT_BUCKET_FLAT, g, bf16_wire=True)
+    torch.cuda.synchronize()
+    del flats
+    idx = sample_indices(oplan, 1 << 20, 300)
+    pidx = OI.param_index_of_flat(oplan, OI.flat_pos_of_shard(oplan, 0, idx))
+    cs = [OI.values_at(w, W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16, pidx) for q in range(P)]
+    assert_bits(gather_dev(g, idx), reduce_mean_bf16_wire(cs, 0), "bf16-wire mean (sampled)")
