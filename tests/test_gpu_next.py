@@ -169,9 +169,14 @@ def test_fp32_reduce_every_rank_count(P):
     numel = [int(x) for x in rng.integers(1, 5000, 9)]
     plan = G.Plan(numel, 6000, P, 8).upload()
     oplan = make_plan(numel, 6000, P, align=8)
-    host_flats = [opack.pack_f32(oplan, [np.asarray(rng.integers(0, 65536, n), np.uint16) & 0xBFFF
-                                         for n in numel]) for _ in range(P)]
-    flats = [torch.from_numpy(f).cuda() for f in host_flats]
+    host_flats, flats = [], []
+    for _ in range(P):
+        grads = [np.asarray(rng.integers(0, 65536, n), np.uint16) & 0xBFFF for n in numel]
+        host_flats.append(opack.pack_f32(oplan, grads))              # oracle side
+        f = torch.empty(plan.flat_len, dtype=torch.float32, device="cuda")
+        G.bucket_pack_f32(plan, [torch.from_numpy(x.view(np.int16)).cuda().view(torch.uint16)
+                                 for x in grads], f)                 # library side
+        flats.append(f)
     ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     part = torch.zeros(1, dtype=torch.float64, device="cuda")
     for r in sorted({0, P // 2, P - 1}):

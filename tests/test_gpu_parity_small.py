@@ -255,9 +255,15 @@ def test_non_finite_values_propagate():
     plan = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size).upload()
     oplan = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
     flats = [OI.rank_flat(oplan, w, q) for q in range(4)]
-    flats[2][100] = 0x7FC0          # NaN
-    flats[1][plan.flat_len - 200000] = 0x7F80   # +inf
-    dev = [torch.from_numpy(f.view(np.int16).copy()).view(torch.uint16).cuda() for f in flats]
+    bad = {2: (100, 0x7FC0), 1: (plan.flat_len - 200000, 0x7F80)}   # a NaN and a +inf
+    dev = []
+    for q in range(4):                       # the GPU side packs with the library's own plan
+        f = torch.empty(plan.flat_len, dtype=torch.uint16, device="cuda")
+        G.bucket_pack(plan, GI.rank_grads_separate(w, q), f)
+        dev.append(f)
+    for q, (pos, bits) in bad.items():       # the same positions poisoned on both sides
+        flats[q][pos] = bits
+        dev[q].view(torch.int16)[pos] = np.int16(np.uint16(bits).view(np.int16))
     out = run_gpu_step(w, plan, dev)
     th, m, v = OI.full_state(oplan, w)
     ref = zero_step_all_owners(oplan, flats, th, m, v, w.hp)
