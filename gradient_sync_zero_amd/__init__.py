@@ -10,12 +10,13 @@ from ._binding import (AdamWHP, GszError, LAYOUT_BUCKET_FLAT, LAYOUT_SHARD_COMPA
                        bucket_accumulate, bucket_accumulate_f32, bucket_pack, bucket_pack_f32,
                        bucket_unpack, clip_coef, load, ledger_bytes_per_param, make_hp,
                        shard_adamw_step, shard_grad_sqnorm, shard_reduce_mean,
-                       shard_reduce_mean_f32, workspace_bytes)
+                       set_grid_limit, shard_reduce_mean_f32, workspace_bytes)
 
 load()
 
 __all__ = ["AdamWHP", "GszError", "LAYOUT_BUCKET_FLAT", "LAYOUT_SHARD_COMPACT", "LIB_PATH",
            "MAX_RANKS", "Plan", "adamw_step", "allgather_layout_write", "allreduce_mean",
            "bucket_accumulate", "bucket_accumulate_f32", "bucket_pack", "bucket_pack_f32",
-           "bucket_unpack", "clip_coef", "ledger_bytes_per_param", "make_hp", "shard_adamw_step",
-           "shard_grad_sqnorm", "shard_reduce_mean", "shard_reduce_mean_f32", "workspace_bytes"]
+           "bucket_unpack", "clip_coef", "ledger_bytes_per_param", "make_hp", "set_grid_limit",
+           "shard_adamw_step", "shard_grad_sqnorm", "shard_reduce_mean", "shard_reduce_mean_f32",
+           "workspace_bytes"]

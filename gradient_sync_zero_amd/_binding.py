@@ -63,6 +63,7 @@ _SIGS = {
     "gsz_plan_upload": [_P],
     "gsz_ledger_bytes_per_param": [_I32, _I32, ctypes.POINTER(ctypes.c_double)],
     "gsz_workspace_bytes": [ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
+    "gsz_set_grid_limit": [ctypes.c_int64],
     "gsz_bucket_pack": [_P, _P, _P, _P],
     "gsz_shard_reduce_mean": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_shard_grad_sqnorm": [_P, _I64, _P, _P, ctypes.c_size_t, _P],
@@ -221,6 +222,12 @@ def workspace_bytes(n):
     out = ctypes.c_size_t()
     _check(load().gsz_workspace_bytes(int(n), ctypes.byref(out)))
     return out.value
+
+
+def set_grid_limit(max_blocks):
+    """Caps the blocks of every later data-sized launch, process-wide (0 restores
+    the built-in caps); blocks then stride over several tiles."""
+    _check(load().gsz_set_grid_limit(int(max_blocks)))
 
 
 def bucket_pack(plan, grads, flat, stream=None):

@@ -32,9 +32,11 @@ constexpr int kBlock = 256;
 constexpr int kPackBlock = 64;
 // AdamW's block size (8 waves of 512 elements): measured faster than 256.
 constexpr int kAdamBlock = 512;
-// Largest grid: grid * block work-items must stay below 2^32 per dispatch.
-// Bigger inputs make blocks stride over the remaining tiles.
-constexpr int64_t kMaxFlatGrid = (int64_t)1 << 23;
+// Work-items of one dispatch stay at or below 2^31 (the dispatch packet's grid
+// size is a 32-bit count).  Grids are capped accordingly; bigger inputs make
+// blocks stride over the remaining tiles.
+constexpr int64_t kMaxWorkItems = (int64_t)1 << 31;
+constexpr int64_t kMaxFlatGrid = kMaxWorkItems / kBlock;          // 2^23 blocks of 256
 // MI355X dispatches block b of a grid to XCD b mod 8.  xcd_remap gives XCD x one
 // contiguous range of logical blocks instead (a bijection on [0, G)): the
 // reduce, which reads P buffers at the same offsets, runs 1.7-1.9% faster that

@@ -50,11 +50,18 @@ int current_device(int* dev_out) {
     return GSZ_OK;
 }
 
-// Blocks of a one-tile-per-block launch over n_tiles tiles.
-int flat_grid(int64_t n_tiles) {
+// Process-wide cap on the blocks of grid-sized launches (0: the built-in caps).
+std::atomic<int64_t> g_grid_limit{0};
+
+// Blocks of a one-tile-per-block launch over n_tiles tiles: at most `builtin`
+// (the dispatch limit for the kernel's block size) and the caller's cap.
+int tile_grid(int64_t n_tiles, int64_t builtin) {
+    const int64_t lim = g_grid_limit.load(std::memory_order_relaxed);
+    const int64_t cap = lim > 0 && lim < builtin ? lim : builtin;
     if (n_tiles < 1) return 1;
-    return (int)(n_tiles < kMaxFlatGrid ? n_tiles : kMaxFlatGrid);
+    return (int)(n_tiles < cap ? n_tiles : cap);
 }
+int flat_grid(int64_t n_tiles) { return tile_grid(n_tiles, kMaxFlatGrid); }
 
 // Partials of the reductions: grid blocks wrote ws[0, grid); sum them in a
 // fixed order into *out (two stages when there are many).
@@ -178,6 +185,15 @@ extern "C" int gsz_plan_destroy(gsz_plan* p) {
     return GSZ_OK;
 }
 
+extern "C" int gsz_set_grid_limit(int64_t max_blocks) {
+    if (max_blocks < 0) {
+        set_error("gsz_set_grid_limit: max_blocks %lld is negative", (long long)max_blocks);
+        return GSZ_ERR_INVALID_ARG;
+    }
+    g_grid_limit.store(max_blocks, std::memory_order_relaxed);
+    return GSZ_OK;
+}
+
 extern "C" int gsz_plan_upload(gsz_plan* p) {
     if (!p) { set_error("gsz_plan_upload: NULL plan"); return GSZ_ERR_INVALID_ARG; }
     int dev = 0;
@@ -242,8 +258,7 @@ int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, void* flat, int mod
         for (int k = 0; k < nk; ++k) pp.p[k] = ptrs[T - 1 - (k0 + k)];
         const int64_t tb = p->pack[3 * k0 + 2], te = p->pack[3 * (k0 + nk) + 2];
         if (te == tb) continue;
-        constexpr int64_t kMaxPackGrid = ((int64_t)1 << 31) / kPackBlock;   // work-items < 2^32
-        const int grid = (int)(te - tb < kMaxPackGrid ? te - tb : kMaxPackGrid);
+        const int grid = tile_grid(te - tb, kMaxWorkItems / kPackBlock);
         uint16_t* f16 = static_cast<uint16_t*>(flat);
         float* f32 = static_cast<float*>(flat);
         if (mode == kPack)
@@ -457,9 +472,8 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
     }
     const AdamScalars s = adam_scalars(*hp);
     const int64_t ntile = (S + 511) / 512;
-    int64_t blocks = (ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64);
-    if (blocks > kMaxFlatGrid) blocks = kMaxFlatGrid;
-    const dim3 grid((unsigned)blocks);
+    const dim3 grid(tile_grid((ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64),
+                              kMaxWorkItems / kAdamBlock));
     const int nseg = (int)p->buckets.size();
     if (gathered && shard_bf16)
         hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, S, gathered, shard_bf16);
@@ -568,9 +582,9 @@ extern "C" int gsz_adamw_step(float* master, float* m, float* v, const float* g,
     }
     const AdamScalars s = adam_scalars(*hp);
     const int64_t ntile = (n + 511) / 512;
-    int64_t blocks = (ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64);
-    if (blocks > kMaxFlatGrid) blocks = kMaxFlatGrid;
-    hipLaunchKernelGGL((k_adamw<false, true>), dim3((unsigned)blocks), dim3(kAdamBlock), 0, stream, master, m, v, g,
+    const int blocks = tile_grid((ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64),
+                                 kMaxWorkItems / kAdamBlock);
+    hipLaunchKernelGGL((k_adamw<false, true>), dim3(blocks), dim3(kAdamBlock), 0, stream, master, m, v, g,
                        coef, s, nullptr, 0, (int64_t)0, n, nullptr, out_bf16);
     return launched(who);
 }

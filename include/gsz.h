@@ -161,6 +161,17 @@ int gsz_ledger_bytes_per_param(int32_t world_size, int32_t zero_stage, double* o
  * GSZ_ERR_INVALID_ARG if n < 0 or out is NULL. */
 int gsz_workspace_bytes(int64_t n, size_t* out);
 
+/* Launch-shape control for tests and tuning (no page defines it).  Caps the
+ * number of blocks of every data-sized launch made after the call, for the
+ * whole process and every thread; 0 restores the built-in caps (2^31
+ * work-items per launch, reached only by inputs of more than about 17e9
+ * elements).  Under a cap each block strides over several tiles: the path that
+ * otherwise runs only on such inputs.  Results are bit-identical to uncapped
+ * launches except the fp64 norm partials, whose summation grouping follows the
+ * grid.  Launches already enqueued keep their grids; workspace sizes do not
+ * change.  GSZ_ERR_INVALID_ARG if max_blocks < 0. */
+int gsz_set_grid_limit(int64_t max_blocks);
+
 /* -------------------------------------------------------------- steps --- */
 
 /* Step 1: flat[base_b + ...] <- gradients of bucket b in bucket order, zero pads.

@@ -136,6 +136,10 @@ def test_argument_validation():
         assert G.workspace_bytes(n) == 8 * (blocks + 1024), n
     with pytest.raises(G.GszError):
         G.workspace_bytes(-1)
+    with pytest.raises(G.GszError) as e:                   # the grid cap is a count of blocks
+        G.set_grid_limit(-1)
+    assert "-1" in str(e.value)
+    G.set_grid_limit(0)
     lib = G.load()
     assert lib.gsz_status_string(-5) == b"plan mismatch"
     assert lib.gsz_plan_destroy(None) == 0
