@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "gsz_device.h"
 #include "gsz_internal.h"
@@ -123,6 +124,21 @@ int check_owner(const gsz_plan* p, int32_t owner, const char* who) {
         return GSZ_ERR_BAD_RANK;
     }
     return GSZ_OK;
+}
+
+// Calls f(std::integral_constant<int, PS>{}) with PS = P for the world sizes that
+// have unrolled kernels and PS = 0 (the runtime-P loop) for every other P.
+template <class F>
+void with_static_p(int P, F&& f) {
+    switch (P) {
+        case 2: f(std::integral_constant<int, 2>{}); break;
+        case 4: f(std::integral_constant<int, 4>{}); break;
+        case 8: f(std::integral_constant<int, 8>{}); break;
+        case 16: f(std::integral_constant<int, 16>{}); break;
+        case 32: f(std::integral_constant<int, 32>{}); break;
+        case 64: f(std::integral_constant<int, 64>{}); break;
+        default: f(std::integral_constant<int, 0>{}); break;
+    }
 }
 
 template <int PS>
@@ -350,16 +366,10 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         const bool flat = layout == GSZ_LAYOUT_BUCKET_FLAT;
         const int nseg = (int)p->buckets.size();
         double* wsd = static_cast<double*>(ws);
-        const dim3 gr(grid);
-        switch (P) {
-            case 2: launch_reduce_f32<2>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
-            case 4: launch_reduce_f32<4>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
-            case 8: launch_reduce_f32<8>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
-            case 16: launch_reduce_f32<16>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
-            case 32: launch_reduce_f32<32>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
-            case 64: launch_reduce_f32<64>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
-            default: launch_reduce_f32<0>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, S, g, wsd); break;
-        }
+        with_static_p(P, [&](auto ps) {
+            launch_reduce_f32<decltype(ps)::value>(norm, flat, dim3(grid), stream, rp, P, invP, pow2,
+                                                   p->d_seg, nseg, owner, S, g, wsd);
+        });
         if ((rc = launched(who))) return rc;
     } else if (S > 0) {
         RankPtrs rp{};
@@ -370,16 +380,10 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         const bool flat = layout == GSZ_LAYOUT_BUCKET_FLAT;
         const int nseg = (int)p->buckets.size();
         double* wsd = static_cast<double*>(ws);
-        const dim3 gr(grid);
-        switch (P) {
-            case 2: launch_reduce<2>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
-            case 4: launch_reduce<4>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
-            case 8: launch_reduce<8>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
-            case 16: launch_reduce<16>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
-            case 32: launch_reduce<32>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
-            case 64: launch_reduce<64>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
-            default: launch_reduce<0>(norm, flat, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, owner, nvec, g, wsd, false, wire16); break;
-        }
+        with_static_p(P, [&](auto ps) {
+            launch_reduce<decltype(ps)::value>(norm, flat, dim3(grid), stream, rp, P, invP, pow2,
+                                               p->d_seg, nseg, owner, nvec, g, wsd, false, wire16);
+        });
         if ((rc = launched(who))) return rc;
     }
     if (partial_out) {
@@ -547,15 +551,10 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
     for (int c = 0; c < P; ++c) {
         RankPtrs rp{};
         for (int k = 0; k < P; ++k) rp.p[k] = contrib[(c + 1 + k) % P];
-        switch (P) {
-            case 2: launch_reduce<2>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
-            case 4: launch_reduce<4>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
-            case 8: launch_reduce<8>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
-            case 16: launch_reduce<16>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
-            case 32: launch_reduce<32>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
-            case 64: launch_reduce<64>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
-            default: launch_reduce<0>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, nseg, c, nvec, g_flat, wsd, true); break;
-        }
+        with_static_p(P, [&](auto ps) {
+            launch_reduce<decltype(ps)::value>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg,
+                                               nseg, c, nvec, g_flat, wsd, true);
+        });
         if ((rc = launched(who))) return rc;
         if (norm) {
             launch_finalize(wsd, grid, partials + c, stream);
