@@ -560,6 +560,26 @@ def main():
     if flat_mode:
         rows.append(("bucket_accumulate",
                      lambda: G.bucket_accumulate(plan, my_grads, flats[r]), 6 * w.n_params))
+    if not flat_mode:
+        # The owner's pack on a window of the model: the trailing tensors that
+        # fill its first 20 buckets (the plan of those tensors alone has the same
+        # buckets).  The whole model's gradients and flat buffer would not fit
+        # beside the P contributions.
+        nb_win = min(20, plan.n_buckets)
+        last = plan.bucket(nb_win - 1)
+        t_min = last["first_tensor"] - last["n_tensors"] + 1
+        wplan = G.Plan(w.numel[t_min:], w.bucket_cap_bytes, P).upload()
+        wn = sum(w.numel[t_min:])
+        wbuf = torch.empty(wn, dtype=torch.uint16, device="cuda")
+        wgrads = list(torch.split(wbuf, w.numel[t_min:]))
+        GI.fill_pieces(wbuf, [(0, sum(w.numel[:t_min]), wn)], w, W.KIND_GRAD, r, w.grad_std,
+                       gen.MODE_BF16)
+        wflat = torch.empty(wplan.flat_len, dtype=torch.uint16, device="cuda")
+        rows.append((f"bucket_pack_window{nb_win}",
+                     lambda: G.bucket_pack(wplan, wgrads, wflat),
+                     4 * wn + 2 * (wplan.flat_len - wn)))
+        log(f"[gpu] pack window: the first {nb_win} buckets, tensors {t_min}..{len(w.numel) - 1}, "
+            f"{wn} params")
     for name, fn, nbytes in rows:
         ms = time_call(fn)
         standalone[name] = dict(ms=ms, bytes=nbytes, GBps=nbytes / (ms * 1e-3) / 1e9,

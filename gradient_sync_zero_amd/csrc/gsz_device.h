@@ -109,21 +109,41 @@ __device__ double block_sum(double x) {
     return s;
 }
 
+// Plan lookup tables (position -> interval) on the device: one 8-byte cell per
+// 2^shift positions holding {lo, hi} (int32 each), the intervals that contain the
+// cell's first and last position.  Kernels take the cells as a __restrict__
+// pointer argument: only then may the compiler read them through the scalar
+// cache (as a plain pointer they became vector loads and cost 7% of the pack's
+// rate).
+// The interval k in [lo_min, hi_max] that holds position x: the largest k with
+// starts[k * stride] <= x, starts non-decreasing.  One 8-byte load of the cell;
+// a binary search only over the intervals that start inside it (none for most
+// cells).  The bounds narrow the search to a subset known to hold the answer.
+// Host-callable so that a CPU test runs this very code against brute force.
+__host__ __device__ __forceinline__ int lut_find(const uint64_t* __restrict__ cells, int shift,
+                                                 const int64_t* __restrict__ starts, int stride,
+                                                 int64_t x, int lo_min, int hi_max) {
+    const uint64_t c = cells[x >> shift];
+    int lo = (int)(uint32_t)c, hi = (int)(uint32_t)(c >> 32);
+    lo = lo > lo_min ? lo : lo_min;
+    hi = hi < hi_max ? hi : hi_max;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (starts[(int64_t)mid * stride] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
 // Walks the bucket segments of a shard in increasing order.  seg rows are
-// {shard_off, base, chunk}; row nseg is {S, 0, 0}.  For shard index i in bucket
-// b, the all-gather / flat position is i + delta with
+// {shard_off, base, chunk}, one per bucket, then {S, 0, 0}.  For shard index i
+// in bucket b, the all-gather / flat position is i + delta with
 // delta = base_b + owner*C_b - shard_off_b.
 struct SegCursor {
     const int64_t* seg;
     int64_t owner, end, delta;
     int b;
-    __device__ void seek(int64_t i, int nseg) {
-        int lo = 0, hi = nseg - 1;          // largest b with shard_off[b] <= i
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (seg[3 * mid] <= i) lo = mid; else hi = mid - 1;
-        }
-        b = lo;
+    __device__ void seek(int64_t i, const uint64_t* __restrict__ lut, int shift) {   // i < S
+        b = lut_find(lut, shift, seg, 3, i, 0, 0x7fffffff);   // the bucket that holds i
         load();
     }
     __device__ void load() {

@@ -33,6 +33,21 @@ struct Bucket {
     int64_t base, n, padded, chunk, shard_off;
 };
 
+// Position -> interval lookup tables, in place of a binary search over every
+// interval in the kernels.  The intervals (the pack's tensors by first tile, the
+// shard's buckets by shard offset) have non-decreasing starts; positions
+// [0, total) are cut into at most 2^kLutCellsLog2 cells of 2^shift positions,
+// and cell j holds {lo, hi}: the intervals that contain its first and its last
+// position.  A kernel reads the cell of its position; lo == hi is the answer,
+// otherwise a search over [lo, hi] (the few intervals that start inside the cell).
+constexpr int kLutCellsLog2 = 16;
+struct Lut {
+    int shift = 0;
+    std::vector<int32_t> cells;      // 2 per cell: lo, hi
+};
+// starts(k) = tab[k * stride + offset] for k in [0, n); starts(0) == 0.
+Lut build_lut(const std::vector<int64_t>& tab, int stride, int offset, int64_t n, int64_t total);
+
 void set_error(const char* fmt, ...);
 
 }  // namespace gsz
@@ -55,6 +70,9 @@ struct gsz_plan {
     std::vector<int64_t> pack;
     // pads: per padded bucket {start, length}.
     std::vector<int64_t> pads;
+    // Lookup tables: shard index -> bucket (over seg), tile -> bucket-order tensor
+    // position (over pack).
+    gsz::Lut seg_lut, pack_lut;
 
     // Device tables (one allocation) and the device they live on.
     std::mutex mu;
@@ -63,4 +81,6 @@ struct gsz_plan {
     const int64_t* d_seg = nullptr;
     const int64_t* d_pack = nullptr;
     const int64_t* d_pads = nullptr;
+    const uint64_t* d_seg_lut = nullptr;     // {lo, hi} int32 pairs, one per cell
+    const uint64_t* d_pack_lut = nullptr;
 };

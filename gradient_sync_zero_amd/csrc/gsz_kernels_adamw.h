@@ -33,7 +33,8 @@ template <bool GATH, bool SHARD>
 __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master, float* __restrict__ m,
                                                       float* __restrict__ v, const float* __restrict__ g,
                                                       const float* __restrict__ coefp, AdamScalars s,
-                                                      const int64_t* __restrict__ seg, int nseg,
+                                                      const int64_t* __restrict__ seg,
+                                                      const uint64_t* __restrict__ slut, int sshift,
                                                       int64_t owner, int64_t S,
                                                       uint16_t* __restrict__ gathered,
                                                       uint16_t* __restrict__ shard_bf16) {
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master
     const int64_t ntile = (S + 511) / 512;
     const float coef = *coefp;
     SegCursor cur{seg, owner, 0, 0, 0};
-    if (GATH && wv < ntile) cur.seek(wv * 512, nseg);        // wave-uniform: scalar loads
+    if (GATH && wv < ntile) cur.seek(wv * 512, slut, sshift);        // wave-uniform: scalar loads
     for (; wv < ntile; wv += nwaves) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -72,13 +73,14 @@ __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master
 
 // gathered[i + delta_b] = shard[i] for shard index i of bucket b.
 __global__ __launch_bounds__(kBlock) void k_ag_write(const uint16_t* __restrict__ shard,
-                                                     const int64_t* __restrict__ seg, int nseg,
+                                                     const int64_t* __restrict__ seg,
+                                                     const uint64_t* __restrict__ slut, int sshift,
                                                      int64_t owner, int64_t nvec,
                                                      uint16_t* __restrict__ gathered) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     SegCursor cur{seg, owner, 0, 0, 0};
-    if (v < nvec) cur.seek((int64_t)blockIdx.x * kBlock * 8, nseg);   // the block's first element
+    if (v < nvec) cur.seek((int64_t)blockIdx.x * kBlock * 8, slut, sshift);   // the block's first element
     for (; v < nvec; v += stride) {
         const int64_t i = v * 8;
         st16(gathered + cur.map(i), ld16(shard + i));

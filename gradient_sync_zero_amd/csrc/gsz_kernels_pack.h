@@ -28,23 +28,22 @@ __device__ __forceinline__ uint16_t add_bf16(uint16_t a, uint16_t b) {
 
 // Moves the tensors of one batch (bucket-order positions [k0, k0+nk)) to or
 // from the flat buffer as MODE says.  tab rows: {flat offset, numel, first
-// tile}.  One block per tile of kPackTile = 8 * kPackBlock elements (one
-// 16-byte vector per lane), the grid covering the batch's tiles [t_begin, t_end): short
-// blocks dispatched in address order keep the lines in flight close together,
-// which MI355X's HBM rewards over long-running grid-stride blocks.  Grids are
-// capped below the dispatch limit; blocks then stride over the remaining tiles.
+// tile}; lut maps a tile to its tensor in one load (a binary search over 256
+// tensors, eight dependent loads before a block's first data load, cost 7% of
+// the copy rate on a 7B model).  One block per tile of kPackTile = 8 *
+// kPackBlock elements (one 16-byte vector per lane), the grid covering the
+// batch's tiles [t_begin, t_end): short blocks dispatched in address order keep
+// the lines in flight close together, which MI355X's HBM rewards over
+// long-running grid-stride blocks.  Grids are capped below the dispatch limit;
+// blocks then stride over the remaining tiles.
 template <int MODE>
 __global__ __launch_bounds__(kPackBlock) void k_pack(PackPtrs pp, const int64_t* __restrict__ tab,
+                                                 const uint64_t* __restrict__ tlut, int tshift,
                                                  int k0, int nk, int64_t t_begin, int64_t t_end,
                                                  uint16_t* __restrict__ flat) {
     const int tid = threadIdx.x;
     for (int64_t tile = t_begin + blockIdx.x; tile < t_end; tile += gridDim.x) {
-        int lo = k0, hi = k0 + nk - 1;          // largest k with first_tile[k] <= tile
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (tab[3 * mid + 2] <= tile) lo = mid; else hi = mid - 1;
-        }
-        const int k = lo;
+        const int k = lut_find(tlut, tshift, tab + 2, 3, tile, k0, k0 + nk - 1);   // block-uniform
         const int64_t n = tab[3 * k + 1];
         const int64_t j0 = (tile - tab[3 * k + 2]) * gsz::kPackTile;
         const int64_t j1 = j0 + gsz::kPackTile < n ? j0 + gsz::kPackTile : n;
@@ -92,16 +91,12 @@ __device__ __forceinline__ void stf8(float* p, const float a[8]) {
 }
 template <bool ACC>
 __global__ __launch_bounds__(kPackBlock) void k_pack_f32(PackPtrs pp, const int64_t* __restrict__ tab,
+                                                     const uint64_t* __restrict__ tlut, int tshift,
                                                      int k0, int nk, int64_t t_begin, int64_t t_end,
                                                      float* __restrict__ flat) {
     const int tid = threadIdx.x;
     for (int64_t tile = t_begin + blockIdx.x; tile < t_end; tile += gridDim.x) {
-        int lo = k0, hi = k0 + nk - 1;          // largest k with first_tile[k] <= tile
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (tab[3 * mid + 2] <= tile) lo = mid; else hi = mid - 1;
-        }
-        const int k = lo;
+        const int k = lut_find(tlut, tshift, tab + 2, 3, tile, k0, k0 + nk - 1);   // block-uniform
         const int64_t n = tab[3 * k + 1];
         const int64_t j0 = (tile - tab[3 * k + 2]) * gsz::kPackTile;
         const int64_t j1 = j0 + gsz::kPackTile < n ? j0 + gsz::kPackTile : n;

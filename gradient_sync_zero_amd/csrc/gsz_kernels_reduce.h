@@ -22,7 +22,8 @@ namespace {
 // wire carries bf16 partial sums); the final division stays fp32.
 template <int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
-                                                        const int64_t* __restrict__ seg, int nseg,
+                                                        const int64_t* __restrict__ seg,
+                                                        const uint64_t* __restrict__ slut, int sshift,
                                                         int64_t owner, int64_t nvec,
                                                         float* __restrict__ g,
                                                         double* __restrict__ ws) {
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
     int64_t v = bx * kBlock + threadIdx.x;
     double sq = 0.0;
     SegCursor cur{seg, owner, 0, 0, 0};
-    if (FLAT && v < nvec) cur.seek(bx * kRedTile, nseg);      // uniform: scalar loads
+    if (FLAT && v < nvec) cur.seek(bx * kRedTile, slut, sshift);      // uniform: scalar loads
     const float fP = (float)P;
     for (; v < nvec; v += stride) {
         const int64_t i = v * 8;
@@ -95,7 +96,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
 // partials as k_reduce_mean.
 template <int PS, bool NORM, bool FLAT>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P, float invP, int pow2,
-                                                            const int64_t* __restrict__ seg, int nseg,
+                                                            const int64_t* __restrict__ seg,
+                                                            const uint64_t* __restrict__ slut, int sshift,
                                                             int64_t owner, int64_t S,
                                                             float* __restrict__ g,
                                                             double* __restrict__ ws) {
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P,
     double sq = 0.0;
     SegCursor cur{seg, owner, 0, 0, 0};
     int64_t t = bx * kRedTile;
-    if (FLAT && t < S) cur.seek(t, nseg);                     // uniform: scalar loads
+    if (FLAT && t < S) cur.seek(t, slut, sshift);                     // uniform: scalar loads
     const float fP = (float)P;
     for (; t < S; t += (int64_t)gridDim.x * kRedTile) {
         const int64_t i0 = t + 512 * wave + 4 * lane, i1 = i0 + 256;

@@ -143,45 +143,45 @@ void with_static_p(int P, F&& f) {
 
 template <int PS>
 void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPtrs& rp, int P,
-                   float invP, int pow2, const int64_t* seg, int nseg, int64_t owner, int64_t nvec,
+                   float invP, int pow2, const int64_t* seg, const uint64_t* slut, int sshift, int64_t owner, int64_t nvec,
                    float* g, double* ws, bool outflat = false, bool wire16 = false) {
     if (wire16) {
         if (norm && flat)
-            hipLaunchKernelGGL((k_reduce_mean<PS, true, true, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+            hipLaunchKernelGGL((k_reduce_mean<PS, true, true, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
         else if (norm)
-            hipLaunchKernelGGL((k_reduce_mean<PS, true, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+            hipLaunchKernelGGL((k_reduce_mean<PS, true, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
         else if (flat)
-            hipLaunchKernelGGL((k_reduce_mean<PS, false, true, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+            hipLaunchKernelGGL((k_reduce_mean<PS, false, true, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
         else
-            hipLaunchKernelGGL((k_reduce_mean<PS, false, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+            hipLaunchKernelGGL((k_reduce_mean<PS, false, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
         return;
     }
     if (outflat && norm)
-        hipLaunchKernelGGL((k_reduce_mean<PS, true, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean<PS, true, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
     else if (outflat)
-        hipLaunchKernelGGL((k_reduce_mean<PS, false, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean<PS, false, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
     else if (norm && flat)
-        hipLaunchKernelGGL((k_reduce_mean<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
     else if (norm)
-        hipLaunchKernelGGL((k_reduce_mean<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
     else if (flat)
-        hipLaunchKernelGGL((k_reduce_mean<PS, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean<PS, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
     else
-        hipLaunchKernelGGL((k_reduce_mean<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, nvec, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
 }
 
 template <int PS>
 void launch_reduce_f32(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPtrsF& rp, int P,
-                       float invP, int pow2, const int64_t* seg, int nseg, int64_t owner, int64_t S,
+                       float invP, int pow2, const int64_t* seg, const uint64_t* slut, int sshift, int64_t owner, int64_t S,
                        float* g, double* ws) {
     if (norm && flat)
-        hipLaunchKernelGGL((k_reduce_mean_f32<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, S, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean_f32<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g, ws);
     else if (norm)
-        hipLaunchKernelGGL((k_reduce_mean_f32<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, S, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean_f32<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g, ws);
     else if (flat)
-        hipLaunchKernelGGL((k_reduce_mean_f32<PS, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, S, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean_f32<PS, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g, ws);
     else
-        hipLaunchKernelGGL((k_reduce_mean_f32<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, nseg, owner, S, g, ws);
+        hipLaunchKernelGGL((k_reduce_mean_f32<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g, ws);
 }
 
 }  // namespace
@@ -225,24 +225,31 @@ extern "C" int gsz_plan_upload(gsz_plan* p) {
         p->dev_mem = nullptr;
         p->device = -1;
     }
+    // One allocation: seg, pack and pads rows (int64), then the two lookup tables
+    // (a {lo, hi} pair of int32 per cell, one 8-byte slot each), then 2 spare slots.
     const size_t n_seg = p->seg.size(), n_pack = p->pack.size(), n_pads = p->pads.size();
-    const size_t bytes = (n_seg + n_pack + n_pads + 2) * sizeof(int64_t);
-    void* mem = nullptr;
-    hipError_t e = hipMalloc(&mem, bytes);
-    if (e != hipSuccess) return hip_fail("gsz_plan_upload: hipMalloc", e);
-    int64_t* d = static_cast<int64_t*>(mem);
+    const size_t n_slut = p->seg_lut.cells.size() / 2, n_plut = p->pack_lut.cells.size() / 2;
+    const size_t slots = n_seg + n_pack + n_pads + n_slut + n_plut + 2;
     std::vector<int64_t> img;
-    img.reserve(n_seg + n_pack + n_pads + 2);
+    img.reserve(slots);
     img.insert(img.end(), p->seg.begin(), p->seg.end());
     img.insert(img.end(), p->pack.begin(), p->pack.end());
     img.insert(img.end(), p->pads.begin(), p->pads.end());
-    img.resize(img.size() + 2, 0);
-    e = hipMemcpy(mem, img.data(), img.size() * sizeof(int64_t), hipMemcpyHostToDevice);
+    img.resize(slots, 0);
+    std::memcpy(img.data() + n_seg + n_pack + n_pads, p->seg_lut.cells.data(), n_slut * 8);
+    std::memcpy(img.data() + n_seg + n_pack + n_pads + n_slut, p->pack_lut.cells.data(), n_plut * 8);
+    void* mem = nullptr;
+    hipError_t e = hipMalloc(&mem, slots * sizeof(int64_t));
+    if (e != hipSuccess) return hip_fail("gsz_plan_upload: hipMalloc", e);
+    int64_t* d = static_cast<int64_t*>(mem);
+    e = hipMemcpy(mem, img.data(), slots * sizeof(int64_t), hipMemcpyHostToDevice);
     if (e != hipSuccess) { (void)hipFree(mem); return hip_fail("gsz_plan_upload: hipMemcpy", e); }
     p->dev_mem = mem;
     p->device = dev;
     p->d_seg = d;
     p->d_pack = d + n_seg;
+    p->d_seg_lut = reinterpret_cast<const uint64_t*>(d + n_seg + n_pack + n_pads);
+    p->d_pack_lut = reinterpret_cast<const uint64_t*>(d + n_seg + n_pack + n_pads + n_slut);
     p->d_pads = d + n_seg + n_pack;
     return GSZ_OK;
 }
@@ -278,15 +285,15 @@ int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, void* flat, int mod
         uint16_t* f16 = static_cast<uint16_t*>(flat);
         float* f32 = static_cast<float*>(flat);
         if (mode == kPack)
-            hipLaunchKernelGGL(k_pack<kPack>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f16);
+            hipLaunchKernelGGL(k_pack<kPack>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f16);
         else if (mode == kUnpack)
-            hipLaunchKernelGGL(k_pack<kUnpack>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f16);
+            hipLaunchKernelGGL(k_pack<kUnpack>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f16);
         else if (mode == kAccumulate)
-            hipLaunchKernelGGL(k_pack<kAccumulate>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f16);
+            hipLaunchKernelGGL(k_pack<kAccumulate>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f16);
         else if (mode == kPackF32)
-            hipLaunchKernelGGL(k_pack_f32<false>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f32);
+            hipLaunchKernelGGL(k_pack_f32<false>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f32);
         else
-            hipLaunchKernelGGL(k_pack_f32<true>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, k0, nk, tb, te, f32);
+            hipLaunchKernelGGL(k_pack_f32<true>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f32);
         if ((rc = launched(who))) return rc;
     }
     const int npad = (int)(p->pads.size() / 2);
@@ -364,11 +371,12 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         const float invP = pow2 ? 1.0f / (float)P : 0.0f;
         const bool norm = partial_out != nullptr;
         const bool flat = layout == GSZ_LAYOUT_BUCKET_FLAT;
-        const int nseg = (int)p->buckets.size();
+        const uint64_t* slut = p->d_seg_lut;
+        const int sshift = p->seg_lut.shift;
         double* wsd = static_cast<double*>(ws);
         with_static_p(P, [&](auto ps) {
             launch_reduce_f32<decltype(ps)::value>(norm, flat, dim3(grid), stream, rp, P, invP, pow2,
-                                                   p->d_seg, nseg, owner, S, g, wsd);
+                                                   p->d_seg, slut, sshift, owner, S, g, wsd);
         });
         if ((rc = launched(who))) return rc;
     } else if (S > 0) {
@@ -378,11 +386,12 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         const float invP = pow2 ? 1.0f / (float)P : 0.0f;
         const bool norm = partial_out != nullptr;
         const bool flat = layout == GSZ_LAYOUT_BUCKET_FLAT;
-        const int nseg = (int)p->buckets.size();
+        const uint64_t* slut = p->d_seg_lut;
+        const int sshift = p->seg_lut.shift;
         double* wsd = static_cast<double*>(ws);
         with_static_p(P, [&](auto ps) {
             launch_reduce<decltype(ps)::value>(norm, flat, dim3(grid), stream, rp, P, invP, pow2,
-                                               p->d_seg, nseg, owner, nvec, g, wsd, false, wire16);
+                                               p->d_seg, slut, sshift, owner, nvec, g, wsd, false, wire16);
         });
         if ((rc = launched(who))) return rc;
     }
@@ -478,13 +487,14 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
     const int64_t ntile = (S + 511) / 512;
     const dim3 grid(tile_grid((ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64),
                               kMaxWorkItems / kAdamBlock));
-    const int nseg = (int)p->buckets.size();
+    const uint64_t* slut = p->d_seg_lut;
+    const int sshift = p->seg_lut.shift;
     if (gathered && shard_bf16)
-        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
     else if (gathered)
-        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
     else
-        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, nseg, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
     return launched(who);
 }
 
@@ -501,7 +511,8 @@ extern "C" int gsz_allgather_layout_write(const gsz_plan* p, int32_t owner,
     if (misaligned(shard_bf16) || misaligned(gathered)) { set_error("%s: misaligned buffer", who); return GSZ_ERR_MISALIGNED; }
     const int64_t nvec = S / 8;
     hipLaunchKernelGGL(k_ag_write, dim3(flat_grid((nvec + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream, shard_bf16,
-                       p->d_seg, (int)p->buckets.size(), (int64_t)owner, nvec, gathered);
+                       p->d_seg, p->d_seg_lut, p->seg_lut.shift, (int64_t)owner, nvec,
+                       gathered);
     return launched(who);
 }
 
@@ -543,7 +554,8 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
     const dim3 gr(grid);
     const int pow2 = (P & (P - 1)) == 0;
     const float invP = pow2 ? 1.0f / (float)P : 0.0f;
-    const int nseg = (int)p->buckets.size();
+    const uint64_t* slut = p->d_seg_lut;
+    const int sshift = p->seg_lut.shift;
     const bool norm = partials != nullptr;
     double* wsd = static_cast<double*>(ws);
     // chunk c of every bucket, summed in ring order ending at rank c; its norm
@@ -553,7 +565,7 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
         for (int k = 0; k < P; ++k) rp.p[k] = contrib[(c + 1 + k) % P];
         with_static_p(P, [&](auto ps) {
             launch_reduce<decltype(ps)::value>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg,
-                                               nseg, c, nvec, g_flat, wsd, true);
+                                               slut, sshift, c, nvec, g_flat, wsd, true);
         });
         if ((rc = launched(who))) return rc;
         if (norm) {
@@ -584,6 +596,6 @@ extern "C" int gsz_adamw_step(float* master, float* m, float* v, const float* g,
     const int blocks = tile_grid((ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64),
                                  kMaxWorkItems / kAdamBlock);
     hipLaunchKernelGGL((k_adamw<false, true>), dim3(blocks), dim3(kAdamBlock), 0, stream, master, m, v, g,
-                       coef, s, nullptr, 0, (int64_t)0, n, nullptr, out_bf16);
+                       coef, s, nullptr, nullptr, 0, (int64_t)0, n, nullptr, out_bf16);
     return launched(who);
 }

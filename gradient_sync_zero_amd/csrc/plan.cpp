@@ -7,6 +7,7 @@
 // the cap; each bucket is zero-padded to a multiple of P*align so it splits
 // into P equal chunks ("Data Parallelism: From Parameter Server to Ring
 // All-Reduce" §5: N chunks of size M/N); rank r owns chunk r of every bucket.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -44,6 +45,27 @@ struct Fnv {
 };
 
 }  // namespace
+
+Lut build_lut(const std::vector<int64_t>& tab, int stride, int offset, int64_t n, int64_t total) {
+    Lut lut;
+    if (n <= 0 || total <= 0) return lut;
+    while (((total - 1) >> lut.shift) + 1 > ((int64_t)1 << kLutCellsLog2)) ++lut.shift;
+    const int64_t cells = ((total - 1) >> lut.shift) + 1;
+    lut.cells.resize(2 * (size_t)cells);
+    auto start = [&](int64_t k) { return tab[(size_t)(k * stride + offset)]; };
+    int64_t lo = 0;   // largest k with start(k) <= x; both walks only move forward
+    for (int64_t j = 0; j < cells; ++j) {
+        const int64_t x = j << lut.shift;
+        const int64_t y = std::min(x + ((int64_t)1 << lut.shift), total) - 1;
+        while (lo + 1 < n && start(lo + 1) <= x) ++lo;
+        int64_t hi = lo;
+        while (hi + 1 < n && start(hi + 1) <= y) ++hi;
+        lut.cells[2 * (size_t)j] = (int32_t)lo;
+        lut.cells[2 * (size_t)j + 1] = (int32_t)hi;
+    }
+    return lut;
+}
+
 }  // namespace gsz
 
 using gsz::set_error;
@@ -139,6 +161,9 @@ extern "C" int gsz_plan_create(const int64_t* numel, int32_t n_tensors, int64_t 
 
         for (const auto& bk : p->buckets)
             if (bk.padded > bk.n) { p->pads.push_back(bk.base + bk.n); p->pads.push_back(bk.padded - bk.n); }
+
+        p->seg_lut = gsz::build_lut(p->seg, 3, 0, (int64_t)B, p->shard_len);
+        p->pack_lut = gsz::build_lut(p->pack, 3, 2, n_tensors, tiles);
     } catch (const std::bad_alloc&) {
         delete p;
         set_error("gsz_plan_create: out of host memory");
