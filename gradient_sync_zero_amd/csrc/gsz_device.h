@@ -30,8 +30,11 @@ constexpr int kBlock = 256;
 // The pack kernels' block: one wave per 1 KiB tile copied 2.7% faster than
 // 256-lane blocks on 2 KiB tiles (7B share, MI355X).
 constexpr int kPackBlock = 64;
-// AdamW's block size (8 waves of 512 elements): measured faster than 256.
-constexpr int kAdamBlock = 512;
+// AdamW: one wave per block and one tile of 256 elements (4 per lane) per
+// block, with nontemporal hints on every access: 6% (7B share) to 10% (70B
+// share) faster than 512-lane blocks of 512 elements per wave without them.
+constexpr int kAdamBlock = 64;
+constexpr int64_t kAdamTile = 4 * kAdamBlock;
 // Work-items of one dispatch stay at or below 2^31 (the dispatch packet's grid
 // size is a 32-bit count).  Grids are capped accordingly; bigger inputs make
 // blocks stride over the remaining tiles.
@@ -72,6 +75,21 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Nontemporal forms, for bytes a kernel touches once: with the hint on both
+// its loads and its stores a streaming kernel moves 2-10% more bytes per second
+// on MI355X (the hint on one side alone changes little).
+__device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ f32x4 ldf4_nt(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void stf4_nt(float* p, f32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void st8_nt(uint16_t* p, u32x2 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
 __device__ __forceinline__ f32x4 ldf4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void stf4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 

@@ -23,12 +23,12 @@ __device__ __forceinline__ void adamw1(float& th, float& mm, float& vv, float gg
     vv = v1;
 }
 
-// A wave owns 512 consecutive shard elements per iteration, as two groups of
-// 256; lane l updates elements 4l..4l+3 of each group, so every 16-byte load
-// and store instruction of the wave covers 1 KiB of whole 128-byte lines (a
-// lane that loads 32 contiguous bytes as two 16-byte halves makes each
-// instruction touch half of every line, and half-line misses to the same line
-// are fetched twice).  The bf16 result goes out as 8 bytes per lane.
+// One block (one wave) updates kAdamTile = 256 consecutive shard elements per
+// iteration; lane l takes elements 4l..4l+3, so every 16-byte load and store
+// instruction covers 1 KiB of whole 128-byte lines (a lane that loads 32
+// contiguous bytes as two 16-byte halves makes each instruction touch half of
+// every line, and half-line misses to the same line are fetched twice).  Every
+// access is nontemporal.  The bf16 result goes out as 8 bytes per lane.
 template <bool GATH, bool SHARD>
 __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master, float* __restrict__ m,
                                                       float* __restrict__ v, const float* __restrict__ g,
@@ -38,35 +38,31 @@ __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master
                                                       int64_t owner, int64_t S,
                                                       uint16_t* __restrict__ gathered,
                                                       uint16_t* __restrict__ shard_bf16) {
-    constexpr int kWaves = kAdamBlock / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t nwaves = (int64_t)gridDim.x * kWaves;
-    int64_t wv = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t ntile = (S + 511) / 512;
+    static_assert(kAdamBlock == 64 && kAdamTile == 4 * kAdamBlock, "one wave, 4 elements per lane");
+    const int lane = threadIdx.x;
+    const int64_t ntile = (S + kAdamTile - 1) / kAdamTile;
     const float coef = *coefp;
+    int64_t t = blockIdx.x;
     SegCursor cur{seg, owner, 0, 0, 0};
-    if (GATH && wv < ntile) cur.seek(wv * 512, slut, sshift);        // wave-uniform: scalar loads
-    for (; wv < ntile; wv += nwaves) {
+    if (GATH && t < ntile) cur.seek(t * kAdamTile, slut, sshift);   // block-uniform: scalar loads
+    for (; t < ntile; t += gridDim.x) {
+        const int64_t i = t * kAdamTile + 4 * lane;
+        if (i < S) {                           // S and i are multiples of 4
+            const f32x4 g4 = ldf4_nt(g + i);
+            const f32x4 t4 = ldf4_nt(master + i), m4 = ldf4_nt(m + i), v4 = ldf4_nt(v + i);
+            float th[4] = {t4.x, t4.y, t4.z, t4.w};
+            float mm[4] = {m4.x, m4.y, m4.z, m4.w};
+            float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+            const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t i = wv * 512 + h * 256 + 4 * lane;
-            if (i < S) {                       // S and i are multiples of 4
-                const f32x4 g4 = ldf4(g + i);
-                const f32x4 t4 = ldf4(master + i), m4 = ldf4(m + i), v4 = ldf4(v + i);
-                float th[4] = {t4.x, t4.y, t4.z, t4.w};
-                float mm[4] = {m4.x, m4.y, m4.z, m4.w};
-                float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-                const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) adamw1(th[j], mm[j], vv[j], gg[j], coef, s);
-                stf4(master + i, f32x4{th[0], th[1], th[2], th[3]});
-                stf4(m + i, f32x4{mm[0], mm[1], mm[2], mm[3]});
-                stf4(v + i, f32x4{vv[0], vv[1], vv[2], vv[3]});
-                const u32x2 p = u32x2{bf16_rne(th[0]) | (bf16_rne(th[1]) << 16),
-                                      bf16_rne(th[2]) | (bf16_rne(th[3]) << 16)};
-                if (GATH) *reinterpret_cast<u32x2*>(gathered + cur.map(i)) = p;
-                if (SHARD) *reinterpret_cast<u32x2*>(shard_bf16 + i) = p;
-            }
+            for (int j = 0; j < 4; ++j) adamw1(th[j], mm[j], vv[j], gg[j], coef, s);
+            stf4_nt(master + i, f32x4{th[0], th[1], th[2], th[3]});
+            stf4_nt(m + i, f32x4{mm[0], mm[1], mm[2], mm[3]});
+            stf4_nt(v + i, f32x4{vv[0], vv[1], vv[2], vv[3]});
+            const u32x2 p = u32x2{bf16_rne(th[0]) | (bf16_rne(th[1]) << 16),
+                                  bf16_rne(th[2]) | (bf16_rne(th[3]) << 16)};
+            if (GATH) st8_nt(gathered + cur.map(i), p);
+            if (SHARD) st8_nt(shard_bf16 + i, p);
         }
     }
 }

@@ -19,7 +19,8 @@ namespace {
 // OUTFLAT (bucket-flat input only) g is indexed by flat position instead of
 // shard index: P launches, one per chunk owner, give the all-reduce result.
 // W16: the partial sum is rounded to bf16 after every addition (a ring whose
-// wire carries bf16 partial sums); the final division stays fp32.
+// wire carries bf16 partial sums); the final division stays fp32.  Loads and
+// stores are nontemporal (2% faster at P = 8, 5% at P = 64 than plain ones).
 template <int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
                                                         const int64_t* __restrict__ seg,
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
             for (int k0 = 0; k0 < PS; k0 += G) {
                 u32x4 w[G];
 #pragma unroll
-                for (int j = 0; j < G; ++j) w[j] = ld16(rp.p[k0 + j] + off);
+                for (int j = 0; j < G; ++j) w[j] = ld16_nt(rp.p[k0 + j] + off);
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
                     if (k0 + j == 0) widen8(w[j], a);
@@ -53,16 +54,16 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
                 }
             }
         } else {
-            widen8(ld16(rp.p[0] + off), a);
+            widen8(ld16_nt(rp.p[0] + off), a);
             int k = 1;
             for (; k + 8 <= P; k += 8) {
                 u32x4 w[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) w[j] = ld16(rp.p[k + j] + off);
+                for (int j = 0; j < 8; ++j) w[j] = ld16_nt(rp.p[k + j] + off);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) { add8(w[j], a); if (W16) round8_bf16(a); }
             }
-            for (; k < P; ++k) { add8(ld16(rp.p[k] + off), a); if (W16) round8_bf16(a); }
+            for (; k < P; ++k) { add8(ld16_nt(rp.p[k] + off), a); if (W16) round8_bf16(a); }
         }
         if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
 #pragma unroll
@@ -72,8 +73,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
             for (int j = 0; j < 8; ++j) a[j] = a[j] / fP;
         }
         const int64_t o = OUTFLAT ? off : i;    // all-reduce output: the flat position
-        stf4(g + o, f32x4{a[0], a[1], a[2], a[3]});
-        stf4(g + o + 4, f32x4{a[4], a[5], a[6], a[7]});
+        stf4_nt(g + o, f32x4{a[0], a[1], a[2], a[3]});
+        stf4_nt(g + o + 4, f32x4{a[4], a[5], a[6], a[7]});
         if (NORM) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
 // taken as they are.  A wave owns 512 shard elements of its block's tile as two
 // groups of 256; lane l handles elements 4l..4l+3 of each, so every 16-byte
 // load and store of a wave covers whole lines.  Blocks, XCD order and norm
-// partials as k_reduce_mean.
+// partials as k_reduce_mean; nontemporal loads and stores as there.
 template <int PS, bool NORM, bool FLAT>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P, float invP, int pow2,
                                                             const int64_t* __restrict__ seg,
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P,
                 f32x4 w0[G], w1[G];
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
-                    w0[j] = ok0 ? ldf4(rp.p[k0 + j] + off0) : zero;
-                    w1[j] = ok1 ? ldf4(rp.p[k0 + j] + off1) : zero;
+                    w0[j] = ok0 ? ldf4_nt(rp.p[k0 + j] + off0) : zero;
+                    w1[j] = ok1 ? ldf4_nt(rp.p[k0 + j] + off1) : zero;
                 }
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
@@ -135,11 +136,11 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P,
                 }
             }
         } else {
-            a = ok0 ? ldf4(rp.p[0] + off0) : zero;
-            b = ok1 ? ldf4(rp.p[0] + off1) : zero;
+            a = ok0 ? ldf4_nt(rp.p[0] + off0) : zero;
+            b = ok1 ? ldf4_nt(rp.p[0] + off1) : zero;
             for (int k = 1; k < P; ++k) {
-                const f32x4 w0 = ok0 ? ldf4(rp.p[k] + off0) : zero;
-                const f32x4 w1 = ok1 ? ldf4(rp.p[k] + off1) : zero;
+                const f32x4 w0 = ok0 ? ldf4_nt(rp.p[k] + off0) : zero;
+                const f32x4 w1 = ok1 ? ldf4_nt(rp.p[k] + off1) : zero;
                 a.x = a.x + w0.x; a.y = a.y + w0.y; a.z = a.z + w0.z; a.w = a.w + w0.w;
                 b.x = b.x + w1.x; b.y = b.y + w1.y; b.z = b.z + w1.z; b.w = b.w + w1.w;
             }
@@ -151,8 +152,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P,
             a = f32x4{a.x / fP, a.y / fP, a.z / fP, a.w / fP};
             b = f32x4{b.x / fP, b.y / fP, b.z / fP, b.w / fP};
         }
-        if (ok0) stf4(g + i0, a);
-        if (ok1) stf4(g + i1, b);
+        if (ok0) stf4_nt(g + i0, a);
+        if (ok1) stf4_nt(g + i1, b);
         if (NORM) {
             const double d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll

@@ -484,9 +484,7 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
         set_error("%s: a buffer is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED;
     }
     const AdamScalars s = adam_scalars(*hp);
-    const int64_t ntile = (S + 511) / 512;
-    const dim3 grid(tile_grid((ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64),
-                              kMaxWorkItems / kAdamBlock));
+    const dim3 grid(tile_grid((S + kAdamTile - 1) / kAdamTile, kMaxWorkItems / kAdamBlock));
     const uint64_t* slut = p->d_seg_lut;
     const int sshift = p->seg_lut.shift;
     if (gathered && shard_bf16)
@@ -592,9 +590,7 @@ extern "C" int gsz_adamw_step(float* master, float* m, float* v, const float* g,
         set_error("%s: a buffer is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED;
     }
     const AdamScalars s = adam_scalars(*hp);
-    const int64_t ntile = (n + 511) / 512;
-    const int blocks = tile_grid((ntile + kAdamBlock / 64 - 1) / (kAdamBlock / 64),
-                                 kMaxWorkItems / kAdamBlock);
+    const int blocks = tile_grid((n + kAdamTile - 1) / kAdamTile, kMaxWorkItems / kAdamBlock);
     hipLaunchKernelGGL((k_adamw<false, true>), dim3(blocks), dim3(kAdamBlock), 0, stream, master, m, v, g,
                        coef, s, nullptr, nullptr, 0, (int64_t)0, n, nullptr, out_bf16);
     return launched(who);

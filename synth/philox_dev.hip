@@ -78,16 +78,19 @@ __global__ void synth_fill_pieces_kernel(uint32_t seed, uint32_t key1,
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming probes: one 16-byte vector per lane per tile of 256 vectors, one
-// short block per tile and a grid that covers the data (blocks stride over the
-// rest when the grid is capped) -- the launch shape that moves the most bytes
-// per second on MI355X.  The copy is also the byte-counter calibration kernel.
+// Streaming probes: one 16-byte vector per lane, one short block per tile and a
+// grid that covers the data (blocks stride over the rest when the grid is
+// capped) -- the launch shape that moves the most bytes per second on MI355X.
+// The copy is also the byte-counter calibration kernel.
 constexpr int64_t kProbeMaxGrid = (int64_t)1 << 23;
 
-__global__ __launch_bounds__(256) void synth_copy_kernel(const u32x4* __restrict__ src,
-                                                         u32x4* __restrict__ dst, int64_t n16) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+// Copy: 64-lane blocks and nontemporal loads and stores, the fastest copy shape
+// measured (6.7 TB/s; 256-lane blocks: 6.5 with the hints, 6.3 without).
+__global__ __launch_bounds__(64) void synth_copy_kernel(const u32x4* __restrict__ src,
+                                                        u32x4* __restrict__ dst, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * 64;
+    for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 // XOR of the 64 lanes' words, written by lane 0 to out[wave]: one word per
@@ -210,13 +213,14 @@ int synth_fill_dev_pieces(uint32_t seed, uint32_t key1, const int64_t* tab, int 
 }
 
 // Copies nbytes (a multiple of 16; both pointers 16-byte aligned).  grid <= 0
-// covers the data (one block per 256 vectors).
+// covers the data (one block per 64 vectors, at most 2^25 blocks).
 int synth_copy_dev(const void* src, void* dst, int64_t nbytes, int grid, hipStream_t stream) {
     if (nbytes < 0 || (nbytes & 15) || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return -1;
     if (nbytes == 0) return 0;
     const int64_t n16 = nbytes / 16;
-    const int64_t g = grid > 0 ? grid : probe_grid(n16);
-    hipLaunchKernelGGL(synth_copy_kernel, dim3((unsigned)g), dim3(256), 0, stream,
+    int64_t g = grid > 0 ? grid : (n16 + 63) / 64;
+    if (g > 4 * kProbeMaxGrid) g = 4 * kProbeMaxGrid;
+    hipLaunchKernelGGL(synth_copy_kernel, dim3((unsigned)g), dim3(64), 0, stream,
                        (const u32x4*)src, (u32x4*)dst, n16);
     return (int)hipGetLastError();
 }
