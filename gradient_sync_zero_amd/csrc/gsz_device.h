@@ -30,6 +30,9 @@ constexpr int kBlock = 256;
 // The pack kernels' block: one wave per 1 KiB tile copied 2.7% faster than
 // 256-lane blocks on 2 KiB tiles (7B share, MI355X).
 constexpr int kPackBlock = 64;
+// The fp32 accumulation buckets' block: 128 lanes, one group of 4 elements per
+// lane per 512-element tile (3% faster than 64 lanes with two groups each).
+constexpr int kF32Block = 128;
 // AdamW: one wave per block and one tile of 256 elements (4 per lane) per
 // block, with nontemporal hints on every access: 6% (7B share) to 10% (70B
 // share) faster than 512-lane blocks of 512 elements per wave without them.
@@ -83,6 +86,9 @@ __device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
 }
 __device__ __forceinline__ f32x4 ldf4_nt(const float* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(uint16_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 __device__ __forceinline__ void stf4_nt(float* p, f32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));

@@ -80,17 +80,18 @@ __global__ __launch_bounds__(kBlock) void k_zero_pads(const int64_t* __restrict_
 // fp32 accumulation buckets (gradient accumulation with an fp32 reduction
 // dtype): ACC = false widens the tensors of one batch into flat32 (the first
 // micro-batch), ACC = true adds them: flat32[off_t + j] = flat32[off_t + j] +
-// f32(grad_t[j]), one IEEE fp32 addition.  Tiles and grid as k_pack.  In a full
-// tile lane l takes elements 4l..4l+3 and 256+4l..256+4l+3 (two 8-byte bf16
-// loads), so each 16-byte fp32 load and store of the wave covers whole lines;
-// with nontemporal hints on every access this runs 5-6% faster than one 16-byte
-// bf16 load per lane widened into two half-line fp32 stores.
+// f32(grad_t[j]), one IEEE fp32 addition.  Tiles as k_pack, in blocks of
+// kF32Block = 128 lanes: in a full tile lane l takes elements 4l..4l+3 (one
+// 8-byte bf16 load), so each 16-byte fp32 load and store of a wave covers
+// whole lines; with nontemporal hints on every access this runs 5-6% faster
+// than one 16-byte bf16 load per lane widened into two half-line fp32 stores,
+// and one group per lane 3% faster than 64 lanes with two groups each.
 __device__ __forceinline__ void stf8(float* p, const float a[8]) {
     stf4(p, f32x4{a[0], a[1], a[2], a[3]});
     stf4(p + 4, f32x4{a[4], a[5], a[6], a[7]});
 }
 template <bool ACC>
-__global__ __launch_bounds__(kPackBlock) void k_pack_f32(PackPtrs pp, const int64_t* __restrict__ tab,
+__global__ __launch_bounds__(kF32Block) void k_pack_f32(PackPtrs pp, const int64_t* __restrict__ tab,
                                                      const uint64_t* __restrict__ tlut, int tshift,
                                                      int k0, int nk, int64_t t_begin, int64_t t_end,
                                                      float* __restrict__ flat) {
@@ -104,23 +105,18 @@ __global__ __launch_bounds__(kPackBlock) void k_pack_f32(PackPtrs pp, const int6
         float* __restrict__ dst = flat + tab[3 * k];
         const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
         if (vec && j1 - j0 == gsz::kPackTile) {
-            static_assert(gsz::kPackTile == 8 * kPackBlock, "two groups of 4 elements per lane");
-            const int64_t ja = j0 + 4 * tid, jb = ja + 4 * kPackBlock;
+            static_assert(gsz::kPackTile == 4 * kF32Block, "one group of 4 elements per lane");
+            const int64_t ja = j0 + 4 * tid;
             const u32x2 wa = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src + ja));
-            const u32x2 wb = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src + jb));
             f32x4 xa = f32x4{bf16_lo(wa.x), bf16_hi(wa.x), bf16_lo(wa.y), bf16_hi(wa.y)};
-            f32x4 xb = f32x4{bf16_lo(wb.x), bf16_hi(wb.x), bf16_lo(wb.y), bf16_hi(wb.y)};
             if (ACC) {
-                const f32x4 da = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dst + ja));
-                const f32x4 db = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(dst + jb));
+                const f32x4 da = ldf4_nt(dst + ja);
                 xa = f32x4{da.x + xa.x, da.y + xa.y, da.z + xa.z, da.w + xa.w};
-                xb = f32x4{db.x + xb.x, db.y + xb.y, db.z + xb.z, db.w + xb.w};
             }
-            __builtin_nontemporal_store(xa, reinterpret_cast<f32x4*>(dst + ja));
-            __builtin_nontemporal_store(xb, reinterpret_cast<f32x4*>(dst + jb));
+            stf4_nt(dst + ja, xa);
         } else if (vec) {
             const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
-            for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kPackBlock) {
+            for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kF32Block) {
                 float a[8];
                 widen8(ld16(src + j), a);
                 if (ACC) {
@@ -130,12 +126,12 @@ __global__ __launch_bounds__(kPackBlock) void k_pack_f32(PackPtrs pp, const int6
                 }
                 stf8(dst + j, a);
             }
-            for (int64_t j = jv + tid; j < j1; j += kPackBlock) {
+            for (int64_t j = jv + tid; j < j1; j += kF32Block) {
                 const float x = __uint_as_float((uint32_t)src[j] << 16);
                 dst[j] = ACC ? dst[j] + x : x;
             }
         } else {
-            for (int64_t j = j0 + tid; j < j1; j += kPackBlock) {
+            for (int64_t j = j0 + tid; j < j1; j += kF32Block) {
                 const float x = __uint_as_float((uint32_t)src[j] << 16);
                 dst[j] = ACC ? dst[j] + x : x;
             }

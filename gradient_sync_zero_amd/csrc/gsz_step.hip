@@ -281,7 +281,8 @@ int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, void* flat, int mod
         for (int k = 0; k < nk; ++k) pp.p[k] = ptrs[T - 1 - (k0 + k)];
         const int64_t tb = p->pack[3 * k0 + 2], te = p->pack[3 * (k0 + nk) + 2];
         if (te == tb) continue;
-        const int grid = tile_grid(te - tb, kMaxWorkItems / kPackBlock);
+        const int block = mode >= kPackF32 ? kF32Block : kPackBlock;
+        const int grid = tile_grid(te - tb, kMaxWorkItems / block);
         uint16_t* f16 = static_cast<uint16_t*>(flat);
         float* f32 = static_cast<float*>(flat);
         if (mode == kPack)
@@ -291,9 +292,9 @@ int run_pack(const gsz_plan* p, const uint16_t* const* ptrs, void* flat, int mod
         else if (mode == kAccumulate)
             hipLaunchKernelGGL(k_pack<kAccumulate>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f16);
         else if (mode == kPackF32)
-            hipLaunchKernelGGL(k_pack_f32<false>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f32);
+            hipLaunchKernelGGL(k_pack_f32<false>, dim3(grid), dim3(kF32Block), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f32);
         else
-            hipLaunchKernelGGL(k_pack_f32<true>, dim3(grid), dim3(kPackBlock), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f32);
+            hipLaunchKernelGGL(k_pack_f32<true>, dim3(grid), dim3(kF32Block), 0, stream, pp, p->d_pack, p->d_pack_lut, p->pack_lut.shift, k0, nk, tb, te, f32);
         if ((rc = launched(who))) return rc;
     }
     const int npad = (int)(p->pads.size() / 2);
