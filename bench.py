@@ -90,6 +90,15 @@ def short_name(full):
             return "k_reduce_mean_bf16_wire"
         if len(args) >= 4 and args[3] == "true":
             return "k_allreduce_mean"
+    if "k_reduce_mean_lc<" in full:          # <T, PS, NORM, FLAT, OUTFLAT, W16>
+        args = [a.strip() for a in full.split("k_reduce_mean_lc<")[1].split(">")[0].split(",")]
+        if args[0] == "float":
+            return "k_reduce_mean_f32"
+        if len(args) == 6 and args[5] == "true":
+            return "k_reduce_mean_bf16_wire"
+        if len(args) == 6 and args[4] == "true":
+            return "k_allreduce_mean"
+        return "k_reduce_mean"
     if "k_finalize_ranges" in full:
         return "k_finalize_ranges"
     if "k_pack_f32<false>" in full:

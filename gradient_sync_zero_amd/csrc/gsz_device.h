@@ -57,8 +57,10 @@ constexpr int64_t kRedTile = 8 * kBlock;
 static_assert(kRedTile == gsz::kRedElems && kMaxFlatGrid == gsz::kMaxRedGrid,
               "the workspace size assumes these grids");
 
-struct RankPtrs { const uint16_t* p[GSZ_MAX_RANKS]; };
-struct RankPtrsF { const float* p[GSZ_MAX_RANKS]; };
+template <typename T>
+struct RankPtrsT { const T* p[GSZ_MAX_RANKS]; };
+using RankPtrs = RankPtrsT<uint16_t>;
+using RankPtrsF = RankPtrsT<float>;
 struct PackPtrs { const uint16_t* p[gsz::kPackBatch]; };
 
 // fp32 constants of the AdamW update, each rounded once from double on the host.
@@ -110,6 +112,24 @@ __device__ __forceinline__ void add8(u32x4 w, float a[8]) {
     a[2] = a[2] + bf16_lo(w.y); a[3] = a[3] + bf16_hi(w.y);
     a[4] = a[4] + bf16_lo(w.z); a[5] = a[5] + bf16_hi(w.z);
     a[6] = a[6] + bf16_lo(w.w); a[7] = a[7] + bf16_hi(w.w);
+}
+
+// Four consecutive contribution values widened to fp32 (nontemporal): bf16 as
+// one 8-byte load, fp32 as one 16-byte load.
+__device__ __forceinline__ f32x4 ld4f_nt(const uint16_t* p) {
+    const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+}
+__device__ __forceinline__ f32x4 ld4f_nt(const float* p) { return ldf4_nt(p); }
+
+// a <- a + b, one IEEE fp32 add per element, partial sum on the left.
+__device__ __forceinline__ f32x4 add4(f32x4 a, f32x4 b) {
+    return f32x4{a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
+}
+// Each element rounded to bf16 (nearest even), kept as fp32.
+__device__ __forceinline__ f32x4 round4_bf16(f32x4 a) {
+    return f32x4{__uint_as_float(bf16_rne(a.x) << 16), __uint_as_float(bf16_rne(a.y) << 16),
+                 __uint_as_float(bf16_rne(a.z) << 16), __uint_as_float(bf16_rne(a.w) << 16)};
 }
 
 // a[j] <- bf16(a[j]) (round to nearest even), kept as fp32.

@@ -89,19 +89,24 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
     }
 }
 
-// The reduce over fp32 contributions (fp32 accumulation buckets, fp32 on the
-// ring's wire): the same ring order and division as k_reduce_mean, inputs
-// taken as they are.  A wave owns 512 shard elements of its block's tile as two
-// groups of 256; lane l handles elements 4l..4l+3 of each, so every 16-byte
-// load and store of a wave covers whole lines.  Blocks, XCD order and norm
-// partials as k_reduce_mean; nontemporal loads and stores as there.
-template <int PS, bool NORM, bool FLAT>
-__global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P, float invP, int pow2,
-                                                            const int64_t* __restrict__ seg,
-                                                            const uint64_t* __restrict__ slut, int sshift,
-                                                            int64_t owner, int64_t S,
-                                                            float* __restrict__ g,
-                                                            double* __restrict__ ws) {
+// The same ring-order mean in a lane-contiguous layout, for fp32 contributions
+// (fp32 accumulation buckets, fp32 on the ring's wire) and for bf16 ones at
+// small P.  A wave owns 512 shard elements of its block's tile as two groups of
+// 256; lane l handles elements 4l..4l+3 of each (an 8-byte bf16 or 16-byte
+// fp32 load per contribution and group), so every 16-byte fp32 store of a wave
+// covers whole lines.  With nontemporal stores that matters: k_reduce_mean's
+// lanes store 32 contiguous bytes as two half-line stores, which reach HBM as
+// 9% more write bytes, and this layout is 4-5% faster at P = 8-16.  At P = 64
+// its twice as many (half-size) bf16 loads make it 6-7% slower, so the larger
+// P keep k_reduce_mean.  OUTFLAT and W16 as there; blocks, XCD order and norm
+// partials as there.
+template <typename T, int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
+__global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int P, float invP, int pow2,
+                                                           const int64_t* __restrict__ seg,
+                                                           const uint64_t* __restrict__ slut, int sshift,
+                                                           int64_t owner, int64_t S,
+                                                           float* __restrict__ g,
+                                                           double* __restrict__ ws) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);
     double sq = 0.0;
@@ -109,12 +114,15 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P,
     int64_t t = bx * kRedTile;
     if (FLAT && t < S) cur.seek(t, slut, sshift);                     // uniform: scalar loads
     const float fP = (float)P;
+    const f32x4 zero = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (; t < S; t += (int64_t)gridDim.x * kRedTile) {
         const int64_t i0 = t + 512 * wave + 4 * lane, i1 = i0 + 256;
         const bool ok0 = i0 < S, ok1 = i1 < S;               // S and i are multiples of 4
+        // Past the end a lane reads position 0 of each contribution (in bounds) and
+        // discards the result: loads under a condition became one branch and one
+        // full wait per load, serialising them.
         const int64_t off0 = ok0 ? (FLAT ? cur.map(i0) : i0) : 0;
         const int64_t off1 = ok1 ? (FLAT ? cur.map(i1) : i1) : 0;
-        const f32x4 zero = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         f32x4 a = zero, b = zero;
         if constexpr (PS > 0) {
             constexpr int G = PS < 16 ? PS : 16;
@@ -123,26 +131,24 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P,
                 f32x4 w0[G], w1[G];
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
-                    w0[j] = ok0 ? ldf4_nt(rp.p[k0 + j] + off0) : zero;
-                    w1[j] = ok1 ? ldf4_nt(rp.p[k0 + j] + off1) : zero;
+                    w0[j] = ld4f_nt(rp.p[k0 + j] + off0);
+                    w1[j] = ld4f_nt(rp.p[k0 + j] + off1);
                 }
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
-                    if (k0 + j == 0) { a = w0[j]; b = w1[j]; }
-                    else {
-                        a.x = a.x + w0[j].x; a.y = a.y + w0[j].y; a.z = a.z + w0[j].z; a.w = a.w + w0[j].w;
-                        b.x = b.x + w1[j].x; b.y = b.y + w1[j].y; b.z = b.z + w1[j].z; b.w = b.w + w1[j].w;
-                    }
+                    if (k0 + j == 0) { a = w0[j]; b = w1[j]; continue; }
+                    a = add4(a, w0[j]);
+                    b = add4(b, w1[j]);
+                    if (W16) { a = round4_bf16(a); b = round4_bf16(b); }
                 }
             }
         } else {
-            a = ok0 ? ldf4_nt(rp.p[0] + off0) : zero;
-            b = ok1 ? ldf4_nt(rp.p[0] + off1) : zero;
+            a = ld4f_nt(rp.p[0] + off0);
+            b = ld4f_nt(rp.p[0] + off1);
             for (int k = 1; k < P; ++k) {
-                const f32x4 w0 = ok0 ? ldf4_nt(rp.p[k] + off0) : zero;
-                const f32x4 w1 = ok1 ? ldf4_nt(rp.p[k] + off1) : zero;
-                a.x = a.x + w0.x; a.y = a.y + w0.y; a.z = a.z + w0.z; a.w = a.w + w0.w;
-                b.x = b.x + w1.x; b.y = b.y + w1.y; b.z = b.z + w1.z; b.w = b.w + w1.w;
+                a = add4(a, ld4f_nt(rp.p[k] + off0));
+                b = add4(b, ld4f_nt(rp.p[k] + off1));
+                if (W16) { a = round4_bf16(a); b = round4_bf16(b); }
             }
         }
         if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
@@ -152,12 +158,14 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_f32(RankPtrsF rp, int P,
             a = f32x4{a.x / fP, a.y / fP, a.z / fP, a.w / fP};
             b = f32x4{b.x / fP, b.y / fP, b.z / fP, b.w / fP};
         }
-        if (ok0) stf4_nt(g + i0, a);
-        if (ok1) stf4_nt(g + i1, b);
+        if (ok0) stf4_nt(g + (OUTFLAT ? off0 : i0), a);      // all-reduce output: the flat position
+        if (ok1) stf4_nt(g + (OUTFLAT ? off1 : i1), b);
         if (NORM) {
+            a = ok0 ? a : zero;
+            b = ok1 ? b : zero;
             const double d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sq = __fma_rn(d[j], d[j], sq);   // zeros where !ok
+            for (int j = 0; j < 8; ++j) sq = __fma_rn(d[j], d[j], sq);
         }
     }
     if (NORM) {

@@ -170,18 +170,41 @@ void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPt
         hipLaunchKernelGGL((k_reduce_mean<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
 }
 
-template <int PS>
-void launch_reduce_f32(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPtrsF& rp, int P,
-                       float invP, int pow2, const int64_t* seg, const uint64_t* slut, int sshift, int64_t owner, int64_t S,
-                       float* g, double* ws) {
-    if (norm && flat)
-        hipLaunchKernelGGL((k_reduce_mean_f32<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g, ws);
-    else if (norm)
-        hipLaunchKernelGGL((k_reduce_mean_f32<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g, ws);
-    else if (flat)
-        hipLaunchKernelGGL((k_reduce_mean_f32<PS, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g, ws);
-    else
-        hipLaunchKernelGGL((k_reduce_mean_f32<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g, ws);
+// The lane-contiguous reduce (k_reduce_mean_lc) for bf16 contributions at
+// P <= kLcMaxP and for fp32 contributions at every P.
+constexpr int kLcMaxP = 16;
+
+template <typename T, int PS>
+void launch_reduce_lc(bool norm, bool flat, bool outflat, bool wire16, dim3 grid, hipStream_t st,
+                      const RankPtrsT<T>& rp, int P, float invP, int pow2, const int64_t* seg,
+                      const uint64_t* slut, int sshift, int64_t owner, int64_t S, float* g,
+                      double* ws) {
+    auto go = [&](auto nm, auto fl, auto of, auto w16) {
+        hipLaunchKernelGGL((k_reduce_mean_lc<T, PS, decltype(nm)::value, decltype(fl)::value,
+                                             decltype(of)::value, decltype(w16)::value>),
+                           grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g,
+                           ws);
+    };
+    using Y = std::true_type;
+    using N = std::false_type;
+    auto layouts = [&](auto w16) {
+        if (norm && flat) go(Y{}, Y{}, N{}, w16);
+        else if (norm) go(Y{}, N{}, N{}, w16);
+        else if (flat) go(N{}, Y{}, N{}, w16);
+        else go(N{}, N{}, N{}, w16);
+    };
+    if constexpr (std::is_same<T, float>::value) {
+        layouts(N{});                            // fp32 contributions: the reduce rows only
+    } else {
+        if (outflat) {
+            if (norm) go(Y{}, Y{}, Y{}, N{});
+            else go(N{}, Y{}, Y{}, N{});
+        } else if (wire16) {
+            layouts(Y{});
+        } else {
+            layouts(N{});
+        }
+    }
 }
 
 }  // namespace
@@ -376,8 +399,9 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         const int sshift = p->seg_lut.shift;
         double* wsd = static_cast<double*>(ws);
         with_static_p(P, [&](auto ps) {
-            launch_reduce_f32<decltype(ps)::value>(norm, flat, dim3(grid), stream, rp, P, invP, pow2,
-                                                   p->d_seg, slut, sshift, owner, S, g, wsd);
+            launch_reduce_lc<float, decltype(ps)::value>(norm, flat, false, false, dim3(grid), stream,
+                                                         rp, P, invP, pow2, p->d_seg, slut, sshift,
+                                                         owner, S, g, wsd);
         });
         if ((rc = launched(who))) return rc;
     } else if (S > 0) {
@@ -391,8 +415,13 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         const int sshift = p->seg_lut.shift;
         double* wsd = static_cast<double*>(ws);
         with_static_p(P, [&](auto ps) {
-            launch_reduce<decltype(ps)::value>(norm, flat, dim3(grid), stream, rp, P, invP, pow2,
-                                               p->d_seg, slut, sshift, owner, nvec, g, wsd, false, wire16);
+            constexpr int PS = decltype(ps)::value;
+            if constexpr (PS > 0 && PS <= kLcMaxP)
+                launch_reduce_lc<uint16_t, PS>(norm, flat, false, wire16, dim3(grid), stream, rp, P,
+                                               invP, pow2, p->d_seg, slut, sshift, owner, S, g, wsd);
+            else
+                launch_reduce<PS>(norm, flat, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
+                                  sshift, owner, nvec, g, wsd, false, wire16);
         });
         if ((rc = launched(who))) return rc;
     }
@@ -563,8 +592,13 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
         RankPtrs rp{};
         for (int k = 0; k < P; ++k) rp.p[k] = contrib[(c + 1 + k) % P];
         with_static_p(P, [&](auto ps) {
-            launch_reduce<decltype(ps)::value>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg,
-                                               slut, sshift, c, nvec, g_flat, wsd, true);
+            constexpr int PS = decltype(ps)::value;
+            if constexpr (PS > 0 && PS <= kLcMaxP)
+                launch_reduce_lc<uint16_t, PS>(norm, true, true, false, gr, stream, rp, P, invP, pow2,
+                                               p->d_seg, slut, sshift, c, S, g_flat, wsd);
+            else
+                launch_reduce<PS>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, slut, sshift,
+                                  c, nvec, g_flat, wsd, true);
         });
         if ((rc = launched(who))) return rc;
         if (norm) {

@@ -43,6 +43,18 @@ def test_trace_summary_names_template_instances(tmp_path):
     assert lines[2][0] == "k_reduce_mean_bf16_wire"
 
 
+def test_lane_contiguous_reduce_instances_are_named_by_row():
+    lc = "void (anonymous namespace)::k_reduce_mean_lc<{}>(RankPtrsT<{}>, int, float, int)"
+    assert bench.short_name(lc.format("unsigned short, 8, true, true, false, false", "unsigned short")) \
+        == "k_reduce_mean"
+    assert bench.short_name(lc.format("float, 8, true, false, false, false", "float")) \
+        == "k_reduce_mean_f32"
+    assert bench.short_name(lc.format("unsigned short, 4, true, true, false, true", "unsigned short")) \
+        == "k_reduce_mean_bf16_wire"
+    assert bench.short_name(lc.format("unsigned short, 2, false, true, true, false", "unsigned short")) \
+        == "k_allreduce_mean"
+
+
 def test_counter_summary_scales_by_the_copy_kernel_and_is_keyed(tmp_path):
     # FETCH_SIZE / WRITE_SIZE arrive as several rows per dispatch (one per
     # counter instance); the summary sums them per dispatch, averages per
