@@ -171,7 +171,8 @@ void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPt
 }
 
 // The lane-contiguous reduce (k_reduce_mean_lc) for bf16 contributions at
-// P <= kLcMaxP and for fp32 contributions at every P.
+// P <= kLcMaxP (compile-time P for the powers of two, its runtime-P loop for
+// the others) and for fp32 contributions at every P.
 constexpr int kLcMaxP = 16;
 
 template <typename T, int PS>
@@ -416,9 +417,10 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         double* wsd = static_cast<double*>(ws);
         with_static_p(P, [&](auto ps) {
             constexpr int PS = decltype(ps)::value;
-            if constexpr (PS > 0 && PS <= kLcMaxP)
-                launch_reduce_lc<uint16_t, PS>(norm, flat, false, wire16, dim3(grid), stream, rp, P,
-                                               invP, pow2, p->d_seg, slut, sshift, owner, S, g, wsd);
+            if (PS > 0 ? PS <= kLcMaxP : P <= kLcMaxP)
+                launch_reduce_lc<uint16_t, PS <= kLcMaxP ? PS : 0>(
+                    norm, flat, false, wire16, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
+                    sshift, owner, S, g, wsd);
             else
                 launch_reduce<PS>(norm, flat, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
                                   sshift, owner, nvec, g, wsd, false, wire16);
@@ -593,9 +595,10 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
         for (int k = 0; k < P; ++k) rp.p[k] = contrib[(c + 1 + k) % P];
         with_static_p(P, [&](auto ps) {
             constexpr int PS = decltype(ps)::value;
-            if constexpr (PS > 0 && PS <= kLcMaxP)
-                launch_reduce_lc<uint16_t, PS>(norm, true, true, false, gr, stream, rp, P, invP, pow2,
-                                               p->d_seg, slut, sshift, c, S, g_flat, wsd);
+            if (PS > 0 ? PS <= kLcMaxP : P <= kLcMaxP)
+                launch_reduce_lc<uint16_t, PS <= kLcMaxP ? PS : 0>(
+                    norm, true, true, false, gr, stream, rp, P, invP, pow2, p->d_seg, slut, sshift, c,
+                    S, g_flat, wsd);
             else
                 launch_reduce<PS>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, slut, sshift,
                                   c, nvec, g_flat, wsd, true);
