@@ -115,3 +115,38 @@ def test_adamw_step_rejects_ragged_sizes():
     with pytest.raises(G.GszError) as e:
         G.adamw_step(x, x.clone(), x.clone(), x.clone(), coef, W.AdamWHP(), out)
     assert e.value.name == "GSZ_ERR_SIZE"
+
+
+@pytest.mark.parametrize("P", [3, 6, 12, 24, 32])
+def test_allreduce_every_kernel_family(P):
+    """The all-reduce at world sizes that run the lane-contiguous kernel's
+    runtime-P loop (3, 6, 12), the 16-byte kernel's runtime-P loop (24) and its
+    compile-time P (32), against the message-passing ring, with the chunk
+    owners' norm partials."""
+    from oracle.bf16 import narrow
+    from oracle.reduce import ring_allreduce_sim
+    rng = np.random.default_rng(900 + P)
+    numel = [int(x) for x in rng.integers(1, 4000, 7)]
+    plan = G.Plan(numel, 6000, P).upload()
+    oplan = make_plan(numel, 6000, P)
+    flats, dev = [], []
+    for q in range(P):
+        x = rng.normal(size=sum(numel)) * np.exp2(rng.integers(-10, 11, size=sum(numel)))
+        bits = narrow(x.astype(np.float32))
+        grads = [bits[s:s + n] for s, n in zip(OI.prefix(numel), numel)]
+        flats.append(opack.pack(oplan, grads))
+        f = torch.empty(plan.flat_len, dtype=torch.uint16, device="cuda")
+        G.bucket_pack(plan, [torch.from_numpy(gq.view(np.int16).copy()).view(torch.uint16).cuda()
+                             for gq in grads], f)
+        dev.append(f)
+    g = torch.full((plan.flat_len,), float("nan"), dtype=torch.float32, device="cuda")
+    parts = torch.zeros(P, dtype=torch.float64, device="cuda")
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+    G.allreduce_mean(plan, dev, g, parts, ws)
+    torch.cuda.synchronize()
+    results, _, _ = ring_allreduce_sim(oplan, flats)
+    assert_bits(host(g), results[0], f"all-reduce mean, P={P}")
+    for c in range(P):
+        want = sqnorm_partial(opack.owner_view(oplan, results[0], c))
+        assert abs(host(parts)[c] - want) <= 1e-12 * max(want, 1e-300), (P, c)
+

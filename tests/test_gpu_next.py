@@ -200,3 +200,41 @@ def test_fp32_accumulation_unaligned_sources():
     hg = [host(t) for t in grads]
     want = opack.accumulate_f32(oplan, opack.pack_f32(oplan, hg), hg)
     assert_bits(host(flat), want, "unaligned fp32 accumulation")
+
+
+@pytest.mark.parametrize("P", [3, 6, 12, 24, 64])
+def test_bf16_wire_every_kernel_family(P):
+    """The bf16-wire reduce at world sizes that run the lane-contiguous kernel's
+    runtime-P loop (3, 6, 12), the 16-byte kernel's runtime-P loop (24) and its
+    compile-time P (64), both layouts, against the oracle's bf16-wire ring."""
+    from oracle.bf16 import narrow
+    rng = np.random.default_rng(700 + P)
+    numel = [int(x) for x in rng.integers(1, 4000, 7)]
+    plan = G.Plan(numel, 6000, P).upload()
+    oplan = make_plan(numel, 6000, P)
+    flats, dev = [], []
+    for q in range(P):
+        x = rng.normal(size=sum(numel)) * np.exp2(rng.integers(-10, 11, size=sum(numel)))
+        bits = narrow(x.astype(np.float32))
+        grads = [bits[s:s + n] for s, n in zip(OI.prefix(numel), numel)]
+        flats.append(opack.pack(oplan, grads))
+        f = torch.empty(plan.flat_len, dtype=torch.uint16, device="cuda")
+        G.bucket_pack(plan, [torch.from_numpy(gq.view(np.int16).copy()).view(torch.uint16).cuda()
+                             for gq in grads], f)
+        dev.append(f)
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+    part = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for r in sorted({0, P // 2, P - 1}):
+        g = torch.empty(plan.shard_len, dtype=torch.float32, device="cuda")
+        G.shard_reduce_mean(plan, r, dev, G.LAYOUT_BUCKET_FLAT, g, part, ws, bf16_wire=True)
+        gc = torch.empty_like(g)
+        comp = [torch.cat([f[b["base"] + r * b["chunk"]:b["base"] + (r + 1) * b["chunk"]]
+                           for b in plan.buckets()]).contiguous() for f in dev]
+        G.shard_reduce_mean(plan, r, comp, G.LAYOUT_SHARD_COMPACT, gc, None, None, bf16_wire=True)
+        torch.cuda.synchronize()
+        want = reduce_mean_bf16_wire([opack.owner_view(oplan, f, r) for f in flats], r)
+        assert_bits(host(g), want, f"bf16-wire P={P} owner {r}")
+        assert_bits(host(gc), want, f"bf16-wire P={P} owner {r} (shard-compact)")
+        sq = sqnorm_partial(want)
+        assert abs(host(part)[0] - sq) <= 1e-12 * max(sq, 1e-300)
+
