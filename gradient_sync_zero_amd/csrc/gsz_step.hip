@@ -141,33 +141,35 @@ void with_static_p(int P, F&& f) {
     }
 }
 
+// Launches k_reduce_mean<PS, ...> with the flags as template arguments (the
+// combinations the entry points use).
 template <int PS>
 void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPtrs& rp, int P,
-                   float invP, int pow2, const int64_t* seg, const uint64_t* slut, int sshift, int64_t owner, int64_t nvec,
-                   float* g, double* ws, bool outflat = false, bool wire16 = false) {
-    if (wire16) {
-        if (norm && flat)
-            hipLaunchKernelGGL((k_reduce_mean<PS, true, true, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-        else if (norm)
-            hipLaunchKernelGGL((k_reduce_mean<PS, true, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-        else if (flat)
-            hipLaunchKernelGGL((k_reduce_mean<PS, false, true, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-        else
-            hipLaunchKernelGGL((k_reduce_mean<PS, false, false, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-        return;
+                   float invP, int pow2, const int64_t* seg, const uint64_t* slut, int sshift,
+                   int64_t owner, int64_t nvec, float* g, double* ws, bool outflat = false,
+                   bool wire16 = false) {
+    auto go = [&](auto nm, auto fl, auto of, auto w16) {
+        hipLaunchKernelGGL((k_reduce_mean<PS, decltype(nm)::value, decltype(fl)::value,
+                                          decltype(of)::value, decltype(w16)::value>),
+                           grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner,
+                           nvec, g, ws);
+    };
+    using Y = std::true_type;
+    using N = std::false_type;
+    auto layouts = [&](auto w16) {
+        if (norm && flat) go(Y{}, Y{}, N{}, w16);
+        else if (norm) go(Y{}, N{}, N{}, w16);
+        else if (flat) go(N{}, Y{}, N{}, w16);
+        else go(N{}, N{}, N{}, w16);
+    };
+    if (outflat) {
+        if (norm) go(Y{}, Y{}, Y{}, N{});
+        else go(N{}, Y{}, Y{}, N{});
+    } else if (wire16) {
+        layouts(Y{});
+    } else {
+        layouts(N{});
     }
-    if (outflat && norm)
-        hipLaunchKernelGGL((k_reduce_mean<PS, true, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-    else if (outflat)
-        hipLaunchKernelGGL((k_reduce_mean<PS, false, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-    else if (norm && flat)
-        hipLaunchKernelGGL((k_reduce_mean<PS, true, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-    else if (norm)
-        hipLaunchKernelGGL((k_reduce_mean<PS, true, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-    else if (flat)
-        hipLaunchKernelGGL((k_reduce_mean<PS, false, true>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
-    else
-        hipLaunchKernelGGL((k_reduce_mean<PS, false, false>), grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, nvec, g, ws);
 }
 
 // The lane-contiguous reduce (k_reduce_mean_lc) for bf16 contributions at
