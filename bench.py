@@ -128,6 +128,20 @@ def gpu_step_stats(ev):
     return dict(mean=float(np.mean(t)), median=float(np.median(t)), min=float(np.min(t)))
 
 
+def profile_commands(config):
+    """The rocprofv3 command lines (run from the repository root) whose output
+    the summaries below are made from: a kernel trace of the default bench of
+    a workload, and one counter pass each for FETCH_SIZE and WRITE_SIZE."""
+    bench_args = f"python3 bench.py --config {config} --no-cpu-baseline"
+    short = f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline"
+    return {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_c{config} "
+                     f"-o bench -- {bench_args}",
+            "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmcf_c{config} "
+                     f"-o bench -- {short}",
+            "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmcw_c{config} "
+                     f"-o bench -- {short}"}
+
+
 def summarize_trace(csv_path, workload, command, out_dir=None):
     import csv
     rows = list(csv.DictReader(open(csv_path)))
@@ -389,10 +403,13 @@ def main():
         from synth import workloads as W
         wname = W.by_id(args.config).name
         if args.summarize_trace:
-            summarize_trace(args.summarize_trace, wname, args.command)
+            summarize_trace(args.summarize_trace, wname,
+                            args.command or profile_commands(args.config)["trace"])
         if args.summarize_pmc:
             nb = int(args.copy_gib * (1 << 30)) // 16 * 16
-            summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], wname, args.command, nb)
+            cmds = profile_commands(args.config)
+            summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], wname,
+                          args.command or f"{cmds['fetch']} ; {cmds['write']}", nb)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: only --gpus 1 is supported: the P data-parallel ranks are simulated "

@@ -38,6 +38,20 @@ constexpr int kF32Block = 128;
 // share) faster than 512-lane blocks of 512 elements per wave without them.
 constexpr int kAdamBlock = 64;
 constexpr int64_t kAdamTile = 4 * kAdamBlock;
+// Dynamic LDS that AdamW's launches reserve and never touch: 13 KiB per block
+// leaves room for 12 resident blocks per CU in gfx950's 160 KiB, against 32
+// without it.  Fewer waves in flight over AdamW's eight streams ran 3-8% faster
+// (7B share) and 5% faster (70B share); at 10 or fewer blocks per CU it slows
+// down again.
+constexpr size_t kAdamLdsBytes = 13 * 1024;
+// The same occupancy cap for the lane-contiguous reduce (256-lane blocks):
+// 32 KiB per block leaves 5 resident blocks per CU.  It pays where each
+// element's contributions add up to 16 bytes or more (bf16 at P >= 8, fp32 at
+// P >= 4): 3% faster at P=8 bf16 (7B share), 1.7% for fp32 contributions at
+// P=8.  Below that the loads of one wave are too few to keep HBM busy with so
+// few waves: P=2 and 3 ran 15-25% slower with the cap, so they launch without.
+constexpr size_t kRedLcLdsBytes = 32 * 1024;
+constexpr int kRedLcLdsMinBytes = 16;
 // Work-items of one dispatch stay at or below 2^31 (the dispatch packet's grid
 // size is a 32-bit count).  Grids are capped accordingly; bigger inputs make
 // blocks stride over the remaining tiles.

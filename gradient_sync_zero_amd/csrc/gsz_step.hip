@@ -182,10 +182,11 @@ void launch_reduce_lc(bool norm, bool flat, bool outflat, bool wire16, dim3 grid
                       const RankPtrsT<T>& rp, int P, float invP, int pow2, const int64_t* seg,
                       const uint64_t* slut, int sshift, int64_t owner, int64_t S, float* g,
                       double* ws) {
+    const size_t lds = (int64_t)P * (int64_t)sizeof(T) >= kRedLcLdsMinBytes ? kRedLcLdsBytes : 0;
     auto go = [&](auto nm, auto fl, auto of, auto w16) {
         hipLaunchKernelGGL((k_reduce_mean_lc<T, PS, decltype(nm)::value, decltype(fl)::value,
                                              decltype(of)::value, decltype(w16)::value>),
-                           grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g,
+                           grid, dim3(kBlock), lds, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g,
                            ws);
     };
     using Y = std::true_type;
@@ -522,11 +523,11 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
     const uint64_t* slut = p->d_seg_lut;
     const int sshift = p->seg_lut.shift;
     if (gathered && shard_bf16)
-        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
     else if (gathered)
-        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
     else
-        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kAdamBlock), 0, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
     return launched(who);
 }
 
@@ -631,7 +632,7 @@ extern "C" int gsz_adamw_step(float* master, float* m, float* v, const float* g,
     }
     const AdamScalars s = adam_scalars(*hp);
     const int blocks = tile_grid((n + kAdamTile - 1) / kAdamTile, kMaxWorkItems / kAdamBlock);
-    hipLaunchKernelGGL((k_adamw<false, true>), dim3(blocks), dim3(kAdamBlock), 0, stream, master, m, v, g,
+    hipLaunchKernelGGL((k_adamw<false, true>), dim3(blocks), dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g,
                        coef, s, nullptr, nullptr, 0, (int64_t)0, n, nullptr, out_bf16);
     return launched(who);
 }

@@ -80,3 +80,21 @@ def test_counter_summary_scales_by_the_copy_kernel_and_is_keyed(tmp_path):
     p = tmp_path / "traffic_w.txt"
     p.write_text(p.read_text().replace(bench.kernel_source_digest(), "0" * 64))
     assert bench.read_traffic("k_adamw", "w", profiles_dir=str(tmp_path)) is None
+
+
+def test_committed_profiles_record_the_command_that_made_them():
+    prof = os.path.join(ROOT, "profiles")
+    names = sorted(n for n in os.listdir(prof) if n.endswith(".txt"))
+    assert names
+    for n in names:
+        cmd = [l for l in open(os.path.join(prof, n)) if l.startswith("# command:")]
+        assert len(cmd) == 1, n
+        text = cmd[0][len("# command:"):].strip()
+        assert text.startswith("rocprofv3 ") and "-- python3 bench.py --config" in text, (n, text)
+
+
+def test_profile_commands_match_the_summary_kinds():
+    c = bench.profile_commands(3)
+    assert "--kernel-trace --stats" in c["trace"] and "--pmc" not in c["trace"]
+    assert "--pmc FETCH_SIZE" in c["fetch"] and "--pmc WRITE_SIZE" in c["write"]
+    assert all("--config 3" in v for v in c.values())
