@@ -116,24 +116,46 @@ def _check(rc: int):
 
 
 def _stream(stream):
+    """A raw hipStream_t (int), a torch.cuda.Stream, or None for torch's
+    current stream."""
     if stream is not None:
-        return stream
+        return getattr(stream, "cuda_stream", stream)
     import torch
     return torch.cuda.current_stream().cuda_stream
 
 
-def _ptr(t, name, dtypes, allow_none=False):
+def _ptr(t, name, dtypes, allow_none=False, min_numel=None, numel=None):
+    """Device address of tensor t after checking it.  The library receives
+    bare pointers and cannot see how long a buffer is, so the lengths the plan
+    implies are checked here: min_numel for buffers the call reads or writes
+    a known range of, numel for tensors whose size the plan fixes exactly.  A
+    short buffer would otherwise be read or written past its end on the GPU."""
     if t is None:
         if allow_none:
             return None
         raise ValueError(f"{name} is required")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the plan needs exactly {numel}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the call needs at least {min_numel}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _contrib_len(plan, layout):
+    """Elements each contribution must hold: the whole bucket-flat buffer, or
+    the owner's shard in shard-compact layout (unknown layouts are left to the
+    library, which rejects them)."""
+    if layout == LAYOUT_BUCKET_FLAT:
+        return plan.flat_len
+    if layout == LAYOUT_SHARD_COMPACT:
+        return plan.shard_len
+    return None
 
 
 def _bf16_types():
@@ -157,7 +179,8 @@ class Plan:
     def __init__(self, numel, bucket_cap_bytes, world_size, align=64):
         lib = load()
         n = len(numel)
-        arr = (_I64 * max(n, 1))(*[int(x) for x in numel])
+        self.numel = [int(x) for x in numel]
+        arr = (_I64 * max(n, 1))(*self.numel)
         h = _P()
         _check(lib.gsz_plan_create(arr, n, int(bucket_cap_bytes), int(world_size), int(align),
                                    ctypes.byref(h)))
@@ -232,52 +255,63 @@ def set_grid_limit(max_blocks):
 
 def bucket_pack(plan, grads, flat, stream=None):
     bt = _bf16_types()
-    if len(grads) != plan.n_tensors:
-        raise ValueError("need one gradient per plan tensor")
-    ptrs = (_P * max(len(grads), 1))(*[_ptr(t, f"grads[{i}]", bt) if t.numel() else None
-                                       for i, t in enumerate(grads)])
-    _check(load().gsz_bucket_pack(plan.handle, ptrs, _ptr(flat, "flat", bt), _stream(stream)))
+    ptrs = _tensor_ptrs(plan, grads, "grads")
+    _check(load().gsz_bucket_pack(plan.handle, ptrs,
+                                  _ptr(flat, "flat", bt, min_numel=plan.flat_len), _stream(stream)))
 
 
 def bucket_accumulate(plan, grads, flat, stream=None):
     bt = _bf16_types()
-    if len(grads) != plan.n_tensors:
-        raise ValueError("need one gradient per plan tensor")
-    ptrs = (_P * max(len(grads), 1))(*[_ptr(t, f"grads[{i}]", bt) if t.numel() else None
-                                       for i, t in enumerate(grads)])
-    _check(load().gsz_bucket_accumulate(plan.handle, ptrs, _ptr(flat, "flat", bt),
+    ptrs = _tensor_ptrs(plan, grads, "grads")
+    _check(load().gsz_bucket_accumulate(plan.handle, ptrs,
+                                        _ptr(flat, "flat", bt, min_numel=plan.flat_len),
                                         _stream(stream)))
 
 
-def _grad_ptrs(plan, grads):
+def _tensor_ptrs(plan, tensors, name):
+    """Host array of the per-tensor device pointers, forward order; each tensor
+    must hold exactly the plan's size for it (NULL for empty tensors)."""
     bt = _bf16_types()
-    if len(grads) != plan.n_tensors:
-        raise ValueError("need one gradient per plan tensor")
-    return (_P * max(len(grads), 1))(*[_ptr(t, f"grads[{i}]", bt) if t.numel() else None
-                                       for i, t in enumerate(grads)])
+    if len(tensors) != plan.n_tensors:
+        raise ValueError(f"need one {name} tensor per plan tensor ({plan.n_tensors}), "
+                         f"got {len(tensors)}")
+    return (_P * max(len(tensors), 1))(*[
+        _ptr(t, f"{name}[{i}]", bt, numel=plan.numel[i]) if plan.numel[i] else None
+        for i, t in enumerate(tensors)])
+
+
+def _grad_ptrs(plan, grads):
+    return _tensor_ptrs(plan, grads, "grads")
 
 
 def bucket_pack_f32(plan, grads, flat32, stream=None):
     """First micro-batch of an fp32 accumulation window: flat32 = f32(grads), pads 0."""
     _check(load().gsz_bucket_pack_f32(plan.handle, _grad_ptrs(plan, grads),
-                                      _ptr(flat32, "flat32", _f32()), _stream(stream)))
+                                      _ptr(flat32, "flat32", _f32(), min_numel=plan.flat_len),
+                                      _stream(stream)))
 
 
 def bucket_accumulate_f32(plan, grads, flat32, stream=None):
     """Later micro-batches: flat32 += f32(grads) (fp32 adds)."""
     _check(load().gsz_bucket_accumulate_f32(plan.handle, _grad_ptrs(plan, grads),
-                                            _ptr(flat32, "flat32", _f32()), _stream(stream)))
+                                            _ptr(flat32, "flat32", _f32(), min_numel=plan.flat_len),
+                                            _stream(stream)))
 
 
 def shard_reduce_mean_f32(plan, owner, contribs, layout, g, partial_out=None, ws=None, stream=None):
     """gsz_shard_reduce_mean_f32: the ring-order mean of P fp32 contributions."""
     if len(contribs) != plan.world_size:
         raise ValueError("need one contribution per rank")
-    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", _f32()) for i, t in enumerate(contribs)])
+    clen = _contrib_len(plan, layout)
+    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", _f32(), min_numel=clen)
+                                  for i, t in enumerate(contribs)])
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(load().gsz_shard_reduce_mean_f32(plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32()),
-                                            _ptr(partial_out, "partial_out", _f64(), allow_none=True),
+    _check(load().gsz_shard_reduce_mean_f32(plan.handle, owner, ptrs, layout,
+                                            _ptr(g, "g", _f32(), min_numel=plan.shard_len),
+                                            _ptr(partial_out, "partial_out", _f64(),
+                                                 allow_none=True,
+                                                 min_numel=1),
                                             wsp, nbytes, _stream(stream)))
 
 
@@ -287,28 +321,30 @@ def shard_reduce_mean(plan, owner, contribs, layout, g, partial_out=None, ws=Non
     bt = _bf16_types()
     if len(contribs) != plan.world_size:
         raise ValueError("need one contribution per rank")
-    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", bt) for i, t in enumerate(contribs)])
+    clen = _contrib_len(plan, layout)
+    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", bt, min_numel=clen)
+                                  for i, t in enumerate(contribs)])
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     fn = load().gsz_shard_reduce_mean_bf16_wire if bf16_wire else load().gsz_shard_reduce_mean
-    _check(fn(plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32()),
-                                        _ptr(partial_out, "partial_out", _f64(), allow_none=True),
-                                        wsp, nbytes, _stream(stream)))
+    _check(fn(plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32(), min_numel=plan.shard_len),
+              _ptr(partial_out, "partial_out", _f64(), allow_none=True, min_numel=1),
+              wsp, nbytes, _stream(stream)))
 
 
 def shard_grad_sqnorm(g, partial_out, ws, n=None, stream=None):
-    n = g.numel() if n is None else n
-    _check(load().gsz_shard_grad_sqnorm(_ptr(g, "g", _f32()), n,
-                                        _ptr(partial_out, "partial_out", _f64()),
+    n = g.numel() if n is None else int(n)
+    _check(load().gsz_shard_grad_sqnorm(_ptr(g, "g", _f32(), min_numel=n), n,
+                                        _ptr(partial_out, "partial_out", _f64(), min_numel=1),
                                         _ptr(ws, "ws", (ws.dtype,)), ws.numel() * ws.element_size(),
                                         _stream(stream)))
 
 
 def clip_coef(partials, max_norm, coef_out, norm_out=None, total_out=None, stream=None):
     _check(load().gsz_clip_coef(_ptr(partials, "partials", _f64()), partials.numel(),
-                                float(max_norm), _ptr(coef_out, "coef_out", _f32()),
-                                _ptr(norm_out, "norm_out", _f32(), allow_none=True),
-                                _ptr(total_out, "total_out", _f64(), allow_none=True),
+                                float(max_norm), _ptr(coef_out, "coef_out", _f32(), min_numel=1),
+                                _ptr(norm_out, "norm_out", _f32(), allow_none=True, min_numel=1),
+                                _ptr(total_out, "total_out", _f64(), allow_none=True, min_numel=1),
                                 _stream(stream)))
 
 
@@ -321,28 +357,36 @@ def shard_adamw_step(plan, owner, master, m, v, g, coef, hp, gathered=None, shar
     bt = _bf16_types()
     if not isinstance(hp, AdamWHP):
         hp = AdamWHP(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step)
-    _check(load().gsz_shard_adamw_step(plan.handle, owner, _ptr(master, "master", _f32()),
-                                       _ptr(m, "m", _f32()), _ptr(v, "v", _f32()),
-                                       _ptr(g, "g", _f32()), _ptr(coef, "coef", _f32()),
+    S = plan.shard_len
+    _check(load().gsz_shard_adamw_step(plan.handle, owner,
+                                       _ptr(master, "master", _f32(), min_numel=S),
+                                       _ptr(m, "m", _f32(), min_numel=S),
+                                       _ptr(v, "v", _f32(), min_numel=S),
+                                       _ptr(g, "g", _f32(), min_numel=S),
+                                       _ptr(coef, "coef", _f32(), min_numel=1),
                                        ctypes.byref(hp),
-                                       _ptr(gathered, "gathered", bt, allow_none=True),
-                                       _ptr(shard_bf16, "shard_bf16", bt, allow_none=True),
+                                       _ptr(gathered, "gathered", bt, allow_none=True,
+                                            min_numel=plan.flat_len),
+                                       _ptr(shard_bf16, "shard_bf16", bt, allow_none=True,
+                                            min_numel=S),
                                        _stream(stream)))
 
 
 def allgather_layout_write(plan, owner, shard_bf16, gathered, stream=None):
     bt = _bf16_types()
-    _check(load().gsz_allgather_layout_write(plan.handle, owner, _ptr(shard_bf16, "shard_bf16", bt),
-                                             _ptr(gathered, "gathered", bt), _stream(stream)))
+    _check(load().gsz_allgather_layout_write(plan.handle, owner,
+                                             _ptr(shard_bf16, "shard_bf16", bt,
+                                                  min_numel=plan.shard_len),
+                                             _ptr(gathered, "gathered", bt,
+                                                  min_numel=plan.flat_len),
+                                             _stream(stream)))
 
 
 def bucket_unpack(plan, flat, params, stream=None):
     bt = _bf16_types()
-    if len(params) != plan.n_tensors:
-        raise ValueError("need one parameter tensor per plan tensor")
-    ptrs = (_P * max(len(params), 1))(*[_ptr(t, f"params[{i}]", bt) if t.numel() else None
-                                        for i, t in enumerate(params)])
-    _check(load().gsz_bucket_unpack(plan.handle, _ptr(flat, "flat", bt), ptrs, _stream(stream)))
+    ptrs = _tensor_ptrs(plan, params, "params")
+    _check(load().gsz_bucket_unpack(plan.handle, _ptr(flat, "flat", bt, min_numel=plan.flat_len),
+                                    ptrs, _stream(stream)))
 
 
 def allreduce_mean(plan, contribs, g_flat, partials=None, ws=None, stream=None):
@@ -351,11 +395,14 @@ def allreduce_mean(plan, contribs, g_flat, partials=None, ws=None, stream=None):
     bt = _bf16_types()
     if len(contribs) != plan.world_size:
         raise ValueError("need one contribution per rank")
-    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", bt) for i, t in enumerate(contribs)])
+    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", bt, min_numel=plan.flat_len)
+                                  for i, t in enumerate(contribs)])
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(load().gsz_allreduce_mean(plan.handle, ptrs, _ptr(g_flat, "g_flat", _f32()),
-                                     _ptr(partials, "partials", _f64(), allow_none=True),
+    _check(load().gsz_allreduce_mean(plan.handle, ptrs,
+                                     _ptr(g_flat, "g_flat", _f32(), min_numel=plan.flat_len),
+                                     _ptr(partials, "partials", _f64(), allow_none=True,
+                                          min_numel=plan.world_size),
                                      wsp, nbytes, _stream(stream)))
 
 
@@ -363,7 +410,9 @@ def adamw_step(master, m, v, g, coef, hp, out_bf16, stream=None):
     bt = _bf16_types()
     if not isinstance(hp, AdamWHP):
         hp = AdamWHP(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step)
-    _check(load().gsz_adamw_step(_ptr(master, "master", _f32()), _ptr(m, "m", _f32()),
-                                 _ptr(v, "v", _f32()), _ptr(g, "g", _f32()), g.numel(),
-                                 _ptr(coef, "coef", _f32()), ctypes.byref(hp),
-                                 _ptr(out_bf16, "out_bf16", bt), _stream(stream)))
+    n = g.numel()
+    _check(load().gsz_adamw_step(_ptr(master, "master", _f32(), min_numel=n),
+                                 _ptr(m, "m", _f32(), min_numel=n),
+                                 _ptr(v, "v", _f32(), min_numel=n), _ptr(g, "g", _f32()), n,
+                                 _ptr(coef, "coef", _f32(), min_numel=1), ctypes.byref(hp),
+                                 _ptr(out_bf16, "out_bf16", bt, min_numel=n), _stream(stream)))

@@ -221,3 +221,102 @@ def test_planner_and_error_text_are_thread_safe():
     for t in threads:
         t.join()
     assert not failures, failures[:3]
+
+
+class _DevStandIn:
+    """Stands in for a device tensor in the binding's host-side checks: it
+    reports a dtype, a length and a device, and has no storage (address 0).  A
+    call whose checks all pass reaches the library with NULL pointers, which it
+    rejects before touching a device."""
+    is_cuda = True
+
+    def __init__(self, n, dtype):
+        self._n, self.dtype = n, dtype
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return 8 if "64" in str(self.dtype) else 4 if "32" in str(self.dtype) else 2
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return 0
+
+
+def test_binding_checks_buffer_sizes_against_the_plan():
+    """The library takes bare device pointers and cannot see buffer lengths; the
+    binding checks every length the plan implies before the call, so a short
+    (or, for per-tensor gradients, mis-sized) buffer is refused on the host
+    instead of being read or written past its end on the GPU."""
+    import torch
+    w = W.tiny()
+    p = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    S, L, P = p.shard_len, p.flat_len, p.world_size
+    bf, f64 = torch.bfloat16, torch.float64
+    D = _DevStandIn
+    f = lambda n: D(n, torch.float32)
+    b = lambda n: D(n, bf)
+    grads = [b(n) for n in w.numel]
+    short = list(grads)
+    short[3] = b(w.numel[3] - 1)
+    long_ = list(grads)
+    long_[5] = b(w.numel[5] + 8)
+
+    # stream=0 (the null stream) keeps torch's device runtime out of the calls
+    def refused(fn, *args, match="elements"):
+        with pytest.raises(ValueError, match=match):
+            fn(*args, stream=0)
+
+    def reaches_library(fn, *args):
+        with pytest.raises(G.GszError):              # NULL pointers: refused by the library
+            fn(*args, stream=0)
+
+    unpack = lambda plan, params, flat, stream: G.bucket_unpack(plan, flat, params, stream=stream)
+    for fn in (G.bucket_pack, G.bucket_accumulate, unpack):
+        refused(fn, p, short, b(L))
+        refused(fn, p, long_, b(L))
+        refused(fn, p, grads, b(L - 1))
+        refused(fn, p, grads[:-1], b(L), match="per plan tensor")
+        reaches_library(fn, p, grads, b(L))
+    for fn in (G.bucket_pack_f32, G.bucket_accumulate_f32):
+        refused(fn, p, grads, f(L - 1))
+        refused(fn, p, short, f(L))
+        reaches_library(fn, p, grads, f(L))
+    for layout, clen in ((G.LAYOUT_BUCKET_FLAT, L), (G.LAYOUT_SHARD_COMPACT, S)):
+        cs = [b(clen)] * P
+        cs_short = [b(clen)] * (P - 1) + [b(clen - 1)]
+        refused(G.shard_reduce_mean, p, 0, cs_short, layout, f(S))
+        refused(G.shard_reduce_mean, p, 0, cs, layout, f(S - 1))
+        refused(G.shard_reduce_mean, p, 0, cs, layout, f(S), D(0, f64))
+        reaches_library(G.shard_reduce_mean, p, 0, cs, layout, f(S))
+        refused(G.shard_reduce_mean_f32, p, 0, [f(clen)] * (P - 1) + [f(clen - 1)], layout, f(S))
+        refused(G.shard_reduce_mean_f32, p, 0, [f(clen)] * P, layout, f(S - 1))
+        reaches_library(G.shard_reduce_mean_f32, p, 0, [f(clen)] * P, layout, f(S))
+    refused(G.allreduce_mean, p, [b(L)] * (P - 1) + [b(L - 1)], f(L))
+    refused(G.allreduce_mean, p, [b(L)] * P, f(L - 1))
+    refused(G.allreduce_mean, p, [b(L)] * P, f(L), D(P - 1, f64))
+    reaches_library(G.allreduce_mean, p, [b(L)] * P, f(L))
+    refused(G.shard_grad_sqnorm, f(10), D(1, f64), D(1024, f64), 11)
+    refused(G.shard_grad_sqnorm, f(10), D(0, f64), D(1024, f64))
+    refused(G.clip_coef, D(P, f64), 1.0, f(0))
+    coef = f(1)
+    for k in range(4):                                # master, m, v, g
+        st = [f(S) for _ in range(4)]
+        st[k] = f(S - 1)
+        refused(G.shard_adamw_step, p, 0, *st, coef, w.hp, b(L))
+    refused(G.shard_adamw_step, p, 0, f(S), f(S), f(S), f(S), f(0), w.hp, b(L))
+    refused(G.shard_adamw_step, p, 0, f(S), f(S), f(S), f(S), coef, w.hp, b(L - 1))
+    refused(G.shard_adamw_step, p, 0, f(S), f(S), f(S), f(S), coef, w.hp, None, b(S - 1))
+    reaches_library(G.shard_adamw_step, p, 0, f(S), f(S), f(S), f(S), coef, w.hp, b(L))
+    refused(G.adamw_step, f(64), f(64), f(63), f(64), coef, w.hp, b(64))
+    refused(G.adamw_step, f(64), f(64), f(64), f(64), coef, w.hp, b(56))
+    reaches_library(G.adamw_step, f(64), f(64), f(64), f(64), coef, w.hp, b(64))
+    refused(G.allgather_layout_write, p, 0, b(S - 1), b(L))
+    refused(G.allgather_layout_write, p, 0, b(S), b(L - 1))
+    reaches_library(G.allgather_layout_write, p, 0, b(S), b(L))
+    # real host tensors of the right sizes are refused for being on the host
+    grads_host = [torch.zeros(n, dtype=bf) for n in w.numel]
+    refused(G.bucket_pack, p, grads_host, torch.zeros(L, dtype=bf), match="device tensor")
