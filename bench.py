@@ -128,18 +128,25 @@ def gpu_step_stats(ev):
     return dict(mean=float(np.mean(t)), median=float(np.median(t)), min=float(np.min(t)))
 
 
-def profile_commands(config):
+def profile_commands(config, trace_dir, fetch_dir, write_dir):
     """The rocprofv3 command lines (run from the repository root) whose output
     the summaries below are made from: a kernel trace of the default bench of
-    a workload, and one counter pass each for FETCH_SIZE and WRITE_SIZE."""
+    a workload, and one counter pass each for FETCH_SIZE and WRITE_SIZE, each
+    writing <dir>/bench_*.csv."""
     bench_args = f"python3 bench.py --config {config} --no-cpu-baseline"
     short = f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline"
-    return {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_c{config} "
+    return {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} "
                      f"-o bench -- {bench_args}",
-            "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmcf_c{config} "
-                     f"-o bench -- {short}",
-            "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmcw_c{config} "
-                     f"-o bench -- {short}"}
+            "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o bench -- {short}",
+            "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o bench -- {short}"}
+
+
+def _raw_dir(csv_path):
+    """The -d directory of the rocprofv3 run that wrote csv_path, relative to
+    the repository root when it lies inside it."""
+    d = os.path.dirname(os.path.abspath(csv_path))
+    rel = os.path.relpath(d, ROOT)
+    return d if rel.startswith("..") else rel
 
 
 def summarize_trace(csv_path, workload, command, out_dir=None):
@@ -403,11 +410,13 @@ def main():
         from synth import workloads as W
         wname = W.by_id(args.config).name
         if args.summarize_trace:
+            d = _raw_dir(args.summarize_trace)
             summarize_trace(args.summarize_trace, wname,
-                            args.command or profile_commands(args.config)["trace"])
+                            args.command or profile_commands(args.config, d, d, d)["trace"])
         if args.summarize_pmc:
             nb = int(args.copy_gib * (1 << 30)) // 16 * 16
-            cmds = profile_commands(args.config)
+            cmds = profile_commands(args.config, None, _raw_dir(args.summarize_pmc[0]),
+                                    _raw_dir(args.summarize_pmc[1]))
             summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], wname,
                           args.command or f"{cmds['fetch']} ; {cmds['write']}", nb)
         return

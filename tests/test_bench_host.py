@@ -94,7 +94,9 @@ def test_committed_profiles_record_the_command_that_made_them():
 
 
 def test_profile_commands_match_the_summary_kinds():
-    c = bench.profile_commands(3)
+    c = bench.profile_commands(3, "t", "f", "w")
     assert "--kernel-trace --stats" in c["trace"] and "--pmc" not in c["trace"]
     assert "--pmc FETCH_SIZE" in c["fetch"] and "--pmc WRITE_SIZE" in c["write"]
+    assert "-d t " in c["trace"] and "-d f " in c["fetch"] and "-d w " in c["write"]
     assert all("--config 3" in v for v in c.values())
+    assert bench._raw_dir(os.path.join(ROOT, "x", "y", "k.csv")) == os.path.join("x", "y")

@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 @pytest.fixture(scope="module")
-def checker(tmp_path_factory):
+def lut_prog(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not found")
     exe = str(tmp_path_factory.mktemp("lut") / "lut_check")
@@ -38,14 +38,14 @@ def run(exe, plans):
     return r.stdout
 
 
-def test_lookup_tables_on_workload_plans(checker):
+def test_lookup_tables_on_workload_plans(lut_prog):
     plans = [(w.world_size, 64, w.bucket_cap_bytes, w.numel)
              for w in (W.by_id(c) for c in (0, 1, 2, 3, 4, 5))]
-    out = run(checker, plans)
+    out = run(lut_prog, plans)
     assert out.split()[1] == "6"
 
 
-def test_lookup_tables_on_random_and_edge_plans(checker):
+def test_lookup_tables_on_random_and_edge_plans(lut_prog):
     rng = np.random.default_rng(77)
     plans = []
     for _ in range(60):
@@ -63,5 +63,5 @@ def test_lookup_tables_on_random_and_edge_plans(checker):
     plans.append((2, 8, 1 << 40, [3, 0, 0, 1 << 26, 0]))
     plans.append((4, 64, 1, [0] * 255 + [700] + [0] * 3 + [1200]))
     plans.append((1, 8, 100, [0] * 300 + [9]))
-    out = run(checker, plans)
+    out = run(lut_prog, plans)
     assert out.split()[1] == str(len(plans))
