@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) into profiles/traffic_<workload>.txt")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("CSV", "TAG"),
+                    help="turn a rocprofv3 counter_collection.csv with any counters into "
+                         "profiles/counters_<TAG>_<workload>.txt")
     ap.add_argument("--command", default="", help="command line recorded in a summary")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
@@ -225,6 +228,27 @@ def summarize_pmc(fetch_csv, write_csv, workload, command, copy_bytes, out_dir=N
     print(path)
 
 
+def summarize_counters(csv_path, workload, command, tag, out_dir=None):
+    """Per-kernel mean per dispatch of every counter in one rocprofv3 counter
+    CSV (any counters), written to profiles/counters_<tag>_<workload>.txt."""
+    import numpy as np
+    names = sorted({r["Counter_Name"] for r in __import__("csv").DictReader(open(csv_path))})
+    by = {n: _pmc_per_dispatch(csv_path, n) for n in names}
+    kernels = sorted({k for n in names for k in by[n]} - {"synth_fill", "torch_fill",
+                                                          "hip_runtime_copy"})
+    out = [f"# rocprofv3 counters per dispatch (mean over dispatches): {workload}", "#",
+           f"# command: {command}", "#",
+           "# " + f"{'kernel':<24} {'dispatches':>10} " + " ".join(f"{n:>32}" for n in names)]
+    for k in kernels:
+        n_disp = max(len(by[n].get(k, [])) for n in names)
+        vals = " ".join(f"{float(np.mean(by[n][k])):>32.4e}" if k in by[n] else f"{'-':>32}"
+                        for n in names)
+        out.append(f"  {k:<24} {n_disp:>10} {vals}")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"counters_{tag}_{workload}.txt")
+    open(path, "w").write("\n".join(out) + "\n")
+    print(path)
+
+
 def read_traffic(kernel, workload, profiles_dir=None):
     """HBM bytes per launch from the committed counter summary, or None if it
     is missing or was taken on a different kernel source."""
@@ -406,6 +430,13 @@ def bench_ddp(args):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        from synth import workloads as W
+        if not args.command:
+            sys.exit("--summarize-counters needs --command (the rocprofv3 command line)")
+        summarize_counters(args.summarize_counters[0], W.by_id(args.config).name, args.command,
+                           args.summarize_counters[1])
+        return
     if args.summarize_trace or args.summarize_pmc:
         from synth import workloads as W
         wname = W.by_id(args.config).name

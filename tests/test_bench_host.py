@@ -100,3 +100,20 @@ def test_profile_commands_match_the_summary_kinds():
     assert "-d t " in c["trace"] and "-d f " in c["fetch"] and "-d w " in c["write"]
     assert all("--config 3" in v for v in c.values())
     assert bench._raw_dir(os.path.join(ROOT, "x", "y", "k.csv")) == os.path.join("x", "y")
+
+
+def test_counter_summary_of_any_counters(tmp_path):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = [(1, "void (anonymous namespace)::k_adamw<false, true>(float*)", "A_sum", 10.0),
+            (1, "void (anonymous namespace)::k_adamw<false, true>(float*)", "B_sum", 1.0),
+            (1, "void (anonymous namespace)::k_adamw<false, true>(float*)", "B_sum", 2.0),
+            (2, "void (anonymous namespace)::k_adamw<false, true>(float*)", "A_sum", 30.0),
+            (2, "void (anonymous namespace)::k_adamw<false, true>(float*)", "B_sum", 5.0),
+            (3, "synth_fill_kernel(int)", "A_sum", 99.0)]
+    src = tmp_path / "c.csv"
+    _write_csv(src, hdr, rows)
+    bench.summarize_counters(str(src), "w", "rocprofv3 --pmc A_sum B_sum -- python3 bench.py --config 3",
+                             "ab", out_dir=str(tmp_path))
+    text = (tmp_path / "counters_ab_w.txt").read_text()
+    body = [l.split() for l in text.splitlines() if not l.startswith("#")]
+    assert body == [["k_adamw", "2", "2.0000e+01", "4.0000e+00"]]   # per-dispatch sums, then means
