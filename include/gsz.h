@@ -21,9 +21,12 @@
  *   "Data Parallelism: From Parameter Server to Ring All-Reduce"
  *
  * Conventions for every call:
- *   - Return value: GSZ_OK (0) or a negative gsz_status.  On error nothing
- *     is enqueued and gsz_last_error() (thread-local) describes the failure.
- *     Arguments are validated before any work is enqueued.
+ *   - Return value: GSZ_OK (0) or a negative gsz_status; gsz_last_error()
+ *     (thread-local) describes the failure.  Arguments are validated before
+ *     any work is enqueued, so an argument error enqueues nothing.  A call
+ *     that issues several launches (a pack over more than 256 tensors, a
+ *     reduce and its norm finalize) and gets GSZ_ERR_HIP from a later launch
+ *     may leave the earlier ones enqueued.
  *   - Sizes are int64_t element counts.  bf16 values travel as uint16_t bit
  *     patterns.
  *   - "device" pointers are HIP device memory owned by the caller; "host"
@@ -142,7 +145,11 @@ int gsz_plan_check(const gsz_plan* plan, uint64_t peer_hash);
 
 /* Copies the plan's device tables to the current device (allocating them
  * there; the plan owns them) and waits for the copy.  Must precede every
- * device call that takes this plan, on the device it will run on. */
+ * device call that takes this plan, on the device it will run on.  A second
+ * upload on the same device does nothing; an upload to another device moves
+ * the tables there.  Not to be called while device calls on the same plan are
+ * being issued from other threads (the plan is otherwise read-only and may be
+ * shared between threads). */
 int gsz_plan_upload(gsz_plan* plan);
 
 /* ------------------------------------------------------------- ledger --- */

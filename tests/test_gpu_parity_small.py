@@ -384,3 +384,31 @@ def test_random_plans_full_step(seed):
     out2 = run_gpu_step(w, plan, None, G.LAYOUT_SHARD_COMPACT, compacts)
     for r in range(P):
         assert_bits(out2["g"][r], out["g"][r], f"{w.name}: compact g owner {r}")
+
+
+def test_binding_refuses_short_device_buffers():
+    """Buffers shorter than the plan implies are refused by the binding before
+    any launch (the library sees bare pointers); the right lengths then run."""
+    w = W.tiny()
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size).upload()
+    S, L, P = plan.shard_len, plan.flat_len, plan.world_size
+    def dev(n, dt=torch.float32):
+        if dt == torch.uint16:                   # bf16 bits, made through int16
+            return torch.zeros(n, dtype=torch.int16, device="cuda").view(torch.uint16)
+        return torch.zeros(n, dtype=dt, device="cuda")
+    grads = [dev(n, torch.uint16) for n in w.numel]
+    with pytest.raises(ValueError, match="elements"):
+        G.bucket_pack(plan, grads, dev(L - 8, torch.uint16))
+    with pytest.raises(ValueError, match="elements"):
+        G.shard_reduce_mean(plan, 0, [dev(S, torch.uint16)] * (P - 1) + [dev(S - 8, torch.uint16)],
+                            G.LAYOUT_SHARD_COMPACT, dev(S))
+    with pytest.raises(ValueError, match="elements"):
+        G.shard_adamw_step(plan, 0, dev(S), dev(S), dev(S - 4), dev(S), dev(1), w.hp,
+                           dev(L, torch.uint16))
+    torch.cuda.synchronize()
+    flat = dev(L, torch.uint16)
+    G.bucket_pack(plan, grads, flat)
+    g = dev(S)
+    G.shard_reduce_mean(plan, 0, [dev(S, torch.uint16)] * P, G.LAYOUT_SHARD_COMPACT, g)
+    torch.cuda.synchronize()
+    assert not host(g).any() and not host(flat).any()
