@@ -85,11 +85,21 @@ extern "C" int gsz_plan_create(const int64_t* numel, int32_t n_tensors, int64_t 
                   (long long)bucket_cap_bytes, world_size, align_elems, GSZ_MAX_RANKS);
         return GSZ_ERR_INVALID_ARG;
     }
-    for (int32_t t = 0; t < n_tensors; ++t)
+    // Sizes and offsets stay far from int64 overflow: at most 2^48 elements in
+    // all (a 70B model has about 2^36), so padded lengths and byte counts fit.
+    const int64_t kMaxTotal = (int64_t)1 << 48;
+    int64_t total = 0;
+    for (int32_t t = 0; t < n_tensors; ++t) {
         if (numel[t] < 0) {
             set_error("gsz_plan_create: tensor %d has negative size %lld", t, (long long)numel[t]);
             return GSZ_ERR_INVALID_ARG;
         }
+        if (numel[t] > kMaxTotal - total) {
+            set_error("gsz_plan_create: tensor sizes add up past 2^48 elements at tensor %d", t);
+            return GSZ_ERR_SIZE;
+        }
+        total += numel[t];
+    }
 
     gsz_plan* p = new (std::nothrow) gsz_plan();
     if (!p) { set_error("gsz_plan_create: out of host memory"); return GSZ_ERR_NO_MEMORY; }

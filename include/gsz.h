@@ -122,7 +122,8 @@ typedef struct gsz_adamw_hp {
  * L = ceil(n / (P*align)) * P*align; rank r owns chunk r (length L/P) of every
  * bucket and its shard is those chunks concatenated in bucket order.
  * Host only (no device call).  *out receives a plan owned by the caller;
- * release it with gsz_plan_destroy.  n_tensors may be 0; sizes may be 0. */
+ * release it with gsz_plan_destroy.  n_tensors may be 0; sizes may be 0.
+ * GSZ_ERR_SIZE if the sizes add up to more than 2^48 elements. */
 int gsz_plan_create(const int64_t* numel, int32_t n_tensors, int64_t bucket_cap_bytes,
                     int32_t world_size, int32_t align_elems, gsz_plan** out);
 

@@ -124,6 +124,13 @@ def test_argument_validation():
         G.Plan([1, -2], 100, 2)
     with pytest.raises(G.GszError):
         G.Plan([1], 100, G.MAX_RANKS + 1)
+    # sizes that would overflow the planner's int64 offsets are refused
+    for sizes in ([1 << 48, 1], [(1 << 62), (1 << 62)], [(1 << 63) - 1]):
+        with pytest.raises(G.GszError) as e:
+            G.Plan(sizes, 100, 2)
+        assert e.value.name == "GSZ_ERR_SIZE"
+    big = G.Plan([1 << 47, 1 << 47], 1 << 40, 8)          # at the limit: a valid plan
+    assert big.n_params == 1 << 48 and big.flat_len == 1 << 48
     p = G.Plan([5], 100, 2)
     with pytest.raises(G.GszError):
         p.bucket(1)
