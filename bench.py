@@ -131,17 +131,24 @@ def gpu_step_stats(ev):
     return dict(mean=float(np.mean(t)), median=float(np.median(t)), min=float(np.min(t)))
 
 
-def profile_commands(config, trace_dir, fetch_dir, write_dir):
+def profile_commands(config, trace_dir, fetch_dir, write_dir, variant="zero"):
     """The rocprofv3 command lines (run from the repository root) whose output
     the summaries below are made from: a kernel trace of the default bench of
     a workload, and one counter pass each for FETCH_SIZE and WRITE_SIZE, each
     writing <dir>/bench_*.csv."""
-    bench_args = f"python3 bench.py --config {config} --no-cpu-baseline"
-    short = f"python3 bench.py --config {config} --steps 3 --warmup 1 --no-cpu-baseline"
+    var = " --variant ddp" if variant == "ddp" else ""
+    bench_args = f"python3 bench.py --config {config}{var} --no-cpu-baseline"
+    short = f"python3 bench.py --config {config}{var} --steps 3 --warmup 1 --no-cpu-baseline"
     return {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} "
                      f"-o bench -- {bench_args}",
             "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o bench -- {short}",
             "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o bench -- {short}"}
+
+
+def profile_name(workload, variant):
+    """Name of a workload's profile summaries: the unsharded (DDP) step gets
+    its own files."""
+    return f"{workload}-ddp" if variant == "ddp" else workload
 
 
 def _raw_dir(csv_path):
@@ -410,9 +417,44 @@ def bench_ddp(args):
     byts = {"bucket_pack": 4 * w.n_params + 2 * (L - w.n_params),
             "allreduce_mean": (2 * P + 4) * L, "clip_coef": 8 * P + 12,
             "adamw_step": 30 * L, "bucket_unpack": 4 * w.n_params}
+    # the all-reduce is P launches (one per chunk owner), pack and unpack one per
+    # 256 tensors, the others one
+    launches = {"bucket_pack": -(-len(w.numel) // 256),
+                "allreduce_mean": P, "clip_coef": 1, "adamw_step": 1,
+                "bucket_unpack": -(-len(w.numel) // 256)}
     kern = {n: dict(ms=per[n], ms_median=float(np.median(samples[n])), ms_min=float(np.min(samples[n])),
-                    bytes=byts[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9) for n in names}
+                    launches=launches[n], bytes=byts[n], GBps=byts[n] / (per[n] * 1e-3) / 1e9)
+            for n in names}
+    for n in names:
+        kern[n]["frac"] = kern[n]["GBps"] / HBM_PEAK_GBPS
+    # roofline: the longer of the all-reduce and the replicated AdamW
+    dom = max(("allreduce_mean", "adamw_step"), key=lambda n: per[n])
+    dom_bytes = byts[dom] / launches[dom]
+    dom_ms = per[dom] / launches[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    kernel_symbol = {"allreduce_mean": "k_allreduce_mean", "adamw_step": "k_adamw"}[dom]
+    roofline = {"bound": "hbm", "kernel": kernel_symbol, "achieved": achieved,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                "traffic": read_traffic(kernel_symbol, profile_name(w.name, "ddp")),
+                "bytes_per_launch": dom_bytes, "ms_per_launch": dom_ms}
     step_gbps = sum(byts.values()) / (ms_step * 1e-3) / 1e9
+    # the plain copy (the practical ceiling and the calibration kernel of the
+    # counter runs), after the timed steps as in the sharded bench
+    from synth import gen
+    nb = int(args.copy_gib * (1 << 30)) // 16 * 16
+    a = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        gen.dev_copy(a, b, nb)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        gen.dev_copy(a, b, nb)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nb / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del a, b
     log(f"[gpu] DDP {w.name}: {ms_step:.3f} ms/step; " + "; ".join(
         f"{n} {kern[n]['ms']:.3f} ms {kern[n]['GBps']:.0f} GB/s" for n in names))
     print(json.dumps({
@@ -424,7 +466,8 @@ def bench_ddp(args):
         "config": {"workload": w.name, "variant": "ddp", "world_size_P": P,
                    "model_params": w.n_params, "step": " + ".join(names)},
         "hbm_GBps": step_gbps, "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
-        "step_ms_gpu": step_gpu, "kernels": kern}),
+        "step_ms_gpu": step_gpu, "copy_ceiling_GBps": copy_gbps, "kernels": kern,
+        "roofline": roofline}),
         flush=True)
 
 
@@ -439,15 +482,16 @@ def main():
         return
     if args.summarize_trace or args.summarize_pmc:
         from synth import workloads as W
-        wname = W.by_id(args.config).name
+        wname = profile_name(W.by_id(args.config).name, args.variant)
         if args.summarize_trace:
             d = _raw_dir(args.summarize_trace)
             summarize_trace(args.summarize_trace, wname,
-                            args.command or profile_commands(args.config, d, d, d)["trace"])
+                            args.command or profile_commands(args.config, d, d, d,
+                                                             args.variant)["trace"])
         if args.summarize_pmc:
             nb = int(args.copy_gib * (1 << 30)) // 16 * 16
             cmds = profile_commands(args.config, None, _raw_dir(args.summarize_pmc[0]),
-                                    _raw_dir(args.summarize_pmc[1]))
+                                    _raw_dir(args.summarize_pmc[1]), args.variant)
             summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], wname,
                           args.command or f"{cmds['fetch']} ; {cmds['write']}", nb)
         return

@@ -100,6 +100,10 @@ def test_profile_commands_match_the_summary_kinds():
     assert "-d t " in c["trace"] and "-d f " in c["fetch"] and "-d w " in c["write"]
     assert all("--config 3" in v for v in c.values())
     assert bench._raw_dir(os.path.join(ROOT, "x", "y", "k.csv")) == os.path.join("x", "y")
+    d = bench.profile_commands(2, "t", "f", "w", variant="ddp")
+    assert all("--config 2 --variant ddp" in v for v in d.values())
+    assert bench.profile_name("gpt-1.3B-P8", "ddp") == "gpt-1.3B-P8-ddp"
+    assert bench.profile_name("gpt-1.3B-P8", "zero") == "gpt-1.3B-P8"
 
 
 def test_counter_summary_of_any_counters(tmp_path):
