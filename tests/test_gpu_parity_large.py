@@ -265,3 +265,88 @@ def test_bf16_rows_full_size_sampled():
     pidx = OI.param_index_of_flat(oplan, OI.flat_pos_of_shard(oplan, 0, idx))
     cs = [OI.values_at(w, W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16, pidx) for q in range(P)]
     assert_bits(gather_dev(g, idx), reduce_mean_bf16_wire(cs, 0), "bf16-wire mean (sampled)")
+
+
+def test_ddp_full_size_sampled():
+    """The unsharded (DDP) step at the 1.3B model's full size, in the launch
+    configuration of `bench.py --variant ddp --config 2`: the all-reduce mean
+    over the P bucket-flat buffers (each chunk summed in the ring order that
+    ends at its owner), the owners' fused norm partials, AdamW over the whole
+    flat buffer and the unpack, checked at sampled flat positions against the
+    oracle recomputed from the same seeded inputs."""
+    w = W.by_id(2)
+    P = w.world_size
+    plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+    oplan = make_plan(w.numel, w.bucket_cap_bytes, P)
+    L = plan.flat_len
+    say(f"[{w.name}] DDP: generating and packing {P} ranks x {w.n_params} gradients")
+    buf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+    flats = []
+    for q in range(P):
+        _, views = GI.rank_grads(w, q, buf)
+        flat = torch.empty(L, dtype=torch.uint16, device="cuda")
+        G.bucket_pack(plan, views, flat)
+        flats.append(flat)
+    torch.cuda.synchronize()
+    del buf, views
+    ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+    parts = torch.zeros(P, dtype=torch.float64, device="cuda")
+    g = torch.empty(L, dtype=torch.float32, device="cuda")
+    say(f"[{w.name}] DDP: all-reduce mean over {P} ranks, L={L}")
+    G.allreduce_mean(plan, flats, g, parts, ws)
+    torch.cuda.synchronize()
+
+    # sampled flat positions: random, plus both ends of every chunk of every bucket
+    rng = np.random.default_rng(7)
+    edges = []
+    for bk in oplan.buckets:
+        for c in range(P):
+            s0 = bk.base + c * bk.chunk
+            edges += [s0, s0 + 1, s0 + bk.chunk - 2, s0 + bk.chunk - 1]
+    fpos = np.unique(np.concatenate([rng.integers(0, L, 1 << 20), np.array(edges, np.int64)]))
+    bases = np.array([bk.base for bk in oplan.buckets], np.int64)
+    chunks = np.array([bk.chunk for bk in oplan.buckets], np.int64)
+    b = np.searchsorted(bases, fpos, side="right") - 1
+    owner = (fpos - bases[b]) // chunks[b]
+    pidx = OI.param_index_of_flat(oplan, fpos)
+    cs = [OI.values_at(w, W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16, pidx) for q in range(P)]
+    g_ref = np.empty(fpos.size, np.float32)
+    for c in range(P):
+        sel = owner == c
+        g_ref[sel] = o_reduce([x[sel] for x in cs], c)
+    assert_bits(gather_dev(g, fpos), g_ref, "DDP g (sampled)")
+
+    # property at full size: partials[c] is the fp64 sum of squares of owner c's chunks
+    got = host(parts)
+    for c in range(P):
+        prop = 0.0
+        for bk in oplan.buckets:
+            x = g[bk.base + c * bk.chunk: bk.base + (c + 1) * bk.chunk].double()
+            prop += float(torch.sum(x * x))
+        assert abs(got[c] - prop) <= 1e-12 * prop, (c, got[c], prop)
+
+    say(f"[{w.name}] DDP: AdamW over the whole flat buffer with coefficient {COEF}, then unpack")
+    del flats, ws
+    torch.cuda.empty_cache()
+    th, m, v = GI.full_state(plan, w)
+    coef = torch.full((1,), float(COEF), dtype=torch.float32, device="cuda")
+    pflat = torch.empty(L, dtype=torch.uint16, device="cuda")
+    G.adamw_step(th, m, v, g, coef, w.hp, pflat)
+    pbuf = torch.empty(w.n_params, dtype=torch.int16, device="cuda").view(torch.uint16)
+    pre = GI.prefix(w.numel)
+    params = [pbuf[s0:s0 + n] for s0, n in zip(pre, w.numel)]
+    G.bucket_unpack(plan, pflat, params)
+    torch.cuda.synchronize()
+    st = [OI.values_at(w, kind, 0, std, mode, pidx) for kind, std, mode in OI.STATE_KINDS]
+    hp = w.hp
+    t1, m1, v1, p1 = o_adamw(st[0], st[1], st[2], g_ref, COEF, hp.lr, hp.beta1, hp.beta2,
+                             hp.eps, hp.weight_decay, hp.step)
+    assert_bits(gather_dev(th, fpos), t1, "DDP master (sampled)")
+    assert_bits(gather_dev(m, fpos), m1, "DDP m (sampled)")
+    assert_bits(gather_dev(v, fpos), v1, "DDP v (sampled)")
+    assert_bits(gather_dev(pflat, fpos), p1, "DDP bf16 flat (sampled)")
+    # unpack: parameter index i of a non-pad sample holds the flat value at its position
+    real = pidx >= 0
+    assert_bits(gather_dev(pbuf, pidx[real]), p1[real], "DDP unpacked parameters (sampled)")
+    del th, m, v, g, pflat, pbuf, params
+    torch.cuda.empty_cache()
