@@ -9,6 +9,14 @@
 
 namespace {
 
+// Loads per group for a compile-time P: the largest divisor of PS up to cap, so
+// that the groups read contributions 0..PS-1 and none past them.
+constexpr int load_group(int ps, int cap) {
+    for (int g = cap < ps ? cap : ps; g > 1; --g)
+        if (ps % g == 0) return g;
+    return 1;
+}
+
 // ---------------------------------------------------------- reduce-mean --
 
 // g[i] = (((c0 + c1) + c2) + ... + c_{P-1}) / P with rp.p[k] = contribution of
@@ -21,8 +29,8 @@ namespace {
 // W16: the partial sum is rounded to bf16 after every addition (a ring whose
 // wire carries bf16 partial sums); the final division stays fp32.  Loads and
 // stores are nontemporal (2% faster at P = 8, 5% at P = 64 than plain ones).
-// This kernel serves P = 32 and 64 and every P that is not a power of two; the
-// powers of two up to 16 run k_reduce_mean_lc below.
+// This kernel serves P > 16 (compile-time P for 24, 32, 64 and 96, its
+// runtime-P loop for the others); P <= 16 runs k_reduce_mean_lc below.
 template <int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
                                                         const int64_t* __restrict__ seg,
@@ -43,7 +51,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
         float a[8];
         if constexpr (PS > 0) {
             // up to 32 loads before their adds (at P = 64 that measured 1.4% faster than 16)
-            constexpr int G = PS < 32 ? PS : 32;
+            constexpr int G = load_group(PS, 32);
+            static_assert(PS % G == 0, "the groups cover exactly the P contributions");
 #pragma unroll
             for (int k0 = 0; k0 < PS; k0 += G) {
                 u32x4 w[G];
@@ -127,7 +136,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int 
         const int64_t off1 = ok1 ? (FLAT ? cur.map(i1) : i1) : 0;
         f32x4 a = zero, b = zero;
         if constexpr (PS > 0) {
-            constexpr int G = PS < 16 ? PS : 16;
+            constexpr int G = load_group(PS, 16);
+            static_assert(PS % G == 0, "the groups cover exactly the P contributions");
 #pragma unroll
             for (int k0 = 0; k0 < PS; k0 += G) {
                 f32x4 w0[G], w1[G];

@@ -127,18 +127,33 @@ int check_owner(const gsz_plan* p, int32_t owner, const char* who) {
 }
 
 // Calls f(std::integral_constant<int, PS>{}) with PS = P for the world sizes that
-// have unrolled kernels and PS = 0 (the runtime-P loop) for every other P.
-template <class F>
+// have unrolled kernels and PS = 0 (the runtime-P loop) for every other P.  The
+// bf16 reduces also unroll P = 3, 6, 24 and 96, where the runtime loop waits
+// for its last (P-1) mod 8 contributions one at a time (measured on two boxes:
+// P = 3 7-9% faster unrolled, P = 6 2-5%, P = 24 1-2%, P = 96 0.5-6.5%; P = 12,
+// 48 and 128 gained nothing); the fp32 reduce keeps the powers of two (unrolled
+// at 48 or more it needs all 256 registers per lane).
+template <bool kBf16 = false, class F>
 void with_static_p(int P, F&& f) {
     switch (P) {
-        case 2: f(std::integral_constant<int, 2>{}); break;
-        case 4: f(std::integral_constant<int, 4>{}); break;
-        case 8: f(std::integral_constant<int, 8>{}); break;
-        case 16: f(std::integral_constant<int, 16>{}); break;
-        case 32: f(std::integral_constant<int, 32>{}); break;
-        case 64: f(std::integral_constant<int, 64>{}); break;
-        default: f(std::integral_constant<int, 0>{}); break;
+        case 2: f(std::integral_constant<int, 2>{}); return;
+        case 4: f(std::integral_constant<int, 4>{}); return;
+        case 8: f(std::integral_constant<int, 8>{}); return;
+        case 16: f(std::integral_constant<int, 16>{}); return;
+        case 32: f(std::integral_constant<int, 32>{}); return;
+        case 64: f(std::integral_constant<int, 64>{}); return;
+        default: break;
     }
+    if constexpr (kBf16) {
+        switch (P) {
+            case 3: f(std::integral_constant<int, 3>{}); return;
+            case 6: f(std::integral_constant<int, 6>{}); return;
+            case 24: f(std::integral_constant<int, 24>{}); return;
+            case 96: f(std::integral_constant<int, 96>{}); return;
+            default: break;
+        }
+    }
+    f(std::integral_constant<int, 0>{});
 }
 
 // Launches k_reduce_mean<PS, ...> with the flags as template arguments (the
@@ -173,7 +188,7 @@ void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPt
 }
 
 // The lane-contiguous reduce (k_reduce_mean_lc) for bf16 contributions at
-// P <= kLcMaxP (compile-time P for the powers of two, its runtime-P loop for
+// P <= kLcMaxP (compile-time P for 2, 3, 4, 6, 8 and 16, its runtime-P loop for
 // the others) and for fp32 contributions at every P.
 constexpr int kLcMaxP = 16;
 
@@ -418,15 +433,22 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         const uint64_t* slut = p->d_seg_lut;
         const int sshift = p->seg_lut.shift;
         double* wsd = static_cast<double*>(ws);
-        with_static_p(P, [&](auto ps) {
+        with_static_p<true>(P, [&](auto ps) {
             constexpr int PS = decltype(ps)::value;
-            if (PS > 0 ? PS <= kLcMaxP : P <= kLcMaxP)
-                launch_reduce_lc<uint16_t, PS <= kLcMaxP ? PS : 0>(
+            auto lc = [&](auto pc) {
+                launch_reduce_lc<uint16_t, decltype(pc)::value>(
                     norm, flat, false, wire16, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
                     sshift, owner, S, g, wsd);
-            else
-                launch_reduce<PS>(norm, flat, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
-                                  sshift, owner, nvec, g, wsd, false, wire16);
+            };
+            auto wide = [&](auto pc) {
+                launch_reduce<decltype(pc)::value>(norm, flat, dim3(grid), stream, rp, P, invP, pow2,
+                                                   p->d_seg, slut, sshift, owner, nvec, g, wsd,
+                                                   false, wire16);
+            };
+            if constexpr (PS > kLcMaxP) wide(ps);
+            else if constexpr (PS > 0) lc(ps);
+            else if (P <= kLcMaxP) lc(ps);
+            else wide(ps);
         });
         if ((rc = launched(who))) return rc;
     }
@@ -596,15 +618,21 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
     for (int c = 0; c < P; ++c) {
         RankPtrs rp{};
         for (int k = 0; k < P; ++k) rp.p[k] = contrib[(c + 1 + k) % P];
-        with_static_p(P, [&](auto ps) {
+        with_static_p<true>(P, [&](auto ps) {
             constexpr int PS = decltype(ps)::value;
-            if (PS > 0 ? PS <= kLcMaxP : P <= kLcMaxP)
-                launch_reduce_lc<uint16_t, PS <= kLcMaxP ? PS : 0>(
+            auto lc = [&](auto pc) {
+                launch_reduce_lc<uint16_t, decltype(pc)::value>(
                     norm, true, true, false, gr, stream, rp, P, invP, pow2, p->d_seg, slut, sshift, c,
                     S, g_flat, wsd);
-            else
-                launch_reduce<PS>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg, slut, sshift,
-                                  c, nvec, g_flat, wsd, true);
+            };
+            auto wide = [&](auto pc) {
+                launch_reduce<decltype(pc)::value>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg,
+                                                   slut, sshift, c, nvec, g_flat, wsd, true);
+            };
+            if constexpr (PS > kLcMaxP) wide(ps);
+            else if constexpr (PS > 0) lc(ps);
+            else if (P <= kLcMaxP) lc(ps);
+            else wide(ps);
         });
         if ((rc = launched(who))) return rc;
         if (norm) {

@@ -117,12 +117,12 @@ def test_adamw_step_rejects_ragged_sizes():
     assert e.value.name == "GSZ_ERR_SIZE"
 
 
-@pytest.mark.parametrize("P", [3, 6, 12, 24, 32])
+@pytest.mark.parametrize("P", [3, 6, 12, 24, 32, 96])
 def test_allreduce_every_kernel_family(P):
-    """The all-reduce at world sizes that run the lane-contiguous kernel's
-    runtime-P loop (3, 6, 12), the 16-byte kernel's runtime-P loop (24) and its
-    compile-time P (32), against the message-passing ring, with the chunk
-    owners' norm partials."""
+    """The all-reduce at world sizes that run each kernel form: the
+    lane-contiguous kernel with compile-time P (3, 6) and its runtime-P loop
+    (12), the 16-byte kernel with compile-time P (24, 32, 96), against the
+    message-passing ring, with the chunk owners' norm partials."""
     from oracle.bf16 import narrow
     from oracle.reduce import ring_allreduce_sim
     rng = np.random.default_rng(900 + P)

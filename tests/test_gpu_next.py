@@ -202,11 +202,12 @@ def test_fp32_accumulation_unaligned_sources():
     assert_bits(host(flat), want, "unaligned fp32 accumulation")
 
 
-@pytest.mark.parametrize("P", [3, 6, 12, 24, 64])
+@pytest.mark.parametrize("P", [3, 6, 12, 24, 64, 96, 100])
 def test_bf16_wire_every_kernel_family(P):
-    """The bf16-wire reduce at world sizes that run the lane-contiguous kernel's
-    runtime-P loop (3, 6, 12), the 16-byte kernel's runtime-P loop (24) and its
-    compile-time P (64), both layouts, against the oracle's bf16-wire ring."""
+    """The bf16-wire reduce at world sizes that run each kernel form: the
+    lane-contiguous kernel with compile-time P (3, 6) and its runtime-P loop
+    (12), the 16-byte kernel with compile-time P (24, 64, 96) and its runtime-P
+    loop (100), both layouts, against the oracle's bf16-wire ring."""
     from oracle.bf16 import narrow
     rng = np.random.default_rng(700 + P)
     numel = [int(x) for x in rng.integers(1, 4000, 7)]

@@ -165,7 +165,7 @@ def test_clip_kernel_against_oracle_on_given_partials():
         assert gn == n32 and gc == c32, (parts, gn, n32, gc, c32)
 
 
-@pytest.mark.parametrize("P", [1, 2, 3, 5, 6, 12, 16, 32, 64, 100, 256])
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 6, 12, 16, 24, 32, 64, 96, 100, 256])
 def test_reduce_every_rank_count(P):
     """Static-P kernels (2..64) and the dynamic-P kernel (1, 3, 5, 6, 12, 100,
     and 256 = the largest world size, a full pointer table), power-of-two and
