@@ -327,3 +327,27 @@ def test_binding_checks_buffer_sizes_against_the_plan():
     # real host tensors of the right sizes are refused for being on the host
     grads_host = [torch.zeros(n, dtype=bf) for n in w.numel]
     refused(G.bucket_pack, p, grads_host, torch.zeros(L, dtype=bf), match="device tensor")
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With libgsz.so absent the package refuses to import: there is no CPU
+    fallback.  A copy of the package without the library is imported in a
+    fresh process."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "gradient_sync_zero_amd"
+    pkg.mkdir()
+    src = os.path.dirname(G.LIB_PATH)
+    for name in ("__init__.py", "_binding.py"):
+        shutil.copy(os.path.join(src, name), pkg / name)
+    code = ("try:\n"
+            "    import gradient_sync_zero_amd as G\n"
+            "except ImportError as e:\n"
+            "    print('refused:', e)\n"
+            "else:\n"
+            "    print('ran without the library')\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=str(tmp_path), capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.startswith("refused:") and "no fallback" in out.stdout, out.stdout
