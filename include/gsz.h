@@ -197,9 +197,9 @@ int gsz_bucket_pack(const gsz_plan* plan, const uint16_t* const* grads, uint16_t
  * with c[q] the bf16 value rank q contributes for element i of owner r's shard
  * (indices mod P); each addition is an IEEE fp32 add, the division is exact
  * IEEE division.  This is the reduce-scatter of "Data Parallelism: From
- * Parameter Server to Ring All-Reduce" §5 (the received chunk is added into
- * the local partial sum; after N-1 steps the owner holds the reduced chunk),
- * averaged as in "Data parallelism in depth" §2, accumulated in fp32 as in
+ * Parameter Server to Ring All-Reduce" §5 (chunk c's partial sum starts at
+ * rank c+1 and takes one fp32 addition per hop around the ring, ending at its
+ * owner c), averaged as in "Data parallelism in depth" §2, accumulated in fp32 as in
  * "Distributed Training ...", section FSDP1 vs FSDP2 (reduce_dtype=fp32).
  *   contrib (host array of P device pointers), layout GSZ_LAYOUT_*.
  *   g (device, S fp32): written.

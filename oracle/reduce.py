@@ -5,12 +5,13 @@ Followed passages:
     gradient is the average (1/N) sum_k g_k of the per-rank gradients, not
     their sum (a sum would scale the learning rate by N).
   * "Data Parallelism: From Parameter Server to Ring All-Reduce" §1 (The
-    Contract): G = sum_i G_i / N on every rank; §5 (Ring All-Reduce =
-    Reduce-Scatter + All-Gather): at each step every rank sends one chunk to its
-    clockwise neighbour, the received chunk is added into a local partial sum,
-    and after N-1 steps every rank owns one fully reduced chunk; the all-gather
-    then forwards reduced chunks for N-1 more steps.  Per-rank send volume is
-    (N-1)*M/N per phase, 2*(N-1)/N*M in total.
+    Contract): every rank ends with the same G, the sum of the N rank
+    gradients divided by N; §5 (Ring All-Reduce = Reduce-Scatter +
+    All-Gather): the buffer is cut into N chunks; chunk c's fp32 partial sum
+    starts at one rank, moves one neighbour per step and takes one addition at
+    each hop, so after N-1 steps it is complete at the rank that owns c; the
+    all-gather phase then circulates the finished chunks for N-1 more steps.
+    Each rank sends (N-1)/N of the buffer per phase, 2(N-1)/N of it in all.
   * "Data parallelism in depth" §5.1-§5.2: AllReduce = ReduceScatter +
     AllGather, per-GPU volume 2*Psi*(N-1)/N.
   * "Distributed Training: Data Parallel, Model Parallel and FSDP Strategies",

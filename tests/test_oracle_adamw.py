@@ -78,9 +78,20 @@ def test_matches_torch_adamw(gstd, coef, vscale, foreach):
     c = np.float32(coef)
     th1, m1, v1, p = run(th, m, v, g, c)
     tth, tm, tv = torch_adamw(th, m, v, g, c, foreach=foreach)
-    np.testing.assert_allclose(m1, tm, rtol=2.5e-7, atol=5e-11)
-    np.testing.assert_allclose(v1, tv, rtol=3e-7, atol=1e-20)
-    np.testing.assert_allclose(th1, tth, rtol=1e-6, atol=2e-8)
+    assert torch_pin_ok((th1, m1, v1), (tth, tm, tv))
+
+
+# The pin's tolerances (absolute plus relative: torch orders the operations
+# differently, so it fixes the formula, not each rounding).  The planted
+# mistakes below are judged with these same tolerances.
+PIN_TOL = {"m": dict(rtol=2.5e-7, atol=5e-11), "v": dict(rtol=3e-7, atol=1e-20),
+           "theta": dict(rtol=1e-6, atol=2e-8)}
+
+
+def torch_pin_ok(ours, theirs):
+    """True if (theta, m, v) agree with torch's AdamW within the pin's tolerances."""
+    return all(np.allclose(a, b, **PIN_TOL[k])
+               for k, a, b in zip(("theta", "m", "v"), ours, theirs))
 
 
 def _mutant(monkeypatch, kind):
@@ -101,6 +112,15 @@ def _mutant(monkeypatch, kind):
         if kind == "l2_not_decoupled":
             return real(theta, m, v, g + f(weight_decay) * theta, coef, lr, beta1, beta2, eps,
                         0.0, step)
+        if kind == "bias_exponent_off_by_one":
+            bc1, bc2 = f(1 - beta1 ** (step - 1)), f(1 - beta2 ** (step - 1))
+            u = (m1 / bc1) / (np.sqrt(v1 / bc2) + f(eps))
+        if kind == "no_clip":
+            return real(theta, m, v, g, 1.0, lr, beta1, beta2, eps, weight_decay, step)
+        if kind == "betas_swapped":
+            m1 = f(beta2) * m + f(1 - beta2) * gc
+            v1 = f(beta1) * v + f(1 - beta1) * gc * gc
+            u = (m1 / bc1) / (np.sqrt(v1 / bc2) + f(eps))
         if kind == "decay_sign":
             th = theta * f(1 + lr * weight_decay) - f(lr) * u
         else:
@@ -110,7 +130,8 @@ def _mutant(monkeypatch, kind):
 
 
 @pytest.mark.parametrize("kind", ["no_bias_correction", "eps_inside_sqrt", "l2_not_decoupled",
-                                  "decay_sign"])
+                                  "decay_sign", "bias_exponent_off_by_one", "no_clip",
+                                  "betas_swapped"])
 def test_planted_mistakes_fail_the_torch_pin(kind, monkeypatch):
     th, m, v, g = state(20000, seed=9)
     v = (v * np.float32(1e-4)).astype(np.float32)      # small v so eps matters
@@ -118,9 +139,8 @@ def test_planted_mistakes_fail_the_torch_pin(kind, monkeypatch):
     bad = _mutant(monkeypatch, kind)(th, m, v, g, c, HP.lr, HP.beta1, HP.beta2, HP.eps,
                                      HP.weight_decay, HP.step)
     tth, tm, tv = torch_adamw(th, m, v, g, c)
-    ok = (np.allclose(bad[1], tm, rtol=2.5e-7, atol=5e-11) and np.allclose(bad[2], tv, rtol=3e-7, atol=1e-20)
-          and np.allclose(bad[0], tth, rtol=0, atol=2e-8))
-    assert not ok
+    assert torch_pin_ok(run(th, m, v, g, c)[:3], (tth, tm, tv))    # the real update passes here
+    assert not torch_pin_ok(bad[:3], (tth, tm, tv))
 
 
 def test_bf16_output_is_rne_of_theta():

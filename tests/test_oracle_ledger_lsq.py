@@ -56,13 +56,3 @@ def test_mean_of_shard_gradients_is_the_full_batch_gradient():
         g = reduce_mean(contribs, r)
         assert [Fraction(float(x)) for x in g] == full
 
-
-def test_gradient_mean_real_valued():
-    rng = np.random.default_rng(8)
-    X = rng.normal(size=(64, 4))
-    theta = rng.normal(size=4)
-    Y = rng.normal(size=64)
-    r = X @ theta - Y
-    full = (r[:, None] * X).mean(axis=0)
-    gk = [(r[k * 16:(k + 1) * 16, None] * X[k * 16:(k + 1) * 16]).mean(axis=0) for k in range(4)]
-    np.testing.assert_allclose(np.mean(gk, axis=0), full, rtol=1e-12, atol=1e-14)
