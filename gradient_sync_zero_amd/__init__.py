@@ -10,7 +10,8 @@ from ._binding import (AdamWHP, GszError, LAYOUT_BUCKET_FLAT, LAYOUT_SHARD_COMPA
                        bucket_accumulate, bucket_accumulate_f32, bucket_pack, bucket_pack_f32,
                        bucket_unpack, clip_coef, load, ledger_bytes_per_param, make_hp,
                        shard_adamw_step, shard_grad_sqnorm, shard_reduce_mean,
-                       set_grid_limit, shard_reduce_mean_f32, workspace_bytes)
+                       set_grid_limit, shard_reduce_mean_f32, test_hooks, workspace_bytes)
+from . import _binding
 
 load()
 
@@ -19,4 +20,4 @@ __all__ = ["AdamWHP", "GszError", "LAYOUT_BUCKET_FLAT", "LAYOUT_SHARD_COMPACT", 
            "bucket_accumulate", "bucket_accumulate_f32", "bucket_pack", "bucket_pack_f32",
            "bucket_unpack", "clip_coef", "ledger_bytes_per_param", "make_hp", "set_grid_limit",
            "shard_adamw_step", "shard_grad_sqnorm", "shard_reduce_mean", "shard_reduce_mean_f32",
-           "workspace_bytes"]
+           "test_hooks", "workspace_bytes"]

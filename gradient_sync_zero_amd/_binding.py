@@ -7,11 +7,16 @@ library is missing or a call fails, an exception is raised.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
+import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgsz.so")
+# The same sources built with the test hooks (include/gsz_test.h): used only
+# inside test_hooks().
+TEST_LIB_PATH = os.path.join(_HERE, "libgsz_test.so")
 
 LAYOUT_BUCKET_FLAT = 0
 LAYOUT_SHARD_COMPACT = 1
@@ -60,10 +65,10 @@ _SIGS = {
     "gsz_plan_bucket": [_P, _I32, ctypes.POINTER(BucketInfo)],
     "gsz_plan_tensor": [_P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I32)],
     "gsz_plan_check": [_P, ctypes.c_uint64],
-    "gsz_plan_upload": [_P],
+    "gsz_plan_device_bytes": [_P, ctypes.POINTER(ctypes.c_size_t)],
+    "gsz_plan_upload": [_P, _P, ctypes.c_size_t, _P],
     "gsz_ledger_bytes_per_param": [_I32, _I32, ctypes.POINTER(ctypes.c_double)],
     "gsz_workspace_bytes": [ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)],
-    "gsz_set_grid_limit": [ctypes.c_int64],
     "gsz_bucket_pack": [_P, _P, _P, _P],
     "gsz_shard_reduce_mean": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_shard_grad_sqnorm": [_P, _I64, _P, _P, ctypes.c_size_t, _P],
@@ -80,25 +85,32 @@ _SIGS = {
     "gsz_adamw_step": [_P, _P, _P, _P, _I64, _P, ctypes.POINTER(AdamWHP), _P, _P],
 }
 
-_lib = None
+_TEST_SIGS = {"gsz_test_set_grid_limit": [ctypes.c_int64]}
+
+_libs = {}
+_active = threading.local()
 
 
-def load():
-    """Loads libgsz.so (raises if it is not built).
+def load(path=None):
+    """Loads a build of libgsz (default: the one calls go to in this thread,
+    libgsz.so outside test_hooks()); raises if it is not built.
 
     torch is imported first, on purpose: torch ships its own HIP runtime with
     the same soname (libamdhip64.so.7) but asks for it as libamdhip64.so, so if
     libgsz pulled in /opt/rocm's copy first, the process would hold two HIP
     runtimes and torch's would find no GPU.  With torch loaded first, libgsz's
     dependency resolves to the runtime torch already loaded."""
-    global _lib
-    if _lib is None:
+    if path is None:
+        path = getattr(_active, "path", LIB_PATH)
+    lib = _libs.get(path)
+    if lib is None:
         import torch  # noqa: F401  (load order; see above)
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: the HIP library is not built "
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: the HIP library is not built "
                               "(run __graft_entry__.build()); there is no fallback")
-        lib = ctypes.CDLL(LIB_PATH)
-        for name, args in _SIGS.items():
+        lib = ctypes.CDLL(path)
+        sigs = dict(_SIGS, **(_TEST_SIGS if path == TEST_LIB_PATH else {}))
+        for name, args in sigs.items():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
@@ -106,13 +118,37 @@ def load():
         lib.gsz_last_error.restype = ctypes.c_char_p
         lib.gsz_status_string.argtypes = [ctypes.c_int]
         lib.gsz_status_string.restype = ctypes.c_char_p
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return lib
 
 
-def _check(rc: int):
+@contextlib.contextmanager
+def test_hooks():
+    """Within the block, calls made by this thread go to libgsz_test.so, the
+    same sources built with the test hooks (set_grid_limit).  Plans keep the
+    library they were created with, so create them inside the block."""
+    load(TEST_LIB_PATH)
+    prev = getattr(_active, "path", LIB_PATH)
+    _active.path = TEST_LIB_PATH
+    try:
+        yield
+    finally:
+        _active.path = prev
+
+
+def _check(rc: int, lib=None):
     if rc != 0:
-        raise GszError(rc, load().gsz_last_error().decode())
+        lib = lib or load()
+        raise GszError(rc, lib.gsz_last_error().decode())
+
+
+def _lib_for(plan):
+    """The library a plan was created with; it must be the one calls go to."""
+    lib = load()
+    if plan._lib is not lib:
+        raise ValueError("this plan was created with another build of libgsz "
+                         "(inside or outside test_hooks())")
+    return lib
 
 
 def _stream(stream):
@@ -178,6 +214,8 @@ class Plan:
 
     def __init__(self, numel, bucket_cap_bytes, world_size, align=64):
         lib = load()
+        self._lib = lib
+        self._tables = None
         n = len(numel)
         self.numel = [int(x) for x in numel]
         arr = (_I64 * max(n, 1))(*self.numel)
@@ -203,7 +241,7 @@ class Plan:
 
     def bucket(self, b):
         out = BucketInfo()
-        _check(load().gsz_plan_bucket(self._h, b, ctypes.byref(out)))
+        _check(self._lib.gsz_plan_bucket(self._h, b, ctypes.byref(out)), self._lib)
         return {f: getattr(out, f) for f, _ in BucketInfo._fields_}
 
     def buckets(self):
@@ -211,19 +249,31 @@ class Plan:
 
     def tensor(self, t):
         off, b = _I64(), _I32()
-        _check(load().gsz_plan_tensor(self._h, t, ctypes.byref(off), ctypes.byref(b)))
+        _check(self._lib.gsz_plan_tensor(self._h, t, ctypes.byref(off), ctypes.byref(b)), self._lib)
         return off.value, b.value
 
     def check(self, peer_hash):
-        _check(load().gsz_plan_check(self._h, ctypes.c_uint64(peer_hash)))
+        _check(self._lib.gsz_plan_check(self._h, ctypes.c_uint64(peer_hash)), self._lib)
 
-    def upload(self):
-        _check(load().gsz_plan_upload(self._h))
+    def device_bytes(self):
+        out = ctypes.c_size_t()
+        _check(self._lib.gsz_plan_device_bytes(self._h, ctypes.byref(out)), self._lib)
+        return out.value
+
+    def upload(self, stream=None):
+        """Copies the device tables into a device buffer this object owns (a
+        torch allocation on the current device), on the current stream."""
+        import torch
+        nbytes = self.device_bytes()
+        tables = torch.empty((nbytes + 15) // 16 * 2, dtype=torch.int64, device="cuda")
+        _check(self._lib.gsz_plan_upload(self._h, tables.data_ptr(), tables.numel() * 8,
+                                         _stream(stream)), self._lib)
+        self._tables = tables
         return self
 
     def close(self):
         if getattr(self, "_h", None):
-            load().gsz_plan_destroy(self._h)
+            self._lib.gsz_plan_destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -248,22 +298,27 @@ def workspace_bytes(n):
 
 
 def set_grid_limit(max_blocks):
-    """Caps the blocks of every later data-sized launch, process-wide (0 restores
-    the built-in caps); blocks then stride over several tiles."""
-    _check(load().gsz_set_grid_limit(int(max_blocks)))
+    """Test build only (inside test_hooks()): caps the blocks of every later
+    data-sized launch, process-wide (0 restores the built-in caps); blocks then
+    stride over several tiles."""
+    lib = load()
+    if not hasattr(lib, "gsz_test_set_grid_limit") or lib is not _libs.get(TEST_LIB_PATH):
+        raise RuntimeError("set_grid_limit exists only in the test build; call it inside "
+                           "test_hooks()")
+    _check(lib.gsz_test_set_grid_limit(int(max_blocks)), lib)
 
 
 def bucket_pack(plan, grads, flat, stream=None):
     bt = _bf16_types()
     ptrs = _tensor_ptrs(plan, grads, "grads")
-    _check(load().gsz_bucket_pack(plan.handle, ptrs,
+    _check(_lib_for(plan).gsz_bucket_pack(plan.handle, ptrs,
                                   _ptr(flat, "flat", bt, min_numel=plan.flat_len), _stream(stream)))
 
 
 def bucket_accumulate(plan, grads, flat, stream=None):
     bt = _bf16_types()
     ptrs = _tensor_ptrs(plan, grads, "grads")
-    _check(load().gsz_bucket_accumulate(plan.handle, ptrs,
+    _check(_lib_for(plan).gsz_bucket_accumulate(plan.handle, ptrs,
                                         _ptr(flat, "flat", bt, min_numel=plan.flat_len),
                                         _stream(stream)))
 
@@ -286,14 +341,14 @@ def _grad_ptrs(plan, grads):
 
 def bucket_pack_f32(plan, grads, flat32, stream=None):
     """First micro-batch of an fp32 accumulation window: flat32 = f32(grads), pads 0."""
-    _check(load().gsz_bucket_pack_f32(plan.handle, _grad_ptrs(plan, grads),
+    _check(_lib_for(plan).gsz_bucket_pack_f32(plan.handle, _grad_ptrs(plan, grads),
                                       _ptr(flat32, "flat32", _f32(), min_numel=plan.flat_len),
                                       _stream(stream)))
 
 
 def bucket_accumulate_f32(plan, grads, flat32, stream=None):
     """Later micro-batches: flat32 += f32(grads) (fp32 adds)."""
-    _check(load().gsz_bucket_accumulate_f32(plan.handle, _grad_ptrs(plan, grads),
+    _check(_lib_for(plan).gsz_bucket_accumulate_f32(plan.handle, _grad_ptrs(plan, grads),
                                             _ptr(flat32, "flat32", _f32(), min_numel=plan.flat_len),
                                             _stream(stream)))
 
@@ -307,7 +362,7 @@ def shard_reduce_mean_f32(plan, owner, contribs, layout, g, partial_out=None, ws
                                   for i, t in enumerate(contribs)])
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(load().gsz_shard_reduce_mean_f32(plan.handle, owner, ptrs, layout,
+    _check(_lib_for(plan).gsz_shard_reduce_mean_f32(plan.handle, owner, ptrs, layout,
                                             _ptr(g, "g", _f32(), min_numel=plan.shard_len),
                                             _ptr(partial_out, "partial_out", _f64(),
                                                  allow_none=True,
@@ -326,7 +381,8 @@ def shard_reduce_mean(plan, owner, contribs, layout, g, partial_out=None, ws=Non
                                   for i, t in enumerate(contribs)])
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
-    fn = load().gsz_shard_reduce_mean_bf16_wire if bf16_wire else load().gsz_shard_reduce_mean
+    lib = _lib_for(plan)
+    fn = lib.gsz_shard_reduce_mean_bf16_wire if bf16_wire else lib.gsz_shard_reduce_mean
     _check(fn(plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32(), min_numel=plan.shard_len),
               _ptr(partial_out, "partial_out", _f64(), allow_none=True, min_numel=1),
               wsp, nbytes, _stream(stream)))
@@ -358,7 +414,7 @@ def shard_adamw_step(plan, owner, master, m, v, g, coef, hp, gathered=None, shar
     if not isinstance(hp, AdamWHP):
         hp = AdamWHP(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step)
     S = plan.shard_len
-    _check(load().gsz_shard_adamw_step(plan.handle, owner,
+    _check(_lib_for(plan).gsz_shard_adamw_step(plan.handle, owner,
                                        _ptr(master, "master", _f32(), min_numel=S),
                                        _ptr(m, "m", _f32(), min_numel=S),
                                        _ptr(v, "v", _f32(), min_numel=S),
@@ -374,7 +430,7 @@ def shard_adamw_step(plan, owner, master, m, v, g, coef, hp, gathered=None, shar
 
 def allgather_layout_write(plan, owner, shard_bf16, gathered, stream=None):
     bt = _bf16_types()
-    _check(load().gsz_allgather_layout_write(plan.handle, owner,
+    _check(_lib_for(plan).gsz_allgather_layout_write(plan.handle, owner,
                                              _ptr(shard_bf16, "shard_bf16", bt,
                                                   min_numel=plan.shard_len),
                                              _ptr(gathered, "gathered", bt,
@@ -385,7 +441,7 @@ def allgather_layout_write(plan, owner, shard_bf16, gathered, stream=None):
 def bucket_unpack(plan, flat, params, stream=None):
     bt = _bf16_types()
     ptrs = _tensor_ptrs(plan, params, "params")
-    _check(load().gsz_bucket_unpack(plan.handle, _ptr(flat, "flat", bt, min_numel=plan.flat_len),
+    _check(_lib_for(plan).gsz_bucket_unpack(plan.handle, _ptr(flat, "flat", bt, min_numel=plan.flat_len),
                                     ptrs, _stream(stream)))
 
 
@@ -399,7 +455,7 @@ def allreduce_mean(plan, contribs, g_flat, partials=None, ws=None, stream=None):
                                   for i, t in enumerate(contribs)])
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(load().gsz_allreduce_mean(plan.handle, ptrs,
+    _check(_lib_for(plan).gsz_allreduce_mean(plan.handle, ptrs,
                                      _ptr(g_flat, "g_flat", _f32(), min_numel=plan.flat_len),
                                      _ptr(partials, "partials", _f64(), allow_none=True,
                                           min_numel=plan.world_size),

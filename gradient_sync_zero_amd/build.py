@@ -9,6 +9,8 @@ _ROOT = os.path.dirname(_HERE)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 LIB = os.path.join(_HERE, "libgsz.so")
+# The same sources with the test hooks of include/gsz_test.h compiled in.
+TEST_LIB = os.path.join(_HERE, "libgsz_test.so")
 
 # -ffp-contract=off: the AdamW update and the fp32 reduction must keep one
 # rounding per operation (no fused multiply-add).  Packed fp32 instructions are
@@ -24,12 +26,18 @@ SOURCES = ["csrc/plan.cpp", "csrc/gsz_step.hip"]
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True, cwd=_HERE)
-    os.replace(tmp, LIB)
+    """Builds libgsz.so and libgsz_test.so side by side (two hipcc processes)."""
+    jobs = []
+    for out, extra in ((LIB, []), (TEST_LIB, ["-DGSZ_TEST_HOOKS"])):
+        cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((out, cmd, subprocess.Popen(cmd, cwd=_HERE)))
+    failed = [cmd for _, cmd, proc in jobs if proc.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    for out, _, _ in jobs:
+        os.replace(out + ".tmp", out)
     return LIB
 
 

@@ -74,10 +74,16 @@ struct gsz_plan {
     // position (over pack).
     gsz::Lut seg_lut, pack_lut;
 
-    // Device tables (one allocation) and the device they live on.
+    // The device tables as one image of 8-byte slots, built with the plan:
+    // seg, pack and pads rows (int64), then the two lookup tables (a {lo, hi}
+    // pair of int32 per cell, one slot each), then 2 spare slots.  The caller
+    // copies it into device memory it owns (gsz_plan_upload); the plan keeps the
+    // image for as long as it lives, so that copy may complete asynchronously.
+    std::vector<int64_t> image;
+
+    // Where the image was last uploaded: the device and the caller's buffer.
     std::mutex mu;
     int device = -1;
-    void* dev_mem = nullptr;
     const int64_t* d_seg = nullptr;
     const int64_t* d_pack = nullptr;
     const int64_t* d_pads = nullptr;

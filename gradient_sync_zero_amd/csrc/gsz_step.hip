@@ -51,14 +51,22 @@ int current_device(int* dev_out) {
     return GSZ_OK;
 }
 
-// Process-wide cap on the blocks of grid-sized launches (0: the built-in caps).
+#ifdef GSZ_TEST_HOOKS
+// Test builds only (libgsz_test.so, include/gsz_test.h): a process-wide cap on
+// the blocks of grid-sized launches (0: the built-in caps), so that tests can
+// run the block-striding path that otherwise only inputs of more than about
+// 17e9 elements reach.  The product library has no such state.
 std::atomic<int64_t> g_grid_limit{0};
+#endif
 
 // Blocks of a one-tile-per-block launch over n_tiles tiles: at most `builtin`
-// (the dispatch limit for the kernel's block size) and the caller's cap.
+// (the dispatch limit for the kernel's block size).
 int tile_grid(int64_t n_tiles, int64_t builtin) {
+    int64_t cap = builtin;
+#ifdef GSZ_TEST_HOOKS
     const int64_t lim = g_grid_limit.load(std::memory_order_relaxed);
-    const int64_t cap = lim > 0 && lim < builtin ? lim : builtin;
+    if (lim > 0 && lim < builtin) cap = lim;
+#endif
     if (n_tiles < 1) return 1;
     return (int)(n_tiles < cap ? n_tiles : cap);
 }
@@ -107,7 +115,7 @@ int check_plan(const gsz_plan* p, const char* who) {
     int dev = 0;
     int rc = current_device(&dev);
     if (rc) return rc;
-    if (!p->dev_mem || p->device != dev) {
+    if (!p->d_seg || p->device != dev) {
         set_error("%s: plan has no device tables on device %d (call gsz_plan_upload)", who, dev);
         return GSZ_ERR_NOT_UPLOADED;
     }
@@ -230,69 +238,45 @@ void launch_reduce_lc(bool norm, bool flat, bool outflat, bool wire16, dim3 grid
 
 // ---------------------------------------------------------------- C ABI --
 
-extern "C" int gsz_plan_destroy(gsz_plan* p) {
-    if (!p) return GSZ_OK;
-    if (p->dev_mem) {
-        int cur = 0;
-        if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(p->device) == hipSuccess) {
-            (void)hipFree(p->dev_mem);
-            (void)hipSetDevice(cur);
-        }
-    }
-    delete p;
-    return GSZ_OK;
-}
-
-extern "C" int gsz_set_grid_limit(int64_t max_blocks) {
+#ifdef GSZ_TEST_HOOKS
+extern "C" int gsz_test_set_grid_limit(int64_t max_blocks) {
     if (max_blocks < 0) {
-        set_error("gsz_set_grid_limit: max_blocks %lld is negative", (long long)max_blocks);
+        set_error("gsz_test_set_grid_limit: max_blocks %lld is negative", (long long)max_blocks);
         return GSZ_ERR_INVALID_ARG;
     }
     g_grid_limit.store(max_blocks, std::memory_order_relaxed);
     return GSZ_OK;
 }
+#endif
 
-extern "C" int gsz_plan_upload(gsz_plan* p) {
-    if (!p) { set_error("gsz_plan_upload: NULL plan"); return GSZ_ERR_INVALID_ARG; }
+extern "C" int gsz_plan_upload(gsz_plan* p, void* dev_tables, size_t bytes, hipStream_t stream) {
+    const char* who = "gsz_plan_upload";
+    if (!p) { set_error("%s: NULL plan", who); return GSZ_ERR_INVALID_ARG; }
     int dev = 0;
     int rc = current_device(&dev);
     if (rc) return rc;
-    std::lock_guard<std::mutex> lock(p->mu);
-    if (p->dev_mem && p->device == dev) return GSZ_OK;
-    if (p->dev_mem) {
-        hipError_t e = hipSetDevice(p->device);
-        if (e == hipSuccess) e = hipFree(p->dev_mem);
-        (void)hipSetDevice(dev);
-        if (e != hipSuccess) return hip_fail("gsz_plan_upload: freeing old tables", e);
-        p->dev_mem = nullptr;
-        p->device = -1;
+    const size_t need = p->image.size() * sizeof(int64_t);
+    if (!dev_tables) { set_error("%s: NULL device buffer", who); return GSZ_ERR_INVALID_ARG; }
+    if (misaligned(dev_tables)) { set_error("%s: device buffer is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED; }
+    if (bytes < need) {
+        set_error("%s: device buffer of %zu bytes, the plan's tables need %zu (gsz_plan_device_bytes)",
+                  who, bytes, need);
+        return GSZ_ERR_SIZE;
     }
-    // One allocation: seg, pack and pads rows (int64), then the two lookup tables
-    // (a {lo, hi} pair of int32 per cell, one 8-byte slot each), then 2 spare slots.
+    std::lock_guard<std::mutex> lock(p->mu);
+    // The source is the plan's own image, which lives as long as the plan, so
+    // the copy may still be in flight when this returns.
+    const hipError_t e = hipMemcpyAsync(dev_tables, p->image.data(), need, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail("gsz_plan_upload: hipMemcpyAsync", e);
     const size_t n_seg = p->seg.size(), n_pack = p->pack.size(), n_pads = p->pads.size();
-    const size_t n_slut = p->seg_lut.cells.size() / 2, n_plut = p->pack_lut.cells.size() / 2;
-    const size_t slots = n_seg + n_pack + n_pads + n_slut + n_plut + 2;
-    std::vector<int64_t> img;
-    img.reserve(slots);
-    img.insert(img.end(), p->seg.begin(), p->seg.end());
-    img.insert(img.end(), p->pack.begin(), p->pack.end());
-    img.insert(img.end(), p->pads.begin(), p->pads.end());
-    img.resize(slots, 0);
-    std::memcpy(img.data() + n_seg + n_pack + n_pads, p->seg_lut.cells.data(), n_slut * 8);
-    std::memcpy(img.data() + n_seg + n_pack + n_pads + n_slut, p->pack_lut.cells.data(), n_plut * 8);
-    void* mem = nullptr;
-    hipError_t e = hipMalloc(&mem, slots * sizeof(int64_t));
-    if (e != hipSuccess) return hip_fail("gsz_plan_upload: hipMalloc", e);
-    int64_t* d = static_cast<int64_t*>(mem);
-    e = hipMemcpy(mem, img.data(), slots * sizeof(int64_t), hipMemcpyHostToDevice);
-    if (e != hipSuccess) { (void)hipFree(mem); return hip_fail("gsz_plan_upload: hipMemcpy", e); }
-    p->dev_mem = mem;
+    const size_t n_slut = p->seg_lut.cells.size() / 2;
+    const int64_t* d = static_cast<const int64_t*>(dev_tables);
     p->device = dev;
     p->d_seg = d;
     p->d_pack = d + n_seg;
+    p->d_pads = d + n_seg + n_pack;
     p->d_seg_lut = reinterpret_cast<const uint64_t*>(d + n_seg + n_pack + n_pads);
     p->d_pack_lut = reinterpret_cast<const uint64_t*>(d + n_seg + n_pack + n_pads + n_slut);
-    p->d_pads = d + n_seg + n_pack;
     return GSZ_OK;
 }
 

@@ -174,12 +174,28 @@ extern "C" int gsz_plan_create(const int64_t* numel, int32_t n_tensors, int64_t 
 
         p->seg_lut = gsz::build_lut(p->seg, 3, 0, (int64_t)B, p->shard_len);
         p->pack_lut = gsz::build_lut(p->pack, 3, 2, n_tensors, tiles);
+
+        // The device image: seg, pack, pads, the two lookup tables, 2 spare slots.
+        const size_t n_slut = p->seg_lut.cells.size() / 2, n_plut = p->pack_lut.cells.size() / 2;
+        const size_t fixed = p->seg.size() + p->pack.size() + p->pads.size();
+        p->image.reserve(fixed + n_slut + n_plut + 2);
+        p->image.insert(p->image.end(), p->seg.begin(), p->seg.end());
+        p->image.insert(p->image.end(), p->pack.begin(), p->pack.end());
+        p->image.insert(p->image.end(), p->pads.begin(), p->pads.end());
+        p->image.resize(fixed + n_slut + n_plut + 2, 0);
+        if (n_slut) std::memcpy(p->image.data() + fixed, p->seg_lut.cells.data(), n_slut * 8);
+        if (n_plut) std::memcpy(p->image.data() + fixed + n_slut, p->pack_lut.cells.data(), n_plut * 8);
     } catch (const std::bad_alloc&) {
         delete p;
         set_error("gsz_plan_create: out of host memory");
         return GSZ_ERR_NO_MEMORY;
     }
     *out = p;
+    return GSZ_OK;
+}
+
+extern "C" int gsz_plan_destroy(gsz_plan* p) {
+    delete p;          // the device tables live in the caller's memory
     return GSZ_OK;
 }
 
@@ -231,6 +247,12 @@ extern "C" int gsz_plan_check(const gsz_plan* p, uint64_t peer_hash) {
                   (unsigned long long)peer_hash);
         return GSZ_ERR_PLAN_MISMATCH;
     }
+    return GSZ_OK;
+}
+
+extern "C" int gsz_plan_device_bytes(const gsz_plan* p, size_t* out) {
+    if (!p || !out) { set_error("gsz_plan_device_bytes: NULL argument"); return GSZ_ERR_INVALID_ARG; }
+    *out = p->image.size() * sizeof(int64_t);
     return GSZ_OK;
 }
 

@@ -33,11 +33,10 @@
  *     pointers are ordinary host memory read during the call only.  Device
  *     vector pointers must be 16-byte aligned (GSZ_ERR_MISALIGNED otherwise).
  *   - Device work is enqueued on the caller's hipStream_t (0 = the null
- *     stream) and is asynchronous; no call synchronises the host except
- *     gsz_plan_upload.
- *   - The library allocates device memory only in gsz_plan_upload (the plan's
- *     device tables, freed by gsz_plan_destroy).  Scratch space comes from the
- *     caller (gsz_workspace_bytes).
+ *     stream) and is asynchronous; no call synchronises the host.
+ *   - The library never allocates or frees device memory.  The plan's device
+ *     tables (gsz_plan_device_bytes) and scratch space (gsz_workspace_bytes)
+ *     live in buffers the caller provides.
  *   - Device calls refuse any device that is not gfx950 (GSZ_ERR_DEVICE).
  */
 #ifndef GSZ_H
@@ -127,7 +126,8 @@ typedef struct gsz_adamw_hp {
 int gsz_plan_create(const int64_t* numel, int32_t n_tensors, int64_t bucket_cap_bytes,
                     int32_t world_size, int32_t align_elems, gsz_plan** out);
 
-/* Frees the plan and its device tables.  NULL is accepted. */
+/* Frees the plan (host memory only; the device tables are the caller's
+ * buffer).  NULL is accepted. */
 int gsz_plan_destroy(gsz_plan* plan);
 
 int gsz_plan_get_info(const gsz_plan* plan, gsz_plan_info* out);
@@ -144,14 +144,27 @@ int gsz_plan_tensor(const gsz_plan* plan, int32_t t, int64_t* flat_offset, int32
  * GSZ_OK if equal, GSZ_ERR_PLAN_MISMATCH otherwise. */
 int gsz_plan_check(const gsz_plan* plan, uint64_t peer_hash);
 
-/* Copies the plan's device tables to the current device (allocating them
- * there; the plan owns them) and waits for the copy.  Must precede every
- * device call that takes this plan, on the device it will run on.  A second
- * upload on the same device does nothing; an upload to another device moves
- * the tables there.  Not to be called while device calls on the same plan are
- * being issued from other threads (the plan is otherwise read-only and may be
- * shared between threads). */
-int gsz_plan_upload(gsz_plan* plan);
+/* *out = bytes of device memory the plan's tables take (gsz_plan_upload):
+ * per bucket {shard offset, flat base, chunk length}, per tensor {flat offset,
+ * size, first pack tile}, per padded bucket {start, length}, and two lookup
+ * tables of at most 2^16 cells (tile -> tensor, shard index -> bucket), 8
+ * bytes per entry: at most 1,048,640 + 24 * n_tensors + 40 * n_buckets. */
+int gsz_plan_device_bytes(const gsz_plan* plan, size_t* out);
+
+/* Copies the plan's device tables into dev_tables (device memory on the
+ * current device, owned by the caller, 16-byte aligned, at least
+ * gsz_plan_device_bytes long), enqueued on `stream`; the source is the plan's
+ * own host image, so the copy may complete after the call returns (the HIP
+ * runtime may stage the pageable source before returning; nothing waits for
+ * the device).  Every later device call that takes this plan reads the tables
+ * there, on this device, and must be ordered after the copy (the same stream,
+ * or an event).  The caller keeps dev_tables alive and unmodified while such
+ * calls may run, and until it uploads the plan again (to another buffer or
+ * device) or destroys it.  Not to be called while device calls on the same
+ * plan are being issued from other threads (the plan is otherwise read-only
+ * and may be shared between threads).  GSZ_ERR_SIZE if bytes is too small,
+ * GSZ_ERR_MISALIGNED, GSZ_ERR_INVALID_ARG for a NULL buffer. */
+int gsz_plan_upload(gsz_plan* plan, void* dev_tables, size_t bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------- ledger --- */
 
@@ -169,16 +182,6 @@ int gsz_ledger_bytes_per_param(int32_t world_size, int32_t zero_stage, double* o
  * GSZ_ERR_INVALID_ARG if n < 0 or out is NULL. */
 int gsz_workspace_bytes(int64_t n, size_t* out);
 
-/* Launch-shape control for tests and tuning (no page defines it).  Caps the
- * number of blocks of every data-sized launch made after the call, for the
- * whole process and every thread; 0 restores the built-in caps (2^31
- * work-items per launch, reached only by inputs of more than about 17e9
- * elements).  Under a cap each block strides over several tiles: the path that
- * otherwise runs only on such inputs.  Results are bit-identical to uncapped
- * launches except the fp64 norm partials, whose summation grouping follows the
- * grid.  Launches already enqueued keep their grids; workspace sizes do not
- * change.  GSZ_ERR_INVALID_ARG if max_blocks < 0. */
-int gsz_set_grid_limit(int64_t max_blocks);
 
 /* -------------------------------------------------------------- steps --- */
 

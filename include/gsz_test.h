@@ -1,0 +1,33 @@
+/*
+ * gsz_test.h -- test hooks of libgsz, exported only by the test build
+ * (libgsz_test.so: the same sources compiled with GSZ_TEST_HOOKS).  The
+ * product library, libgsz.so, has none of this state.  No page defines these
+ * calls: they exist so that tests can reach code paths that only very large
+ * inputs reach otherwise.
+ */
+#ifndef GSZ_TEST_H
+#define GSZ_TEST_H
+
+#include <stdint.h>
+
+#include "gsz.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Caps the number of blocks of every data-sized launch made after the call,
+ * for the whole process and every thread; 0 restores the built-in caps (2^31
+ * work-items per launch, reached only by inputs of more than about 17e9
+ * elements).  Under a cap each block strides over several tiles: the path
+ * that otherwise runs only on such inputs.  Results are bit-identical to
+ * uncapped launches except the fp64 norm partials, whose summation grouping
+ * follows the grid.  Launches already enqueued keep their grids; workspace
+ * sizes do not change.  GSZ_ERR_INVALID_ARG if max_blocks < 0. */
+int gsz_test_set_grid_limit(int64_t max_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSZ_TEST_H */

@@ -16,6 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 C_SOURCE = r"""
 #include <stdio.h>
 #include "gsz.h"
+#include "gsz_test.h"
 
 int main(void) {
     int64_t numel[5] = {1000, 37, 4096, 0, 5};
@@ -38,6 +39,9 @@ int main(void) {
         if (gsz_plan_tensor(p, t, &off, &bkt) != GSZ_OK) return 4;
         printf("tensor %d %lld %d\n", (int)t, (long long)off, (int)bkt);
     }
+    size_t dev_bytes = 0;
+    if (gsz_plan_device_bytes(p, &dev_bytes) != GSZ_OK) return 7;
+    printf("devbytes %zu\n", dev_bytes);
     printf("check_same %d\n", gsz_plan_check(p, info.hash));
     printf("check_other %d %s\n", gsz_plan_check(p, info.hash ^ 1u),
            gsz_status_string(gsz_plan_check(p, info.hash ^ 1u)));
@@ -82,6 +86,7 @@ def test_c_program_uses_the_abi(tmp_path):
             (bi["base"], bi["n_elems"], bi["chunk"], bi["shard_off"])
     for t, (idx, off, bkt) in enumerate(out["tensor"]):
         assert (int(off), int(bkt)) == plan.tensor(t)
+    assert int(out["devbytes"][0][0]) == plan.device_bytes()
     assert out["check_same"][0] == ["0"]
     assert out["check_other"][0][0] == str(G.load().gsz_plan_check(plan.handle, plan.hash ^ 1))
     assert float(out["ledger"][0][0]) == G.ledger_bytes_per_param(8, 2)

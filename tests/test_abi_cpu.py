@@ -14,11 +14,14 @@ from oracle import ledger as oledger
 from oracle.plan import make_plan
 from synth import workloads as W
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gsz.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADER = os.path.join(INCLUDE, "gsz.h")
+TEST_HEADER = os.path.join(INCLUDE, "gsz_test.h")
+CSRC = os.path.join(os.path.dirname(G.LIB_PATH), "csrc")
 
 
-def declared_symbols():
-    text = open(HEADER).read()
+def declared_symbols(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(gsz_\w+)\s*\(", text, re.M)))
 
 
@@ -29,8 +32,60 @@ def test_library_exports_every_declared_symbol():
     missing = [s for s in syms if not hasattr(lib, s)]
     assert not missing, missing
     for s in ("gsz_bucket_pack", "gsz_shard_reduce_mean", "gsz_shard_grad_sqnorm",
-              "gsz_clip_coef", "gsz_shard_adamw_step", "gsz_allgather_layout_write"):
+              "gsz_clip_coef", "gsz_shard_adamw_step", "gsz_allgather_layout_write",
+              "gsz_plan_device_bytes", "gsz_plan_upload"):
         assert s in syms
+
+
+def test_test_hooks_live_only_in_the_test_build():
+    """The grid cap is process-wide state, so the product library does not
+    have it; the test build exports everything the product does plus the
+    hooks of gsz_test.h."""
+    hooks = declared_symbols(TEST_HEADER)
+    assert hooks == ["gsz_test_set_grid_limit"]
+    prod = ctypes.CDLL(G.LIB_PATH)
+    test = ctypes.CDLL(G._binding.TEST_LIB_PATH)
+    assert not any(hasattr(prod, h) for h in hooks)
+    assert all(hasattr(test, s) for s in declared_symbols() + hooks)
+    with pytest.raises(RuntimeError):
+        G.set_grid_limit(4)                      # outside test_hooks(): refused
+    with G.test_hooks():
+        with pytest.raises(G.GszError) as e:     # the cap is a count of blocks
+            G.set_grid_limit(-1)
+        assert "-1" in str(e.value)
+        G.set_grid_limit(0)
+        p = G.Plan([5], 100, 2)
+    with pytest.raises(ValueError):              # a plan is tied to its build
+        G._binding._lib_for(p)
+
+
+def test_library_neither_allocates_device_memory_nor_waits():
+    """The library's sources make no device allocation, free or synchronising
+    call: device memory is the caller's (plan tables, workspace), and every
+    device call only enqueues work on the caller's stream."""
+    banned = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipExtMalloc\w*|hipMallocManaged|"
+                        r"hipHostMalloc|hipDeviceSynchronize|hipStreamSynchronize|"
+                        r"hipEventSynchronize|hipMemcpy|hipMemset)\s*\(")
+    for name in sorted(os.listdir(CSRC)):
+        text = open(os.path.join(CSRC, name)).read()
+        assert not banned.search(text), (name, banned.search(text).group(0))
+    undefined = {line.split()[-1].split("@")[0] for line in
+                 os.popen(f"nm -D --undefined-only {G.LIB_PATH}").read().splitlines() if line.strip()}
+    assert "hipMemcpyAsync" in undefined and "hipLaunchKernel" in " ".join(undefined)
+    assert not undefined & {"hipMalloc", "hipMallocAsync", "hipMallocManaged", "hipExtMallocWithFlags",
+                            "hipHostMalloc", "hipFree", "hipFreeAsync", "hipHostFree", "hipMemcpy",
+                            "hipMemset", "hipDeviceSynchronize", "hipStreamSynchronize",
+                            "hipEventSynchronize"}
+
+
+def test_plan_device_bytes_is_the_documented_bound():
+    """Header: at most 1,048,640 + 24 * n_tensors + 40 * n_buckets bytes."""
+    for cfg in range(5):
+        w = W.by_id(cfg)
+        p = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size)
+        nb = p.device_bytes()
+        assert nb % 8 == 0 and nb <= 1048640 + 24 * p.n_tensors + 40 * p.n_buckets, cfg
+    assert G.Plan([], 100, 2).device_bytes() > 0
 
 
 def assert_same_plan(cplan, oplan):
@@ -143,10 +198,6 @@ def test_argument_validation():
         assert G.workspace_bytes(n) == 8 * (blocks + 1024), n
     with pytest.raises(G.GszError):
         G.workspace_bytes(-1)
-    with pytest.raises(G.GszError) as e:                   # the grid cap is a count of blocks
-        G.set_grid_limit(-1)
-    assert "-1" in str(e.value)
-    G.set_grid_limit(0)
     lib = G.load()
     assert lib.gsz_status_string(-5) == b"plan mismatch"
     assert lib.gsz_plan_destroy(None) == 0

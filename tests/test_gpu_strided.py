@@ -1,5 +1,5 @@
 """GPU parity of the striding path: every data-sized launch capped at a few
-blocks (gsz_set_grid_limit), so each block walks many tiles -- the path that
+blocks (gsz_test_set_grid_limit, a hook of the test build), so each block walks many tiles -- the path that
 uncapped launches take only past 2^31 work-items per launch.  Every row of the
 step and the rows beyond it against the oracle: bit-exact bytes and reduced
 gradients and state, norm partials within 1e-12 relative (their grouping follows
@@ -26,9 +26,12 @@ LIMITS = [1, 3, 8, 100]
 
 
 @pytest.fixture(autouse=True)
-def _restore_grid_limit():
-    yield
-    G.set_grid_limit(0)
+def _test_build():
+    """Every call of these tests goes to the test build of the library (the
+    same sources with the grid-cap hook), plans included."""
+    with G.test_hooks():
+        yield
+        G.set_grid_limit(0)
 
 
 def say(*a):
