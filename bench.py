@@ -49,7 +49,15 @@ def parse():
                     help="timed steps (default: 50 for the workloads up to 1.3B, 20 for the "
                          "7B and 70B shares)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, help="workload id (synth.workloads)")
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload id (synth.workloads); default 4, the 70B share (P = 64)")
+    ap.add_argument("--layout", choices=["auto", "flat", "compact", "interleaved"], default="auto",
+                    help="contributions: bucket-flat (the P ranks' whole flat buffers), "
+                         "shard-compact (P buffers of S elements) or one rank-interleaved "
+                         "receive buffer; auto = flat when it fits (up to the 7B share), else "
+                         "compact")
+    ap.add_argument("--no-interleaved", action="store_true",
+                    help="skip the second pass over a rank-interleaved receive buffer")
     ap.add_argument("--owner", type=int, default=0)
     ap.add_argument("--variant", choices=["zero", "ddp"], default="zero",
                     help="zero: the ZeRO-1/2 shard step (default); ddp: the unsharded step "
@@ -87,13 +95,15 @@ def short_name(full):
         return "k_unpack"
     if "k_pack<2>" in full:
         return "k_accumulate"
-    if "k_reduce_mean<" in full:
+    if "k_reduce_mean<" in full:             # <PS, NORM, LAY, OUTFLAT, W16>
         args = [a.strip() for a in full.split("k_reduce_mean<")[1].split(">")[0].split(",")]
         if len(args) == 5 and args[4] == "true":
             return "k_reduce_mean_bf16_wire"
         if len(args) >= 4 and args[3] == "true":
             return "k_allreduce_mean"
-    if "k_reduce_mean_lc<" in full:          # <T, PS, NORM, FLAT, OUTFLAT, W16>
+        if len(args) >= 3 and args[2] == "2":
+            return "k_reduce_mean_ilv"
+    if "k_reduce_mean_lc<" in full:          # <T, PS, NORM, LAY, OUTFLAT, W16>
         args = [a.strip() for a in full.split("k_reduce_mean_lc<")[1].split(">")[0].split(",")]
         if args[0] == "float":
             return "k_reduce_mean_f32"
@@ -101,6 +111,8 @@ def short_name(full):
             return "k_reduce_mean_bf16_wire"
         if len(args) == 6 and args[4] == "true":
             return "k_allreduce_mean"
+        if len(args) >= 4 and args[3] == "2":
+            return "k_reduce_mean_ilv"
         return "k_reduce_mean"
     if "k_finalize_ranges" in full:
         return "k_finalize_ranges"
@@ -131,12 +143,14 @@ def gpu_step_stats(ev):
     return dict(mean=float(np.mean(t)), median=float(np.median(t)), min=float(np.min(t)))
 
 
-def profile_commands(config, trace_dir, fetch_dir, write_dir, variant="zero"):
+def profile_commands(config, trace_dir, fetch_dir, write_dir, variant="zero", layout="auto"):
     """The rocprofv3 command lines (run from the repository root) whose output
     the summaries below are made from: a kernel trace of the default bench of
     a workload, and one counter pass each for FETCH_SIZE and WRITE_SIZE, each
     writing <dir>/bench_*.csv."""
     var = " --variant ddp" if variant == "ddp" else ""
+    if layout != "auto":
+        var += f" --layout {layout}"
     bench_args = f"python3 bench.py --config {config}{var} --no-cpu-baseline"
     short = f"python3 bench.py --config {config}{var} --steps 3 --warmup 1 --no-cpu-baseline"
     return {"trace": f"rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} "
@@ -145,10 +159,11 @@ def profile_commands(config, trace_dir, fetch_dir, write_dir, variant="zero"):
             "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o bench -- {short}"}
 
 
-def profile_name(workload, variant):
-    """Name of a workload's profile summaries: the unsharded (DDP) step gets
-    its own files."""
-    return f"{workload}-ddp" if variant == "ddp" else workload
+def profile_name(workload, variant, layout="auto"):
+    """Name of a workload's profile summaries: the unsharded (DDP) step and
+    the rank-interleaved receive layout get their own files."""
+    name = f"{workload}-ddp" if variant == "ddp" else workload
+    return f"{name}-interleaved" if layout == "interleaved" else name
 
 
 def _raw_dir(csv_path):
@@ -274,69 +289,108 @@ def read_traffic(kernel, workload, profiles_dir=None):
     return float(kv[key]) if key in kv else None
 
 
-def cpu_baseline(w, owner):
-    """The oracle as it stands, on one core, over the trailing buckets of the
-    same workload (the first buckets of its plan): owner's pack, reduce-mean,
-    squared norm, clip and AdamW + all-gather layout.  Input generation is not
-    timed."""
+def _oracle_sample(w, owner, n_max):
+    """Host inputs of the oracle baseline: the first n shard elements of the
+    owner's shard (n <= n_max), placed with the oracle's plan: the P ranks'
+    bf16 contributions for those elements and the owner's fp32 master, m, v
+    (pads zero), from the same seeded generator as the device inputs."""
     import numpy as np
-    from oracle import pack as opack
-    from oracle.adamw import adamw
-    from oracle.layout import ag_write
-    from oracle.norm import clip_coef, sqnorm_partial, total
     from oracle.plan import make_plan
-    from oracle.reduce import reduce_mean
     from synth import gen
     from synth import workloads as W
 
-    numel = w.numel
-    m, s = 0, 0
-    while s < 256_000_000 and m < len(numel):
-        m += 1
-        s += numel[-m]
-    sub = numel[-m:]
-    pre = sum(numel[:-m])
+    plan = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    n = min(plan.shard_len, n_max)
+    pre = np.cumsum([0] + list(w.numel))
+    pieces = []          # (shard offset, parameter index, length) inside [0, n)
+    for b, bk in enumerate(plan.buckets):
+        if bk.shard_off >= n:
+            break
+        cs, ce = plan.chunk_range(b, owner)
+        for t in bk.tensors:
+            ts, te = plan.tensor_offset[t], plan.tensor_offset[t] + plan.numel[t]
+            lo, hi = max(cs, ts), min(ce, te)
+            so = bk.shard_off + (lo - cs)
+            if lo < hi and so < n:
+                pieces.append((so, int(pre[t]) + (lo - ts), min(hi - lo, n - so)))
+
+    def fill(kind, rank, std, mode):
+        out = np.zeros(n, dtype=np.uint16 if mode == gen.MODE_BF16 else np.float32)
+        for so, pi, ln in pieces:
+            gen.host_fill(w.cfg_id, kind, rank, pi, ln, std, mode, out=out[so:so + ln])
+        return out
+
+    contribs = [fill(W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16) for q in range(w.world_size)]
+    state = [fill(kind, 0, std, mode) for kind, std, mode in
+             ((W.KIND_MASTER, W.MASTER_STD, gen.MODE_F32), (W.KIND_EXP_AVG, W.EXP_AVG_STD, gen.MODE_F32),
+              (W.KIND_EXP_AVG_SQ, W.EXP_AVG_SQ_STD, gen.MODE_ABS))]
+    return n, contribs, state
+
+
+def cpu_baseline(w, owner, seconds=10.0):
+    """The oracle as it stands, timed on the host over a window of the same
+    workload: the first ~2^28 / P elements of the owner's shard (the P ranks'
+    contributions for them, 512 MiB in all) through the metric's step --
+    ring-order reduce-mean, squared-norm partial, clip coefficient (the other
+    ranks' partials stand in as copies of this one, as on the GPU) and AdamW
+    with the bf16 result.  Timed twice: on one core, and with the window cut
+    into one slice per host core, each slice run by a thread through the same
+    oracle functions (NumPy releases the interpreter lock inside its array
+    operations).  Input generation is not timed."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    from oracle.adamw import adamw
+    from oracle.norm import clip_coef, sqnorm_partial, total
+    from oracle.reduce import reduce_mean
+
     P = w.world_size
-    plan = make_plan(sub, w.bucket_cap_bytes, P)
-    offs = np.cumsum([0] + sub)
-    log(f"[cpu] generating the oracle sample: {len(plan.buckets)} buckets, {s} params x {P} ranks")
-    grads = []
-    for q in range(P):
-        G = gen.host_fill(w.cfg_id, W.KIND_GRAD, q, pre, s, w.grad_std, gen.MODE_BF16)
-        grads.append([G[offs[i]:offs[i + 1]] for i in range(m)])
-    others = [opack.pack(plan, grads[q]) for q in range(P) if q != owner]
-    S = plan.shard_len
-    state = []
-    for kind, std, mode in ((W.KIND_MASTER, W.MASTER_STD, gen.MODE_F32),
-                            (W.KIND_EXP_AVG, W.EXP_AVG_STD, gen.MODE_F32),
-                            (W.KIND_EXP_AVG_SQ, W.EXP_AVG_SQ_STD, gen.MODE_ABS)):
-        state.append(gen.host_fill(w.cfg_id, kind, 0, pre, S, std, mode))
     hp = w.hp
-    log(f"[cpu] timing the oracle step on S = {S} shard elements")
+    log(f"[cpu] generating the oracle sample: {P} contributions of up to {(1 << 28) // P} elements")
+    n, contribs, (th0, m0, v0) = _oracle_sample(w, owner, (1 << 28) // P)
+    cores = max(1, min(16, os.cpu_count() or 1))
 
-    def one_step():
-        mine = opack.pack(plan, grads[owner])
-        flats = others[:owner] + [mine] + others[owner:]
-        g = reduce_mean([opack.owner_view(plan, f, owner) for f in flats], owner)
-        part = sqnorm_partial(g)
+    def step(lo, hi):
+        g = reduce_mean([c[lo:hi] for c in contribs], owner)
+        return g, sqnorm_partial(g)
+
+    def update(g, lo, hi, coef):
+        return adamw(th0[lo:hi], m0[lo:hi], v0[lo:hi], g, coef, hp.lr, hp.beta1, hp.beta2,
+                     hp.eps, hp.weight_decay, hp.step)
+
+    def one_core():
+        g, part = step(0, n)
         _, coef = clip_coef(total([part] * P), hp.max_norm)
-        th, m1, v1, p = adamw(state[0], state[1], state[2], g, coef, hp.lr, hp.beta1, hp.beta2,
-                              hp.eps, hp.weight_decay, hp.step)
-        gathered = np.zeros(plan.flat_len, dtype=np.uint16)
-        ag_write(plan, owner, p, gathered)
+        update(g, 0, n, coef)
 
-    # the same step on the same inputs, repeated until about 10 s of CPU work
-    reps, t0 = 0, time.perf_counter()
-    while reps < 3 or time.perf_counter() - t0 < 10.0:
-        one_step()
-        reps += 1
-    dt = time.perf_counter() - t0
-    return dict(value=S * reps / dt, unit="params/s", cores=1, kind="oracle",
-                host=_cpu_model(),
-                sample=(f"{w.name}: the first {len(plan.buckets)} buckets of the plan "
-                        f"({m} trailing tensors, {s} params, owner {owner} shard of {S}); "
-                        f"pack + reduce-mean + norm + clip + AdamW + all-gather layout, "
-                        f"{reps} repetitions in {dt:.1f} s of single-threaded NumPy"))
+    bounds = [(k * n // cores // 8 * 8, (k + 1) * n // cores // 8 * 8 if k < cores - 1 else n)
+              for k in range(cores)]
+    pool = cf.ThreadPoolExecutor(max_workers=cores)
+
+    def all_cores():
+        res = list(pool.map(lambda b: step(*b), bounds))
+        part = total([pt for _, pt in res])
+        _, coef = clip_coef(total([part] * P), hp.max_norm)
+        list(pool.map(lambda kb: update(res[kb[0]][0], kb[1][0], kb[1][1], coef),
+                      enumerate(bounds)))
+
+    def timed(fn):
+        reps, t0 = 0, time.perf_counter()
+        while reps < 2 or time.perf_counter() - t0 < seconds:
+            fn()
+            reps += 1
+        return reps, time.perf_counter() - t0
+
+    log(f"[cpu] timing the oracle step on {n} shard elements: one core, then {cores} threads")
+    r1, t1 = timed(one_core)
+    rk, tk = timed(all_cores)
+    pool.shutdown()
+    return dict(value=n * rk / tk, unit="params/s", cores=cores, kind="oracle",
+                host=_cpu_model(), single_core_value=n * r1 / t1,
+                sample=(f"{w.name}, owner {owner}: the first {n} elements of the shard with all "
+                        f"{P} ranks' contributions; reduce-mean + norm partial + clip + AdamW "
+                        f"(bf16 out) as the GPU step; {rk} repetitions in {tk:.1f} s on {cores} "
+                        f"threads (one slice each) and {r1} in {t1:.1f} s on one core"))
 
 
 def _cpu_model():
@@ -349,6 +403,20 @@ def _cpu_model():
     return f"unknown ({os.cpu_count()} logical CPUs)"
 
 
+# Input fills a benchmark may issue.  Every buffer is placed with one
+# piece-table launch (a few per rank and per state array); a counter pass of
+# rocprofv3 over a benchmark that issued ~48,000 small fill launches ended in a
+# segmentation fault inside the profiler, so the many-launch fills are kept out
+# of every benchmark and profiled command.
+MAX_FILL_LAUNCHES = 400
+
+
+def check_fill_launches(gen):
+    if gen.fill_launches > MAX_FILL_LAUNCHES:
+        raise RuntimeError(f"{gen.fill_launches} input fill launches (at most {MAX_FILL_LAUNCHES}): "
+                           "place each buffer with one piece-table launch")
+
+
 def bench_ddp(args):
     """The unsharded (DDP / NO_SHARD) step of one rank: pack its gradients,
     all-reduce mean over the P flat buffers (local arithmetic), squared norm,
@@ -358,8 +426,9 @@ def bench_ddp(args):
     import torch
 
     import gradient_sync_zero_amd as G
+    from synth import gen
+    from synth import placement as PL
     from synth import workloads as W
-    from tests import gpu_inputs as GI
 
     torch.cuda.set_device(0)
     w = W.by_id(args.config)
@@ -375,14 +444,15 @@ def bench_ddp(args):
     flats = [torch.empty(L, dtype=torch.uint16, device="cuda") for _ in range(P)]
     for q in range(P - 1, -1, -1):
         if q != r:
-            _, views = GI.rank_grads(w, q, gbuf)
+            _, views = PL.rank_grads(w, q, gbuf)
             G.bucket_pack(plan, views, flats[q])
-    _, my_grads = GI.rank_grads(w, r, gbuf)
-    master, m, v = GI.full_state(plan, w)
+    _, my_grads = PL.rank_grads(w, r, gbuf)
+    master, m, v = PL.full_state(plan, w)
+    check_fill_launches(gen)
     g = torch.empty(L, dtype=torch.float32, device="cuda")
     pflat = torch.empty(L, dtype=torch.uint16, device="cuda")
     pbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
-    params = [pbuf[s0:s0 + n] for s0, n in zip(GI.prefix(w.numel), w.numel)]
+    params = [pbuf[s0:s0 + n] for s0, n in zip(PL.prefix(w.numel), w.numel)]
     # the all-reduce writes the P chunk owners' norm partials in the same pass
     ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     parts = torch.zeros(P, dtype=torch.float64, device="cuda")
@@ -440,7 +510,6 @@ def bench_ddp(args):
     step_gbps = sum(byts.values()) / (ms_step * 1e-3) / 1e9
     # the plain copy (the practical ceiling and the calibration kernel of the
     # counter runs), after the timed steps as in the sharded bench
-    from synth import gen
     nb = int(args.copy_gib * (1 << 30)) // 16 * 16
     a = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
@@ -482,16 +551,16 @@ def main():
         return
     if args.summarize_trace or args.summarize_pmc:
         from synth import workloads as W
-        wname = profile_name(W.by_id(args.config).name, args.variant)
+        wname = profile_name(W.by_id(args.config).name, args.variant, args.layout)
         if args.summarize_trace:
             d = _raw_dir(args.summarize_trace)
             summarize_trace(args.summarize_trace, wname,
-                            args.command or profile_commands(args.config, d, d, d,
-                                                             args.variant)["trace"])
+                            args.command or profile_commands(args.config, d, d, d, args.variant,
+                                                             args.layout)["trace"])
         if args.summarize_pmc:
             nb = int(args.copy_gib * (1 << 30)) // 16 * 16
             cmds = profile_commands(args.config, None, _raw_dir(args.summarize_pmc[0]),
-                                    _raw_dir(args.summarize_pmc[1]), args.variant)
+                                    _raw_dir(args.summarize_pmc[1]), args.variant, args.layout)
             summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], wname,
                           args.command or f"{cmds['fetch']} ; {cmds['write']}", nb)
         return
@@ -508,8 +577,8 @@ def main():
 
     import gradient_sync_zero_amd as G
     from synth import gen
+    from synth import placement as PL
     from synth import workloads as W
-    from tests import gpu_inputs as GI
 
     torch.cuda.set_device(0)
     w = W.by_id(args.config)
@@ -520,69 +589,62 @@ def main():
     log(f"[gpu] {dev.name} ({getattr(dev, 'gcnArchName', '?')}), {w.name}: "
         f"Psi={w.n_params} S={S} flat={L} buckets={plan.n_buckets}")
 
-    # Inputs.  When all P ranks' bucket-major flat buffers fit next to the
-    # state (every config but the 70B share), the step packs the owner's own
-    # per-tensor gradients and reduces over the P flat buffers.  Otherwise the
-    # contributions are the shard-compact buffers the P ranks send to this
-    # owner, and the step is the reduce + clip + AdamW the metric names (the
-    # owner's full-model pack would need 2 x 138 GB more than the GPU holds).
+    # Inputs.  The contributions are the P ranks' whole bucket-major flat
+    # buffers when they fit next to the state (every workload up to the 7B
+    # share), else the shard-compact buffers the P ranks send to this owner (the
+    # 70B share: 64 buffers of S elements, 138 GB), or on request one
+    # rank-interleaved receive buffer.  The timed step is the metric's:
+    # reduce-mean (+ norm partial), clip coefficient, AdamW.
+    layout = args.layout
+    if layout == "auto":
+        fits = (P + 2) * 2 * L + 2 * w.n_params + 18 * S < 240e9
+        layout = "flat" if fits else "compact"
     t0 = time.perf_counter()
-    flat_mode = (P + 2) * 2 * L + 2 * w.n_params + 18 * S < 240e9
-    if flat_mode:
+    my_grads = None
+    if layout == "flat":
         gbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
         flats = [torch.empty(L, dtype=torch.uint16, device="cuda") for _ in range(P)]
-        for q in list(range(P - 1, -1, -1)):
-            if q == r:
-                continue
-            _, views = GI.rank_grads(w, q, gbuf)
+        for q in [q for q in range(P - 1, -1, -1) if q != r] + [r]:
+            _, views = PL.rank_grads(w, q, gbuf)
             G.bucket_pack(plan, views, flats[q])
-        _, my_grads = GI.rank_grads(w, r, gbuf)      # the owner's own per-tensor gradients
-        contribs, layout = flats, G.LAYOUT_BUCKET_FLAT
+        contribs, lay = flats, G.LAYOUT_BUCKET_FLAT
+        my_grads = views                          # the owner's own per-tensor gradients (filled last)
         gathered, shard_out = torch.zeros(L, dtype=torch.uint16, device="cuda"), None
-    else:
-        contribs, layout = GI.compact_contribs(plan, w, r), G.LAYOUT_SHARD_COMPACT
+    elif layout == "compact":
+        contribs, lay = PL.compact_contribs(plan, w, r), G.LAYOUT_SHARD_COMPACT
         gathered, shard_out = None, torch.zeros(S, dtype=torch.uint16, device="cuda")
-    master, m, v = GI.owner_state(plan, w, r)
+    else:
+        contribs = [PL.interleaved_contribs(plan, w, r, G.interleaved_len(plan))]
+        lay = G.LAYOUT_RANK_INTERLEAVED
+        gathered, shard_out = None, torch.zeros(S, dtype=torch.uint16, device="cuda")
+    master, m, v = PL.owner_state(plan, w, r)
+    check_fill_launches(gen)
     g = torch.empty(S, dtype=torch.float32, device="cuda")
     ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
     partials = torch.zeros(P, dtype=torch.float64, device="cuda")
     coef = torch.empty(1, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    log(f"[gpu] inputs ready in {time.perf_counter() - t0:.1f} s "
-        f"({'bucket-flat' if flat_mode else 'shard-compact'} contributions); "
-        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
+    log(f"[gpu] inputs ready in {time.perf_counter() - t0:.1f} s ({layout} contributions, "
+        f"{gen.fill_launches} fill launches); {torch.cuda.memory_allocated() / 1e9:.1f} GB allocated")
 
     # The other ranks' partials come from the exchange that one GPU does not
     # perform; they are stand-ins equal to this shard's partial.
-    if flat_mode:
-        G.bucket_pack(plan, my_grads, flats[r])
-    G.shard_reduce_mean(plan, r, contribs, layout, g, partials[r:r + 1], ws)
+    G.shard_reduce_mean(plan, r, contribs, lay, g, partials[r:r + 1], ws)
     torch.cuda.synchronize()
     partials.fill_(float(partials[r]))
 
-    names = (["bucket_pack"] if flat_mode else []) + ["shard_reduce_mean", "clip_coef",
-                                                       "shard_adamw_step"]
-    launches = {"bucket_pack": -(-plan.n_tensors // 256), "shard_reduce_mean": 1,
-                "clip_coef": 1, "shard_adamw_step": 1}
-    nev = len(names) + 1
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    names = ["shard_reduce_mean", "clip_coef", "shard_adamw_step"]
+    calls = [lambda: G.shard_reduce_mean(plan, r, contribs, lay, g, partials[r:r + 1], ws),
+             lambda: G.clip_coef(partials, w.hp.max_norm, coef),
+             lambda: G.shard_adamw_step(plan, r, master, m, v, g, coef, w.hp, gathered, shard_out)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
 
     def step(e=None):
-        k = 0
-        if e: e[k].record()
-        if flat_mode:
-            G.bucket_pack(plan, my_grads, flats[r])
-            k += 1
+        for k, c in enumerate(calls):
             if e: e[k].record()
-        G.shard_reduce_mean(plan, r, contribs, layout, g, partials[r:r + 1], ws)
-        k += 1
-        if e: e[k].record()
-        G.clip_coef(partials, w.hp.max_norm, coef)
-        k += 1
-        if e: e[k].record()
-        G.shard_adamw_step(plan, r, master, m, v, g, coef, w.hp, gathered, shard_out)
-        k += 1
-        if e: e[k].record()
+            c()
+        if e: e[len(calls)].record()
 
     for _ in range(args.warmup):
         step()
@@ -591,8 +653,7 @@ def main():
     for k in range(args.steps):
         step(ev[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
     samples = {n: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]
                for i, n in enumerate(names)}
     per = {n: float(np.mean(v)) for n, v in samples.items()}
@@ -618,38 +679,27 @@ def main():
         graph_ms = (time.perf_counter() - t0) / args.steps * 1e3
         log(f"[gpu] captured step: {graph_ms:.3f} ms/step over {args.steps} replays")
 
-    # Algorithmic bytes (what the method must move), per call.
-    byts = {"bucket_pack": 4 * w.n_params + 2 * (L - w.n_params),
-            "shard_reduce_mean": (2 * P + 4) * S,
-            "clip_coef": 8 * P + 12,
+    # Algorithmic bytes (what the method must move), per call: the step's
+    # (2P + 34) bytes per shard element.
+    byts = {"shard_reduce_mean": (2 * P + 4) * S, "clip_coef": 8 * P + 12,
             "shard_adamw_step": 30 * S}
-    byts = {n: byts[n] for n in names}
     step_bytes = sum(byts.values())
     kern = {n: dict(ms=per[n], ms_median=float(np.median(samples[n])),
-                    ms_min=float(np.min(samples[n])), launches=launches[n],
+                    ms_min=float(np.min(samples[n])), launches=1,
                     GBps=byts[n] / (per[n] * 1e-3) / 1e9, bytes=byts[n]) for n in names}
     for n in names:
         kern[n]["frac"] = kern[n]["GBps"] / HBM_PEAK_GBPS
-    # The roofline names the longer of the metric's two kernels (reduce-mean and
-    # AdamW): a stable choice, where the longest call of the step (the pack's
-    # two launches and AdamW are within a few percent on the 7B share) is not.
+    # The roofline names the longer of the step's two data kernels.
     dom = max(("shard_reduce_mean", "shard_adamw_step"), key=lambda n: per[n])
-    dom_bytes = byts[dom] / launches[dom]
-    dom_ms = per[dom] / launches[dom]
+    dom_bytes, dom_ms = byts[dom], per[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    kernel_symbol = {"bucket_pack": "k_pack", "shard_reduce_mean": "k_reduce_mean",
-                     "clip_coef": "k_clip", "shard_adamw_step": "k_adamw"}[dom]
-    traffic = read_traffic(kernel_symbol, w.name)
+    kernel_symbol = {"shard_reduce_mean": "k_reduce_mean_ilv" if layout == "interleaved"
+                     else "k_reduce_mean", "shard_adamw_step": "k_adamw"}[dom]
+    traffic = read_traffic(kernel_symbol, profile_name(w.name, "zero", layout))
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
-    # The reduce-mean + AdamW shard step alone ((2P + 34) bytes per shard element).
-    fused_ms = per["shard_reduce_mean"] + per["clip_coef"] + per["shard_adamw_step"]
-    fused_gbps = (2 * P + 34) * S / (fused_ms * 1e-3) / 1e9
-    log(f"[gpu] {ms_step:.3f} ms/step; " + "; ".join(
+    log(f"[gpu] {ms_step:.3f} ms/step, {step_gbps:.0f} GB/s; " + "; ".join(
         f"{n} {kern[n]['ms']:.3f} ms {kern[n]['GBps']:.0f} GB/s" for n in names))
 
-    # The standalone forms of two rows the step runs fused: the squared norm of
-    # g (fused into the reduce) and the all-gather layout writer (fused into
-    # the AdamW store).
     def time_call(fn, reps=5):
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -660,24 +710,31 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    # The other rows of the path, standalone: the pack (the first part of the
+    # rank's share; in the flat layout the owner's own gradients into its flat
+    # buffer, otherwise a window of the model that fits beside the 138 GB of
+    # contributions), the squared norm of g (fused into the reduce on the
+    # step), the all-gather layout writer (fused into the AdamW store), and the
+    # rows beyond the step.
     shard_bf16 = torch.zeros(S, dtype=torch.uint16, device="cuda")
     part1 = torch.zeros(1, dtype=torch.float64, device="cuda")
+    g_step = g.clone()                 # the step's reduced gradient, kept for the layout check
     standalone = {}
     rows = [("shard_grad_sqnorm", lambda: G.shard_grad_sqnorm(g, part1, ws), 4 * S),
             ("shard_reduce_mean_bf16_wire",
-             lambda: G.shard_reduce_mean(plan, r, contribs, layout, g, part1, ws, bf16_wire=True),
+             lambda: G.shard_reduce_mean(plan, r, contribs, lay, g, part1, ws, bf16_wire=True),
              (2 * P + 4) * S)]
-    if gathered is not None:
+    if my_grads is not None:
+        rows.append(("bucket_pack", lambda: G.bucket_pack(plan, my_grads, contribs[r]),
+                     4 * w.n_params + 2 * (L - w.n_params)))
         rows.append(("allgather_layout_write",
                      lambda: G.allgather_layout_write(plan, r, shard_bf16, gathered), 4 * S))
-    if flat_mode:
         rows.append(("bucket_accumulate",
-                     lambda: G.bucket_accumulate(plan, my_grads, flats[r]), 6 * w.n_params))
-    if not flat_mode:
+                     lambda: G.bucket_accumulate(plan, my_grads, contribs[r]), 6 * w.n_params))
+    else:
         # The owner's pack on a window of the model: the trailing tensors that
         # fill its first 20 buckets (the plan of those tensors alone has the same
-        # buckets).  The whole model's gradients and flat buffer would not fit
-        # beside the P contributions.
+        # buckets).
         nb_win = min(20, plan.n_buckets)
         last = plan.bucket(nb_win - 1)
         t_min = last["first_tensor"] - last["n_tensors"] + 1
@@ -685,7 +742,7 @@ def main():
         wn = sum(w.numel[t_min:])
         wbuf = torch.empty(wn, dtype=torch.uint16, device="cuda")
         wgrads = list(torch.split(wbuf, w.numel[t_min:]))
-        GI.fill_pieces(wbuf, [(0, sum(w.numel[:t_min]), wn)], w, W.KIND_GRAD, r, w.grad_std,
+        PL.fill_pieces(wbuf, [(0, sum(w.numel[:t_min]), wn)], w, W.KIND_GRAD, r, w.grad_std,
                        gen.MODE_BF16)
         wflat = torch.empty(wplan.flat_len, dtype=torch.uint16, device="cuda")
         rows.append((f"bucket_pack_window{nb_win}",
@@ -693,16 +750,14 @@ def main():
                      4 * wn + 2 * (wplan.flat_len - wn)))
         log(f"[gpu] pack window: the first {nb_win} buckets, tensors {t_min}..{len(w.numel) - 1}, "
             f"{wn} params")
+    check_fill_launches(gen)
     for name, fn, nbytes in rows:
         ms = time_call(fn)
         standalone[name] = dict(ms=ms, bytes=nbytes, GBps=nbytes / (ms * 1e-3) / 1e9,
                                 frac=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS)
     # fp32 accumulation buckets and the reduce over fp32 contributions, when
-    # their buffers fit beside the working set: one fp32 flat buffer for the
-    # accumulation (10 bytes per parameter: bf16 gradient in, fp32 bucket in and
-    # out) and P shard-compact fp32 contributions for the reduce (4P + 4 bytes
-    # per shard element).
-    if flat_mode and 4 * L < 0.8 * torch.cuda.mem_get_info()[0]:
+    # their buffers fit beside the working set.
+    if my_grads is not None and 4 * L < 0.8 * torch.cuda.mem_get_info()[0]:
         f32 = torch.zeros(L, dtype=torch.float32, device="cuda")
         G.bucket_pack_f32(plan, my_grads, f32)
         ms = time_call(lambda: G.bucket_accumulate_f32(plan, my_grads, f32))
@@ -724,6 +779,59 @@ def main():
                                          for n, v in standalone.items()))
     del shard_bf16
 
+    # The reduce's own read pattern without arithmetic: the first 2*S bytes of
+    # each of the P contribution buffers read at the same offsets (or the one
+    # interleaved buffer read straight through).
+    nbs = 2 * S // 16 * 16
+    sink = torch.empty(max(gen.probe_out_words(nbs), gen.probe_out_words(P * nbs)),
+                       dtype=torch.int32, device="cuda")
+    ceil = {}
+
+    def probe(name, fn, nbytes):
+        for _ in range(2):
+            fn()
+        ceil[name] = nbytes / (time_call(fn, reps=10) * 1e-3) / 1e9
+
+    if layout == "interleaved":
+        probe("read_interleaved", lambda: gen.dev_read(contribs[0], sink, P * nbs), P * nbs)
+    else:
+        probe(f"read_{P}_streams", lambda: gen.dev_read_streams(contribs, nbs, sink), P * nbs)
+
+    # The other receive layout, timed in the same process when both do not fit
+    # at once: the reduce (with its norm partial) over the same values in one
+    # rank-interleaved buffer, its result checked bit for bit against the
+    # step's g.  Allocated after the first layout's buffers are freed.
+    other = None
+    if layout in ("compact", "flat") and not args.no_interleaved:
+        del contribs
+        if layout == "flat":
+            del flats, gbuf, views, my_grads
+        torch.cuda.empty_cache()
+        ibuf = PL.interleaved_contribs(plan, w, r, G.interleaved_len(plan))
+        check_fill_launches(gen)
+        icall = lambda: G.shard_reduce_mean(plan, r, [ibuf], G.LAYOUT_RANK_INTERLEAVED, g,  # noqa: E731
+                                            part1, ws)
+        icall()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(g.view(torch.int32), g_step.view(torch.int32)))
+        ims = time_call(icall, reps=max(5, args.steps // 2))
+        probe("read_interleaved", lambda: gen.dev_read(ibuf, sink, P * nbs), P * nbs)
+        nbytes = (2 * P + 4) * S
+        fused = ims + per["clip_coef"] + per["shard_adamw_step"]
+        other = {"layout": "rank-interleaved (one receive buffer, 512-element pieces per rank)",
+                 "shard_reduce_mean": dict(ms=ims, bytes=nbytes, GBps=nbytes / (ims * 1e-3) / 1e9,
+                                           frac=nbytes / (ims * 1e-3) / 1e9 / HBM_PEAK_GBPS),
+                 "g_bit_identical_to_step": same,
+                 "step_ms_with_this_reduce": fused,
+                 "step_frac_with_this_reduce": step_bytes / (fused * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        log(f"[gpu] interleaved receive buffer: reduce {ims:.3f} ms "
+            f"{nbytes / (ims * 1e-3) / 1e9:.0f} GB/s, g identical: {same}")
+        del ibuf
+        torch.cuda.empty_cache()
+    else:
+        del contribs
+    del sink, g_step
+
     # Plain streaming probes in the kernels' launch shape, run after the timed
     # steps so that their allocations do not fragment the memory the working set
     # was placed in: copy (the practical ceiling for half-read/half-write traffic
@@ -732,22 +840,10 @@ def main():
     a = torch.empty(nb // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
-    # the reduce's own pattern without arithmetic: the first 2*S bytes of each
-    # of the P contribution buffers, read at the same offsets
-    nbs = 2 * S // 16 * 16
-    sink = torch.empty(max(gen.probe_out_words(nb), gen.probe_out_words(nbs)), dtype=torch.int32,
-                       device="cuda")
-    ceil = {}
-    for name, fn, nbytes in (("copy", lambda: gen.dev_copy(a, b, nb), 2 * nb),
-                             ("read", lambda: gen.dev_read(a, sink, nb), nb),
-                             ("write", lambda: gen.dev_write(b, nb), nb),
-                             (f"read_{P}_streams",
-                              lambda: gen.dev_read_streams(contribs, nbs, sink), P * nbs)):
-        for _ in range(2):
-            fn()
-        ms = time_call(fn, reps=10)
-        ceil[name] = nbytes / (ms * 1e-3) / 1e9
-    copy_gbps = ceil["copy"]
+    sink = torch.empty(gen.probe_out_words(nb), dtype=torch.int32, device="cuda")
+    probe("copy", lambda: gen.dev_copy(a, b, nb), 2 * nb)
+    probe("read", lambda: gen.dev_read(a, sink, nb), nb)
+    probe("write", lambda: gen.dev_write(b, nb), nb)
     del a, b, sink
     log("[gpu] streaming ceilings (GB/s): " + ", ".join(f"{k} {v:.0f}" for k, v in ceil.items()))
 
@@ -768,22 +864,21 @@ def main():
         "config": {"workload": w.name, "world_size_P": P, "owner": r, "model_params": w.n_params,
                    "shard_params": S, "bucket_cap_MiB": w.bucket_cap_bytes // (1 << 20),
                    "buckets": plan.n_buckets,
-                   "contribution_layout": "bucket-flat" if flat_mode else "shard-compact",
+                   "contribution_layout": {"flat": "bucket-flat", "compact": "shard-compact",
+                                           "interleaved": "rank-interleaved"}[layout],
                    "precision": "bf16 grads/params, fp32 accumulation and master/m/v",
-                   "step": " + ".join(names) + (" (all-gather layout)" if flat_mode
+                   "step": " + ".join(names) + (" (all-gather layout)" if gathered is not None
                                                  else " (shard-layout bf16)")},
         "graph_ms_per_step": graph_ms,
         "step_ms_gpu": step_gpu,
-        "reduce_adamw_ms": fused_ms,
-        "reduce_adamw_GBps": fused_gbps,
-        "reduce_adamw_frac_of_peak": fused_gbps / HBM_PEAK_GBPS,
         "hbm_GBps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "step_bytes": step_bytes,
-        "copy_ceiling_GBps": copy_gbps,
+        "copy_ceiling_GBps": ceil["copy"],
         "streaming_ceilings_GBps": ceil,
-        "kernels_standalone": standalone,
         "kernels": kern,
+        "kernels_standalone": standalone,
+        "other_layout": other,
         "roofline": {"bound": "hbm", "kernel": kernel_symbol, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_launch": dom_bytes,

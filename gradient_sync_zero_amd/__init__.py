@@ -5,7 +5,8 @@ The work runs in libgsz.so (HIP kernels behind a C ABI, include/gsz.h); this
 package is its ctypes binding and raises ImportError if the library is not
 built.
 """
-from ._binding import (AdamWHP, GszError, LAYOUT_BUCKET_FLAT, LAYOUT_SHARD_COMPACT, LIB_PATH,
+from ._binding import (AdamWHP, GszError, INTERLEAVE_PIECE, LAYOUT_BUCKET_FLAT,
+                       LAYOUT_RANK_INTERLEAVED, LAYOUT_SHARD_COMPACT, LIB_PATH, interleaved_len,
                        MAX_RANKS, Plan, adamw_step, allgather_layout_write, allreduce_mean,
                        bucket_accumulate, bucket_accumulate_f32, bucket_pack, bucket_pack_f32,
                        bucket_unpack, clip_coef, load, ledger_bytes_per_param, make_hp,
@@ -15,7 +16,8 @@ from . import _binding
 
 load()
 
-__all__ = ["AdamWHP", "GszError", "LAYOUT_BUCKET_FLAT", "LAYOUT_SHARD_COMPACT", "LIB_PATH",
+__all__ = ["AdamWHP", "GszError", "INTERLEAVE_PIECE", "LAYOUT_BUCKET_FLAT",
+           "LAYOUT_RANK_INTERLEAVED", "LAYOUT_SHARD_COMPACT", "LIB_PATH", "interleaved_len",
            "MAX_RANKS", "Plan", "adamw_step", "allgather_layout_write", "allreduce_mean",
            "bucket_accumulate", "bucket_accumulate_f32", "bucket_pack", "bucket_pack_f32",
            "bucket_unpack", "clip_coef", "ledger_bytes_per_param", "make_hp", "set_grid_limit",

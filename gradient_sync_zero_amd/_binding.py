@@ -20,6 +20,8 @@ TEST_LIB_PATH = os.path.join(_HERE, "libgsz_test.so")
 
 LAYOUT_BUCKET_FLAT = 0
 LAYOUT_SHARD_COMPACT = 1
+LAYOUT_RANK_INTERLEAVED = 2
+INTERLEAVE_PIECE = 512
 MAX_RANKS = 256
 
 _STATUS = {0: "GSZ_OK", -1: "GSZ_ERR_INVALID_ARG", -2: "GSZ_ERR_MISALIGNED", -3: "GSZ_ERR_SIZE",
@@ -183,15 +185,35 @@ def _ptr(t, name, dtypes, allow_none=False, min_numel=None, numel=None):
     return t.data_ptr()
 
 
+def interleaved_len(plan):
+    """Elements of the one receive buffer of the rank-interleaved layout: P
+    pieces of INTERLEAVE_PIECE per started tile of the shard."""
+    tiles = -(-plan.shard_len // INTERLEAVE_PIECE)
+    return plan.world_size * tiles * INTERLEAVE_PIECE
+
+
 def _contrib_len(plan, layout):
-    """Elements each contribution must hold: the whole bucket-flat buffer, or
-    the owner's shard in shard-compact layout (unknown layouts are left to the
-    library, which rejects them)."""
+    """Elements each contribution must hold: the whole bucket-flat buffer, the
+    owner's shard in shard-compact layout, or the interleaved receive buffer
+    (unknown layouts are left to the library, which rejects them)."""
     if layout == LAYOUT_BUCKET_FLAT:
         return plan.flat_len
     if layout == LAYOUT_SHARD_COMPACT:
         return plan.shard_len
+    if layout == LAYOUT_RANK_INTERLEAVED:
+        return interleaved_len(plan)
     return None
+
+
+def _contrib_ptrs(plan, contribs, layout, dtypes):
+    """Host array of contribution pointers: one per rank, or the single
+    receive buffer of the rank-interleaved layout."""
+    n = 1 if layout == LAYOUT_RANK_INTERLEAVED else plan.world_size
+    if len(contribs) != n:
+        raise ValueError(f"need {n} contribution buffer(s) for layout {layout}, got {len(contribs)}")
+    clen = _contrib_len(plan, layout)
+    return (_P * n)(*[_ptr(t, f"contribs[{i}]", dtypes, min_numel=clen)
+                      for i, t in enumerate(contribs)])
 
 
 def _bf16_types():
@@ -355,11 +377,7 @@ def bucket_accumulate_f32(plan, grads, flat32, stream=None):
 
 def shard_reduce_mean_f32(plan, owner, contribs, layout, g, partial_out=None, ws=None, stream=None):
     """gsz_shard_reduce_mean_f32: the ring-order mean of P fp32 contributions."""
-    if len(contribs) != plan.world_size:
-        raise ValueError("need one contribution per rank")
-    clen = _contrib_len(plan, layout)
-    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", _f32(), min_numel=clen)
-                                  for i, t in enumerate(contribs)])
+    ptrs = _contrib_ptrs(plan, contribs, layout, _f32())
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(_lib_for(plan).gsz_shard_reduce_mean_f32(plan.handle, owner, ptrs, layout,
@@ -373,12 +391,7 @@ def shard_reduce_mean_f32(plan, owner, contribs, layout, g, partial_out=None, ws
 def shard_reduce_mean(plan, owner, contribs, layout, g, partial_out=None, ws=None, stream=None,
                       bf16_wire=False):
     """gsz_shard_reduce_mean (or gsz_shard_reduce_mean_bf16_wire when bf16_wire)."""
-    bt = _bf16_types()
-    if len(contribs) != plan.world_size:
-        raise ValueError("need one contribution per rank")
-    clen = _contrib_len(plan, layout)
-    ptrs = (_P * len(contribs))(*[_ptr(t, f"contribs[{i}]", bt, min_numel=clen)
-                                  for i, t in enumerate(contribs)])
+    ptrs = _contrib_ptrs(plan, contribs, layout, _bf16_types())
     wsp = _ptr(ws, "ws", (ws.dtype,) if ws is not None else (), allow_none=True)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     lib = _lib_for(plan)

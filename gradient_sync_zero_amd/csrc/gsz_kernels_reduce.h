@@ -19,6 +19,26 @@ constexpr int load_group(int ps, int cap) {
 
 // ---------------------------------------------------------- reduce-mean --
 
+// Contribution layouts as the reduce kernels see them: bucket-flat (the
+// owner's chunks read through the plan's segments), shard-compact (index i of
+// every contribution), or rank-interleaved (one receive buffer in which rank
+// q's values for shard elements [512t, 512t + 512) sit at (t*P + q)*512; the
+// host passes p[k] = buffer + q_k * 512, so index i reads p[k] + ilv_index(i)).
+constexpr int kLayFlat = 0, kLayCompact = 1, kLayInterleaved = 2;
+constexpr int64_t kIlvPiece = 512;
+static_assert(kIlvPiece == GSZ_INTERLEAVE_PIECE, "the header's piece size");
+
+__device__ __forceinline__ int64_t ilv_index(int64_t i, int P) {
+    return (i >> 9) * ((int64_t)P << 9) + (i & (kIlvPiece - 1));
+}
+
+template <int LAY>
+__device__ __forceinline__ int64_t contrib_index(SegCursor& cur, int64_t i, int P) {
+    if constexpr (LAY == kLayFlat) return cur.map(i);
+    else if constexpr (LAY == kLayInterleaved) return ilv_index(i, P);
+    else return i;
+}
+
 // g[i] = (((c0 + c1) + c2) + ... + c_{P-1}) / P with rp.p[k] = contribution of
 // rank (owner+1+k) mod P, so the owner's own value is added last.  Each lane
 // handles 8 consecutive shard elements per iteration (one 16-byte load per
@@ -30,8 +50,9 @@ constexpr int load_group(int ps, int cap) {
 // wire carries bf16 partial sums); the final division stays fp32.  Loads and
 // stores are nontemporal (2% faster at P = 8, 5% at P = 64 than plain ones).
 // This kernel serves P > 16 (compile-time P for 24, 32, 64 and 96, its
-// runtime-P loop for the others); P <= 16 runs k_reduce_mean_lc below.
-template <int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
+// runtime-P loop for the others); P <= 16 runs k_reduce_mean_lc below.  LAY
+// is one of the layouts above (kLayFlat for OUTFLAT).
+template <int PS, bool NORM, int LAY, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
                                                         const int64_t* __restrict__ seg,
                                                         const uint64_t* __restrict__ slut, int sshift,
@@ -41,13 +62,15 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);      // logical block: tile bx
     int64_t v = bx * kBlock + threadIdx.x;
+    constexpr bool FLAT = LAY == kLayFlat;
+    static_assert(!OUTFLAT || FLAT, "the all-gather-position output reads bucket-flat input");
     double sq = 0.0;
     SegCursor cur{seg, owner, 0, 0, 0};
     if (FLAT && v < nvec) cur.seek(bx * kRedTile, slut, sshift);      // uniform: scalar loads
     const float fP = (float)P;
     for (; v < nvec; v += stride) {
         const int64_t i = v * 8;
-        const int64_t off = FLAT ? cur.map(i) : i;
+        const int64_t off = contrib_index<LAY>(cur, i, PS > 0 ? PS : P);
         float a[8];
         if constexpr (PS > 0) {
             // up to 32 loads before their adds (at P = 64 that measured 1.4% faster than 16)
@@ -110,14 +133,16 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
 // 9% more write bytes, and this layout is 4-5% faster at P = 8-16.  At P = 64
 // its twice as many (half-size) bf16 loads make it 6-7% slower, so the larger
 // P keep k_reduce_mean.  OUTFLAT and W16 as there; blocks, XCD order and norm
-// partials as there.
-template <typename T, int PS, bool NORM, bool FLAT, bool OUTFLAT = false, bool W16 = false>
+// partials as there; LAY as there.
+template <typename T, int PS, bool NORM, int LAY, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int P, float invP, int pow2,
                                                            const int64_t* __restrict__ seg,
                                                            const uint64_t* __restrict__ slut, int sshift,
                                                            int64_t owner, int64_t S,
                                                            float* __restrict__ g,
                                                            double* __restrict__ ws) {
+    constexpr bool FLAT = LAY == kLayFlat;
+    static_assert(!OUTFLAT || FLAT, "the all-gather-position output reads bucket-flat input");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);
     double sq = 0.0;
@@ -132,8 +157,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int 
         // Past the end a lane reads position 0 of each contribution (in bounds) and
         // discards the result: loads under a condition became one branch and one
         // full wait per load, serialising them.
-        const int64_t off0 = ok0 ? (FLAT ? cur.map(i0) : i0) : 0;
-        const int64_t off1 = ok1 ? (FLAT ? cur.map(i1) : i1) : 0;
+        const int64_t off0 = ok0 ? contrib_index<LAY>(cur, i0, PS > 0 ? PS : P) : 0;
+        const int64_t off1 = ok1 ? contrib_index<LAY>(cur, i1, PS > 0 ? PS : P) : 0;
         f32x4 a = zero, b = zero;
         if constexpr (PS > 0) {
             constexpr int G = load_group(PS, 16);

@@ -164,30 +164,41 @@ void with_static_p(int P, F&& f) {
     f(std::integral_constant<int, 0>{});
 }
 
+// Calls go(Lay{}) with Lay = std::integral_constant<int, lay> for the three
+// contribution layouts.
+template <class F>
+void with_layout(int lay, F&& go) {
+    if (lay == kLayFlat) go(std::integral_constant<int, kLayFlat>{});
+    else if (lay == kLayCompact) go(std::integral_constant<int, kLayCompact>{});
+    else go(std::integral_constant<int, kLayInterleaved>{});
+}
+
 // Launches k_reduce_mean<PS, ...> with the flags as template arguments (the
-// combinations the entry points use).
+// combinations the entry points use): lay is a kLay* layout; outflat (the
+// all-reduce's flat-position output) needs bucket-flat input.
 template <int PS>
-void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPtrs& rp, int P,
+void launch_reduce(bool norm, int lay, dim3 grid, hipStream_t st, const RankPtrs& rp, int P,
                    float invP, int pow2, const int64_t* seg, const uint64_t* slut, int sshift,
                    int64_t owner, int64_t nvec, float* g, double* ws, bool outflat = false,
                    bool wire16 = false) {
-    auto go = [&](auto nm, auto fl, auto of, auto w16) {
-        hipLaunchKernelGGL((k_reduce_mean<PS, decltype(nm)::value, decltype(fl)::value,
+    auto go = [&](auto nm, auto ly, auto of, auto w16) {
+        hipLaunchKernelGGL((k_reduce_mean<PS, decltype(nm)::value, decltype(ly)::value,
                                           decltype(of)::value, decltype(w16)::value>),
                            grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner,
                            nvec, g, ws);
     };
     using Y = std::true_type;
     using N = std::false_type;
+    using Flat = std::integral_constant<int, kLayFlat>;
     auto layouts = [&](auto w16) {
-        if (norm && flat) go(Y{}, Y{}, N{}, w16);
-        else if (norm) go(Y{}, N{}, N{}, w16);
-        else if (flat) go(N{}, Y{}, N{}, w16);
-        else go(N{}, N{}, N{}, w16);
+        with_layout(lay, [&](auto ly) {
+            if (norm) go(Y{}, ly, N{}, w16);
+            else go(N{}, ly, N{}, w16);
+        });
     };
     if (outflat) {
-        if (norm) go(Y{}, Y{}, Y{}, N{});
-        else go(N{}, Y{}, Y{}, N{});
+        if (norm) go(Y{}, Flat{}, Y{}, N{});
+        else go(N{}, Flat{}, Y{}, N{});
     } else if (wire16) {
         layouts(Y{});
     } else {
@@ -201,31 +212,32 @@ void launch_reduce(bool norm, bool flat, dim3 grid, hipStream_t st, const RankPt
 constexpr int kLcMaxP = 16;
 
 template <typename T, int PS>
-void launch_reduce_lc(bool norm, bool flat, bool outflat, bool wire16, dim3 grid, hipStream_t st,
+void launch_reduce_lc(bool norm, int lay, bool outflat, bool wire16, dim3 grid, hipStream_t st,
                       const RankPtrsT<T>& rp, int P, float invP, int pow2, const int64_t* seg,
                       const uint64_t* slut, int sshift, int64_t owner, int64_t S, float* g,
                       double* ws) {
     const size_t lds = (int64_t)P * (int64_t)sizeof(T) >= kRedLcLdsMinBytes ? kRedLcLdsBytes : 0;
-    auto go = [&](auto nm, auto fl, auto of, auto w16) {
-        hipLaunchKernelGGL((k_reduce_mean_lc<T, PS, decltype(nm)::value, decltype(fl)::value,
+    auto go = [&](auto nm, auto ly, auto of, auto w16) {
+        hipLaunchKernelGGL((k_reduce_mean_lc<T, PS, decltype(nm)::value, decltype(ly)::value,
                                              decltype(of)::value, decltype(w16)::value>),
                            grid, dim3(kBlock), lds, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g,
                            ws);
     };
     using Y = std::true_type;
     using N = std::false_type;
+    using Flat = std::integral_constant<int, kLayFlat>;
     auto layouts = [&](auto w16) {
-        if (norm && flat) go(Y{}, Y{}, N{}, w16);
-        else if (norm) go(Y{}, N{}, N{}, w16);
-        else if (flat) go(N{}, Y{}, N{}, w16);
-        else go(N{}, N{}, N{}, w16);
+        with_layout(lay, [&](auto ly) {
+            if (norm) go(Y{}, ly, N{}, w16);
+            else go(N{}, ly, N{}, w16);
+        });
     };
     if constexpr (std::is_same<T, float>::value) {
         layouts(N{});                            // fp32 contributions: the reduce rows only
     } else {
         if (outflat) {
-            if (norm) go(Y{}, Y{}, Y{}, N{});
-            else go(N{}, Y{}, Y{}, N{});
+            if (norm) go(Y{}, Flat{}, Y{}, N{});
+            else go(N{}, Flat{}, Y{}, N{});
         } else if (wire16) {
             layouts(Y{});
         } else {
@@ -370,11 +382,15 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
     int rc = check_plan(p, who);
     if (rc) return rc;
     if ((rc = check_owner(p, owner, who))) return rc;
-    if (layout != GSZ_LAYOUT_BUCKET_FLAT && layout != GSZ_LAYOUT_SHARD_COMPACT) {
+    if (layout != GSZ_LAYOUT_BUCKET_FLAT && layout != GSZ_LAYOUT_SHARD_COMPACT &&
+        layout != GSZ_LAYOUT_RANK_INTERLEAVED) {
         set_error("%s: unknown layout %d", who, layout); return GSZ_ERR_INVALID_ARG;
     }
     const int P = p->P;
     const int64_t S = p->shard_len;
+    // The interleaved layout passes one receive buffer; the others P buffers.
+    const bool ilv = layout == GSZ_LAYOUT_RANK_INTERLEAVED;
+    const int n_ptrs = ilv ? 1 : P;
     if (partial_out) {
         size_t need = 0;
         gsz_workspace_bytes(S, &need);
@@ -384,36 +400,42 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
     if (S > 0) {
         if (!g || !contrib) { set_error("%s: NULL buffer", who); return GSZ_ERR_INVALID_ARG; }
         if (misaligned(g)) { set_error("%s: g is not 16-byte aligned", who); return GSZ_ERR_MISALIGNED; }
-        for (int q = 0; q < P; ++q) {
+        for (int q = 0; q < n_ptrs; ++q) {
             if (!contrib[q]) { set_error("%s: contribution %d is NULL", who, q); return GSZ_ERR_INVALID_ARG; }
             if (misaligned(contrib[q])) { set_error("%s: contribution %d is not 16-byte aligned", who, q); return GSZ_ERR_MISALIGNED; }
         }
     }
     const int64_t nvec = S / 8;
     const int grid = flat_grid((S + kRedTile - 1) / kRedTile);
+    const int lay = layout == GSZ_LAYOUT_BUCKET_FLAT ? kLayFlat : ilv ? kLayInterleaved : kLayCompact;
+    // p[k] = the contribution of rank (owner + 1 + k) mod P: its buffer, or its
+    // piece of the first tile of the interleaved buffer.
+    auto rank_ptr = [&](int k, size_t esize) -> const void* {
+        const int q = (owner + 1 + k) % P;
+        if (!ilv) return contrib[q];
+        return static_cast<const char*>(contrib[0]) + (size_t)q * kIlvPiece * esize;
+    };
     if (S > 0 && f32in) {
         RankPtrsF rp{};
-        for (int k = 0; k < P; ++k) rp.p[k] = static_cast<const float*>(contrib[(owner + 1 + k) % P]);
+        for (int k = 0; k < P; ++k) rp.p[k] = static_cast<const float*>(rank_ptr(k, sizeof(float)));
         const int pow2 = (P & (P - 1)) == 0;
         const float invP = pow2 ? 1.0f / (float)P : 0.0f;
         const bool norm = partial_out != nullptr;
-        const bool flat = layout == GSZ_LAYOUT_BUCKET_FLAT;
         const uint64_t* slut = p->d_seg_lut;
         const int sshift = p->seg_lut.shift;
         double* wsd = static_cast<double*>(ws);
         with_static_p(P, [&](auto ps) {
-            launch_reduce_lc<float, decltype(ps)::value>(norm, flat, false, false, dim3(grid), stream,
+            launch_reduce_lc<float, decltype(ps)::value>(norm, lay, false, false, dim3(grid), stream,
                                                          rp, P, invP, pow2, p->d_seg, slut, sshift,
                                                          owner, S, g, wsd);
         });
         if ((rc = launched(who))) return rc;
     } else if (S > 0) {
         RankPtrs rp{};
-        for (int k = 0; k < P; ++k) rp.p[k] = static_cast<const uint16_t*>(contrib[(owner + 1 + k) % P]);
+        for (int k = 0; k < P; ++k) rp.p[k] = static_cast<const uint16_t*>(rank_ptr(k, sizeof(uint16_t)));
         const int pow2 = (P & (P - 1)) == 0;
         const float invP = pow2 ? 1.0f / (float)P : 0.0f;
         const bool norm = partial_out != nullptr;
-        const bool flat = layout == GSZ_LAYOUT_BUCKET_FLAT;
         const uint64_t* slut = p->d_seg_lut;
         const int sshift = p->seg_lut.shift;
         double* wsd = static_cast<double*>(ws);
@@ -421,11 +443,11 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
             constexpr int PS = decltype(ps)::value;
             auto lc = [&](auto pc) {
                 launch_reduce_lc<uint16_t, decltype(pc)::value>(
-                    norm, flat, false, wire16, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
+                    norm, lay, false, wire16, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
                     sshift, owner, S, g, wsd);
             };
             auto wide = [&](auto pc) {
-                launch_reduce<decltype(pc)::value>(norm, flat, dim3(grid), stream, rp, P, invP, pow2,
+                launch_reduce<decltype(pc)::value>(norm, lay, dim3(grid), stream, rp, P, invP, pow2,
                                                    p->d_seg, slut, sshift, owner, nvec, g, wsd,
                                                    false, wire16);
             };
@@ -606,11 +628,11 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
             constexpr int PS = decltype(ps)::value;
             auto lc = [&](auto pc) {
                 launch_reduce_lc<uint16_t, decltype(pc)::value>(
-                    norm, true, true, false, gr, stream, rp, P, invP, pow2, p->d_seg, slut, sshift, c,
+                    norm, kLayFlat, true, false, gr, stream, rp, P, invP, pow2, p->d_seg, slut, sshift, c,
                     S, g_flat, wsd);
             };
             auto wide = [&](auto pc) {
-                launch_reduce<decltype(pc)::value>(norm, true, gr, stream, rp, P, invP, pow2, p->d_seg,
+                launch_reduce<decltype(pc)::value>(norm, kLayFlat, gr, stream, rp, P, invP, pow2, p->d_seg,
                                                    slut, sshift, c, nvec, g_flat, wsd, true);
             };
             if constexpr (PS > kLcMaxP) wide(ps);

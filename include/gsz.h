@@ -74,6 +74,16 @@ typedef enum gsz_status {
                                        of bucket b is read at base_b + owner*C_b     */
 #define GSZ_LAYOUT_SHARD_COMPACT 1  /* contrib[q]: the shard_len elements rank q
                                        sends to this owner, chunks in bucket order   */
+#define GSZ_LAYOUT_RANK_INTERLEAVED 2
+                                    /* contrib[0] (one pointer): a single receive
+                                       buffer of P * ceil(S / 512) * 512 elements in
+                                       which rank q's values for shard elements
+                                       [512t, 512t + 512) sit at (t*P + q)*512 (the
+                                       last tile's pieces are full slots, their
+                                       tails unread); contrib[1..] are not read.
+                                       One tile's P pieces are one contiguous
+                                       stretch, so the reduce streams one buffer.   */
+#define GSZ_INTERLEAVE_PIECE 512     /* elements per rank piece of the layout above */
 
 typedef struct gsz_plan gsz_plan;
 

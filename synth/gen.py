@@ -68,7 +68,8 @@ def _load_dev():
         lib.synth_fill_dev.restype = ctypes.c_int
         lib.synth_fill_dev_pieces.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
                                               ctypes.c_int, ctypes.c_int64, ctypes.c_float,
-                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_void_p]
         lib.synth_fill_dev_pieces.restype = ctypes.c_int
         lib.synth_copy_dev.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int, ctypes.c_void_p]
@@ -127,8 +128,15 @@ def host_fill_idx(cfg_id, kind, rank, idx, std, mode, seed=None):
     return out
 
 
+# Device fill launches issued by this process (dev_fill and dev_fill_pieces).
+# Benchmarks and profiled commands keep this small: they place every buffer
+# with one piece-table launch.
+fill_launches = 0
+
+
 def dev_fill(out, cfg_id, kind, rank, start, std, mode, seed=None, stream=None):
     """Fill the contiguous device tensor `out` with value(start + i)."""
+    global fill_launches
     import torch
     from .workloads import SEED
     seed = SEED if seed is None else seed
@@ -140,23 +148,38 @@ def dev_fill(out, cfg_id, kind, rank, start, std, mode, seed=None, stream=None):
                                     scale_for(std), mode, out.data_ptr(), s)
     if rc != 0:
         raise RuntimeError(f"synth_fill_dev failed ({rc})")
+    fill_launches += 1
     return out
 
 
-def dev_fill_pieces(out, pieces, cfg_id, kind, rank, std, mode, seed=None):
+def interleaved_place(d, P, q):
+    """Index of rank q's value for shard element d in a rank-interleaved
+    receive buffer of P ranks (pieces of 512 elements)."""
+    return ((d >> 9) * P + q) * 512 + (d & 511)
+
+
+def dev_fill_pieces(out, pieces, cfg_id, kind, rank, std, mode, seed=None, interleave=None):
     """out[dst + j] = value(param + j), j < n, for every (dst, param, n) in pieces,
     in one launch on the current stream; elements no piece covers are left as
-    they are.  The piece table is a device tensor on the same stream, so the
-    caching allocator reuses its memory only after the launch."""
+    they are.  With interleave = (P, q) the values go to
+    out[interleaved_place(dst + j, P, q)] instead.  The piece table is a device
+    tensor on the same stream, so the caching allocator reuses its memory only
+    after the launch."""
+    global fill_launches
     import torch
     from .workloads import SEED
     seed = SEED if seed is None else seed
     want = torch.uint16 if mode == MODE_BF16 else torch.float32
     if out.dtype != want or not out.is_contiguous() or not out.is_cuda:
         raise ValueError("dev_fill_pieces needs a contiguous device tensor of the mode's dtype")
+    ilv_P, ilv_q = interleave if interleave is not None else (0, 0)
+    if interleave is not None and not 0 <= ilv_q < ilv_P:
+        raise ValueError(f"interleave rank {ilv_q} outside [0, {ilv_P})")
     rows, cum = [], 0
     for dst, param, n in pieces:
-        if n < 0 or dst < 0 or param < 0 or dst + n > out.numel():
+        last = dst + n - 1
+        end = (interleaved_place(last, ilv_P, ilv_q) if ilv_P else last) + 1
+        if n < 0 or dst < 0 or param < 0 or (n > 0 and end > out.numel()):
             raise ValueError(f"piece ({dst}, {param}, {n}) does not fit a tensor of {out.numel()}")
         rows += [cum, dst, param]
         cum += n
@@ -166,9 +189,11 @@ def dev_fill_pieces(out, pieces, cfg_id, kind, rank, std, mode, seed=None):
     tab = torch.tensor(rows, dtype=torch.int64).to(out.device)
     rc = _load_dev().synth_fill_dev_pieces(seed, key1(cfg_id, kind, rank), tab.data_ptr(),
                                            len(pieces), cum, scale_for(std), mode,
-                                           out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                                           out.data_ptr(), ilv_P, ilv_q,
+                                           torch.cuda.current_stream().cuda_stream)
     if rc != 0:
         raise RuntimeError(f"synth_fill_dev_pieces failed ({rc})")
+    fill_launches += 1
     return out
 
 

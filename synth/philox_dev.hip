@@ -55,13 +55,21 @@ __global__ void synth_fill_kernel(uint32_t seed, uint32_t key1, uint64_t start, 
         synth_store(out, i, synth_value(seed, key1, start + (uint64_t)i, scale), mode);
 }
 
-// Pieces: out[dst_k + j] = value(param_k + j) for j < len_k.  tab holds np + 1
-// rows {cum_k, dst_k, param_k} with cum_k = len_0 + ... + len_{k-1}; the last
-// row is {total, 0, 0}.  Virtual index v in [0, total) belongs to the largest k
-// with cum_k <= v (empty pieces are skipped that way).
+// Pieces: out[place(dst_k + j)] = value(param_k + j) for j < len_k.  tab holds
+// np + 1 rows {cum_k, dst_k, param_k} with cum_k = len_0 + ... + len_{k-1}; the
+// last row is {total, 0, 0}.  Virtual index v in [0, total) belongs to the
+// largest k with cum_k <= v (empty pieces are skipped that way).  place is the
+// identity when ilv_P == 0; otherwise it puts shard index d where rank ilv_q's
+// value sits in a rank-interleaved receive buffer of ilv_P ranks:
+// ((d / 512) * ilv_P + ilv_q) * 512 + d mod 512.
+__device__ __forceinline__ int64_t synth_place(int64_t d, int ilv_P, int ilv_q) {
+    if (ilv_P == 0) return d;
+    return ((d >> 9) * ilv_P + ilv_q) * 512 + (d & 511);
+}
+
 __global__ void synth_fill_pieces_kernel(uint32_t seed, uint32_t key1,
                                          const int64_t* __restrict__ tab, int np, float scale,
-                                         int mode, void* out) {
+                                         int mode, void* out, int ilv_P, int ilv_q) {
     const int64_t total = tab[3 * np];
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total; v += stride) {
@@ -71,7 +79,7 @@ __global__ void synth_fill_pieces_kernel(uint32_t seed, uint32_t key1,
             if (tab[3 * mid] <= v) lo = mid; else hi = mid - 1;
         }
         const int64_t j = v - tab[3 * lo];
-        synth_store(out, tab[3 * lo + 1] + j,
+        synth_store(out, synth_place(tab[3 * lo + 1] + j, ilv_P, ilv_q),
                     synth_value(seed, key1, (uint64_t)(tab[3 * lo + 2] + j), scale), mode);
     }
 }
@@ -199,16 +207,21 @@ int synth_fill_dev(uint32_t seed, uint32_t key1, uint64_t start, int64_t n, floa
 }
 
 // The pieces form of synth_fill_dev (see synth_fill_pieces_kernel): tab is a
-// device array of np + 1 rows; the caller guarantees every dst_k + len_k fits
-// in out.  One launch for any number of pieces.
+// device array of np + 1 rows; the caller guarantees every placed index fits
+// in out.  ilv_P = 0 places at dst_k + j; ilv_P > 0 places rank ilv_q's values
+// in a rank-interleaved buffer of ilv_P ranks.  One launch for any number of
+// pieces.
 int synth_fill_dev_pieces(uint32_t seed, uint32_t key1, const int64_t* tab, int np, int64_t total,
-                          float scale, int mode, void* out, hipStream_t stream) {
-    if (np < 0 || total < 0 || mode < 0 || mode > 2) return -1;
+                          float scale, int mode, void* out, int ilv_P, int ilv_q,
+                          hipStream_t stream) {
+    if (np < 0 || total < 0 || mode < 0 || mode > 2 || ilv_P < 0 || ilv_q < 0 ||
+        (ilv_P > 0 && ilv_q >= ilv_P))
+        return -1;
     if (np == 0 || total == 0) return 0;
     if (!tab || !out) return -1;
     const int block = 256;
     hipLaunchKernelGGL(synth_fill_pieces_kernel, dim3(grid_for(total, block)), dim3(block), 0,
-                       stream, seed, key1, tab, np, scale, mode, out);
+                       stream, seed, key1, tab, np, scale, mode, out, ilv_P, ilv_q);
     return (int)hipGetLastError();
 }
 

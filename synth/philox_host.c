@@ -20,6 +20,7 @@
  * This file holds input generation only; the device implementation lives in
  * philox_dev.hip and must produce identical bits.
  */
+#include <stddef.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -60,19 +61,65 @@ static inline uint16_t to_bf16_rne(float f) {
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-static inline void store(void* out, int64_t i, float x, int mode) {
-    if (mode == 0) ((float*)out)[i] = x;
-    else if (mode == 1) ((float*)out)[i] = bits_f32(f32_bits(x) & 0x7FFFFFFFu);
-    else ((uint16_t*)out)[i] = to_bf16_rne(x);
+/* Fill kernels over a range, one per output mode, each compiled for three
+ * instruction sets (AVX-512, AVX2, baseline x86-64) and chosen at run time:
+ * the loop over elements vectorizes, and the integer and fp32 operations give
+ * the same bits at every width.  idx == NULL means element start + i. */
+#define MODE_LOOPS(GEN)                                                                \
+    if (mode == 0) {                                                                   \
+        float* o = (float*)out;                                                        \
+        for (int64_t i = 0; i < n; ++i) o[i] = GEN(i);                                 \
+    } else if (mode == 1) {                                                            \
+        float* o = (float*)out;                                                        \
+        for (int64_t i = 0; i < n; ++i) o[i] = bits_f32(f32_bits(GEN(i)) & 0x7FFFFFFFu); \
+    } else {                                                                           \
+        uint16_t* o = (uint16_t*)out;                                                  \
+        for (int64_t i = 0; i < n; ++i) o[i] = to_bf16_rne(GEN(i));                    \
+    }
+#define GEN_SEQ(i) value_at(seed, key1, start + (uint64_t)(i), scale)
+#define GEN_IDX(i) value_at(seed, key1, (uint64_t)idx[i], scale)
+#define RANGE_BODY                    \
+    if (idx) { MODE_LOOPS(GEN_IDX) }  \
+    else { MODE_LOOPS(GEN_SEQ) }
+#define RANGE_ARGS uint32_t seed, uint32_t key1, uint64_t start, const int64_t* idx, int64_t n, \
+                   float scale, int mode, void* out
+
+__attribute__((target("avx512f,avx512dq,avx512vl,avx512bw")))
+static void fill_range_avx512(RANGE_ARGS) { RANGE_BODY }
+__attribute__((target("avx2")))
+static void fill_range_avx2(RANGE_ARGS) { RANGE_BODY }
+static void fill_range_base(RANGE_ARGS) { RANGE_BODY }
+
+typedef void (*fill_range_fn)(RANGE_ARGS);
+
+static fill_range_fn fill_range(void) {
+    __builtin_cpu_init();
+    if (__builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512dq") &&
+        __builtin_cpu_supports("avx512vl") && __builtin_cpu_supports("avx512bw"))
+        return fill_range_avx512;
+    if (__builtin_cpu_supports("avx2")) return fill_range_avx2;
+    return fill_range_base;
+}
+
+/* The range [0, n) in chunks, one thread per chunk. */
+static void fill_chunks(uint32_t seed, uint32_t key1, uint64_t start, const int64_t* idx,
+                        int64_t n, float scale, int mode, void* out) {
+    const fill_range_fn f = fill_range();
+    const int64_t chunk = (int64_t)1 << 16, esize = mode == 2 ? 2 : 4;
+    const int64_t nch = (n + chunk - 1) / chunk;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < nch; ++c) {
+        const int64_t a = c * chunk, m = n - a < chunk ? n - a : chunk;
+        f(seed, key1, start + (uint64_t)a, idx ? idx + a : NULL, m, scale, mode,
+          (char*)out + a * esize);
+    }
 }
 
 /* out[i] = value(start + i) for i in [0, n). */
 int synth_fill_host(uint32_t seed, uint32_t key1, uint64_t start, int64_t n,
                     float scale, int mode, void* out) {
     if (n < 0 || mode < 0 || mode > 2 || (n > 0 && !out)) return -1;
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; ++i)
-        store(out, i, value_at(seed, key1, start + (uint64_t)i, scale), mode);
+    fill_chunks(seed, key1, start, NULL, n, scale, mode, out);
     return 0;
 }
 
@@ -80,8 +127,6 @@ int synth_fill_host(uint32_t seed, uint32_t key1, uint64_t start, int64_t n,
 int synth_fill_host_idx(uint32_t seed, uint32_t key1, const int64_t* idx, int64_t n,
                         float scale, int mode, void* out) {
     if (n < 0 || mode < 0 || mode > 2 || (n > 0 && (!out || !idx))) return -1;
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < n; ++i)
-        store(out, i, value_at(seed, key1, (uint64_t)idx[i], scale), mode);
+    fill_chunks(seed, key1, 0, idx, n, scale, mode, out);
     return 0;
 }

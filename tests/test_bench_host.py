@@ -30,7 +30,7 @@ def test_trace_summary_names_template_instances(tmp_path):
              4, 2000000, 1000000, 3000000, 8000000),
             ("void (anonymous namespace)::k_pack<2>(PackPtrs, long const*, int, int, long, long, unsigned short*)",
              2, 3000000, 3000000, 3000000, 6000000),
-            ("void (anonymous namespace)::k_reduce_mean<8, true, true, false, true>(RankPtrs, int, float, int, long const*, int, long, long, float*, double*)",
+            ("void (anonymous namespace)::k_reduce_mean<8, true, 0, false, true>(RankPtrs, int, float, int, long const*, int, long, long, float*, double*)",
              1, 500, 500, 500, 500)]
     src = tmp_path / "stats.csv"
     _write_csv(src, ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "TotalDurationNs"], rows)
@@ -45,14 +45,22 @@ def test_trace_summary_names_template_instances(tmp_path):
 
 def test_lane_contiguous_reduce_instances_are_named_by_row():
     lc = "void (anonymous namespace)::k_reduce_mean_lc<{}>(RankPtrsT<{}>, int, float, int)"
-    assert bench.short_name(lc.format("unsigned short, 8, true, true, false, false", "unsigned short")) \
+    assert bench.short_name(lc.format("unsigned short, 8, true, 0, false, false", "unsigned short")) \
         == "k_reduce_mean"
-    assert bench.short_name(lc.format("float, 8, true, false, false, false", "float")) \
+    assert bench.short_name(lc.format("unsigned short, 8, true, 1, false, false", "unsigned short")) \
+        == "k_reduce_mean"
+    assert bench.short_name(lc.format("unsigned short, 8, true, 2, false, false", "unsigned short")) \
+        == "k_reduce_mean_ilv"
+    assert bench.short_name(lc.format("float, 8, true, 1, false, false", "float")) \
         == "k_reduce_mean_f32"
-    assert bench.short_name(lc.format("unsigned short, 4, true, true, false, true", "unsigned short")) \
+    assert bench.short_name(lc.format("unsigned short, 4, true, 0, false, true", "unsigned short")) \
         == "k_reduce_mean_bf16_wire"
-    assert bench.short_name(lc.format("unsigned short, 2, false, true, true, false", "unsigned short")) \
+    assert bench.short_name(lc.format("unsigned short, 2, false, 0, true, false", "unsigned short")) \
         == "k_allreduce_mean"
+    wide = "void (anonymous namespace)::k_reduce_mean<{}>(RankPtrs, int, float, int)"
+    assert bench.short_name(wide.format("64, true, 1, false, false")) == "k_reduce_mean"
+    assert bench.short_name(wide.format("64, true, 2, false, false")) == "k_reduce_mean_ilv"
+    assert bench.short_name(wide.format("0, true, 0, true, false")) == "k_allreduce_mean"
 
 
 def test_counter_summary_scales_by_the_copy_kernel_and_is_keyed(tmp_path):
