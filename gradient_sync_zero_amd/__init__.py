@@ -10,7 +10,7 @@ from ._binding import (AdamWHP, GszError, INTERLEAVE_PIECE, LAYOUT_BUCKET_FLAT,
                        MAX_RANKS, Plan, adamw_step, allgather_layout_write, allreduce_mean,
                        bucket_accumulate, bucket_accumulate_f32, bucket_pack, bucket_pack_f32,
                        bucket_unpack, clip_coef, load, ledger_bytes_per_param, make_hp,
-                       shard_adamw_step, shard_grad_sqnorm, shard_reduce_mean,
+                       shard_adamw_step, shard_grad_sqnorm, shard_reduce_mean, shard_reduce_mean_noalloc,
                        set_grid_limit, shard_reduce_mean_f32, test_hooks, workspace_bytes)
 from . import _binding
 
@@ -22,4 +22,5 @@ __all__ = ["AdamWHP", "GszError", "INTERLEAVE_PIECE", "LAYOUT_BUCKET_FLAT",
            "bucket_accumulate", "bucket_accumulate_f32", "bucket_pack", "bucket_pack_f32",
            "bucket_unpack", "clip_coef", "ledger_bytes_per_param", "make_hp", "set_grid_limit",
            "shard_adamw_step", "shard_grad_sqnorm", "shard_reduce_mean", "shard_reduce_mean_f32",
+           "shard_reduce_mean_noalloc",
            "test_hooks", "workspace_bytes"]

@@ -83,6 +83,7 @@ _SIGS = {
     "gsz_bucket_accumulate_f32": [_P, _P, _P, _P],
     "gsz_shard_reduce_mean_f32": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_shard_reduce_mean_bf16_wire": [_P, _I32, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+    "gsz_shard_reduce_mean_noalloc": [_P, _I32, _P, _I32, _P, _P, _P],
     "gsz_allreduce_mean": [_P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "gsz_adamw_step": [_P, _P, _P, _P, _I64, _P, ctypes.POINTER(AdamWHP), _P, _P],
 }
@@ -399,6 +400,17 @@ def shard_reduce_mean(plan, owner, contribs, layout, g, partial_out=None, ws=Non
     _check(fn(plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32(), min_numel=plan.shard_len),
               _ptr(partial_out, "partial_out", _f64(), allow_none=True, min_numel=1),
               wsp, nbytes, _stream(stream)))
+
+
+def shard_reduce_mean_noalloc(plan, owner, contribs, layout, g, partial_out=None, stream=None):
+    """gsz_shard_reduce_mean_noalloc: the same reduce with the library's own
+    fixed scratch in place of a workspace (shards of up to 2^31 elements; calls
+    that overlap on one device race)."""
+    ptrs = _contrib_ptrs(plan, contribs, layout, _bf16_types())
+    _check(_lib_for(plan).gsz_shard_reduce_mean_noalloc(
+        plan.handle, owner, ptrs, layout, _ptr(g, "g", _f32(), min_numel=plan.shard_len),
+        _ptr(partial_out, "partial_out", _f64(), allow_none=True, min_numel=1),
+        _stream(stream)))
 
 
 def shard_grad_sqnorm(g, partial_out, ws, n=None, stream=None):

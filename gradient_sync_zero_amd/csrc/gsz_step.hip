@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "gsz_device.h"
@@ -481,6 +482,59 @@ extern "C" int gsz_shard_reduce_mean_f32(const gsz_plan* p, int32_t owner,
                                          hipStream_t stream) {
     return reduce_impl(p, owner, reinterpret_cast<const void* const*>(contrib), layout, g,
                        partial_out, ws, ws_bytes, stream, false, true, "gsz_shard_reduce_mean_f32");
+}
+
+// ------------------------------------------- the allocation-free variant --
+
+// Scratch of gsz_shard_reduce_mean_noalloc: the norm partials of one reduce
+// (one fp64 per 2048 shard elements plus the 1024 second-stage sums), for
+// shards of up to 2^31 elements.  Each device that runs the library holds its
+// own copy for the life of the process.  Host code never passes this name to a
+// kernel (on the host it is a stand-in, not a device address): it uses the
+// address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kScratchMaxShard = (int64_t)1 << 31;
+constexpr int64_t kScratchDoubles = kScratchMaxShard / gsz::kRedElems + gsz::kFinalBlocks;
+static __device__ __align__(256) double scratch[kScratchDoubles];
+
+namespace {
+
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[64];          // per device, set once under g_scratch_mu
+
+// This device's copy of `scratch`, looked up on the first call on the device.
+int scratch_for(int dev, double** out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail("gsz_shard_reduce_mean_noalloc: hipGetSymbolAddress", e);
+        g_scratch_ptr[dev] = static_cast<double*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return GSZ_OK;
+}
+
+}  // namespace
+
+extern "C" int gsz_shard_reduce_mean_noalloc(const gsz_plan* p, int32_t owner,
+                                             const uint16_t* const* contrib, int32_t layout,
+                                             float* g, double* partial_out, hipStream_t stream) {
+    const char* who = "gsz_shard_reduce_mean_noalloc";
+    if (!p) { set_error("%s: NULL plan", who); return GSZ_ERR_INVALID_ARG; }
+    if (p->shard_len > kScratchMaxShard) {
+        set_error("%s: shard of %lld elements exceeds this variant's limit of %lld (its scratch "
+                  "is a fixed array); use gsz_shard_reduce_mean with a workspace",
+                  who, (long long)p->shard_len, (long long)kScratchMaxShard);
+        return GSZ_ERR_SIZE;
+    }
+    int dev = 0;
+    int rc = current_device(&dev);
+    if (rc) return rc;
+    double* ws = nullptr;
+    if (partial_out && (rc = scratch_for(dev, &ws))) return rc;
+    return reduce_impl(p, owner, reinterpret_cast<const void* const*>(contrib), layout, g,
+                       partial_out, ws, partial_out ? kScratchDoubles * sizeof(double) : 0, stream,
+                       false, false, who);
 }
 
 extern "C" int gsz_shard_reduce_mean_bf16_wire(const gsz_plan* p, int32_t owner,

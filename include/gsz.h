@@ -301,6 +301,22 @@ int gsz_shard_reduce_mean_bf16_wire(const gsz_plan* plan, int32_t owner,
                                     double* partial_out, void* ws, size_t ws_bytes,
                                     hipStream_t stream);
 
+/* gsz_shard_reduce_mean without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The norm partials live in a fixed array
+ * inside the library, one per device (8,396,800 bytes, held from the first
+ * call on a device until the process ends), so shard_len may be at most 2^31
+ * elements (GSZ_ERR_SIZE otherwise).  Arguments, outputs, results (bit for bit)
+ * and errors otherwise as gsz_shard_reduce_mean.  Nothing needs clearing
+ * between calls: every call writes the partials it reads.  Calls on the same
+ * device share the array: calls that may overlap (different streams, or
+ * different threads with no ordering between their streams) race and must be
+ * serialised by the caller.  Allocates nothing; the first call on a device
+ * looks up that device's copy of the array. */
+int gsz_shard_reduce_mean_noalloc(const gsz_plan* plan, int32_t owner,
+                                  const uint16_t* const* contrib, int32_t layout, float* g,
+                                  double* partial_out, hipStream_t stream);
+
 /* gsz_shard_reduce_mean over fp32 contributions (fp32 accumulation buckets,
  * fp32 on the wire; reduce_dtype = fp32, "Distributed Training ...", section
  * FSDP1 vs FSDP2 and DTensor): the same ring order

@@ -78,6 +78,18 @@ def test_library_neither_allocates_device_memory_nor_waits():
                             "hipEventSynchronize"}
 
 
+def test_noalloc_reduce_refuses_shards_over_its_fixed_scratch():
+    """The allocation-free reduce has a fixed scratch for shards of at most
+    2^31 elements; a larger plan is refused before any device call."""
+    big = G.Plan([(1 << 31) + 64], 1 << 40, 1)
+    assert big.shard_len > 1 << 31
+    lib = G.load()
+    arr = (ctypes.c_void_p * 1)(None)
+    assert lib.gsz_shard_reduce_mean_noalloc(big.handle, 0, arr, G.LAYOUT_SHARD_COMPACT, None,
+                                             None, None) == -3          # GSZ_ERR_SIZE
+    assert b"2147483648" in lib.gsz_last_error()
+
+
 def test_plan_device_bytes_is_the_documented_bound():
     """Header: at most 1,048,640 + 24 * n_tensors + 40 * n_buckets bytes."""
     for cfg in range(5):
