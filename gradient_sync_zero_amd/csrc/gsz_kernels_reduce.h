@@ -61,16 +61,27 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
                                                         double* __restrict__ ws) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);      // logical block: tile bx
-    int64_t v = bx * kBlock + threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr bool FLAT = LAY == kLayFlat;
     static_assert(!OUTFLAT || FLAT, "the all-gather-position output reads bucket-flat input");
+    // The results reach HBM as whole-line stores: each wave's 512 results pass
+    // through LDS so that one store instruction writes 1 KiB contiguous (lane l
+    // writes what lane l/2 computed).  A lane storing 32 contiguous bytes as two
+    // 16-byte stores makes each instruction cover half of every line, and such
+    // nontemporal half-line stores reached HBM as 9% more write bytes.  So the
+    // loop is wave-uniform: lanes past the end stay in it, load position 0 of
+    // every contribution (in bounds) and discard the result.
+    __shared__ float stage[OUTFLAT ? 1 : kBlock * 8];
     double sq = 0.0;
     SegCursor cur{seg, owner, 0, 0, 0};
-    if (FLAT && v < nvec) cur.seek(bx * kRedTile, slut, sshift);      // uniform: scalar loads
+    const int64_t S = nvec * 8;
+    if (FLAT && bx * kRedTile < S) cur.seek(bx * kRedTile, slut, sshift);  // uniform: scalar loads
     const float fP = (float)P;
-    for (; v < nvec; v += stride) {
+    for (int64_t v0 = bx * kBlock + wave * 64; v0 < nvec; v0 += stride) {
+        const int64_t v = v0 + lane;
+        const bool ok = v < nvec;
         const int64_t i = v * 8;
-        const int64_t off = contrib_index<LAY>(cur, i, PS > 0 ? PS : P);
+        const int64_t off = ok ? contrib_index<LAY>(cur, i, PS > 0 ? PS : P) : 0;
         float a[8];
         if constexpr (PS > 0) {
             // up to 32 loads before their adds (at P = 64 that measured 1.4% faster than 16)
@@ -106,10 +117,26 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
 #pragma unroll
             for (int j = 0; j < 8; ++j) a[j] = a[j] / fP;
         }
-        const int64_t o = OUTFLAT ? off : i;    // all-reduce output: the flat position
-        stf4_nt(g + o, f32x4{a[0], a[1], a[2], a[3]});
-        stf4_nt(g + o + 4, f32x4{a[4], a[5], a[6], a[7]});
-        if (NORM) {
+        if constexpr (OUTFLAT) {
+            if (ok) {                           // all-reduce output: the flat position
+                stf4_nt(g + off, f32x4{a[0], a[1], a[2], a[3]});
+                stf4_nt(g + off + 4, f32x4{a[4], a[5], a[6], a[7]});
+            }
+        } else {
+            float* st = stage + wave * 512;
+            *reinterpret_cast<f32x4*>(st + 8 * lane) = f32x4{a[0], a[1], a[2], a[3]};
+            *reinterpret_cast<f32x4*>(st + 8 * lane + 4) = f32x4{a[4], a[5], a[6], a[7]};
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(st + 4 * lane);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(st + 256 + 4 * lane);
+            const int64_t e0 = v0 * 8 + 4 * lane, e1 = e0 + 256;
+            if (e0 < S) stf4_nt(g + e0, lo);
+            if (e1 < S) stf4_nt(g + e1, hi);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();  // the next iteration's writes come after these reads
+        }
+        if (NORM && ok) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const double d = (double)a[j];
