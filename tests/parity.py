@@ -54,3 +54,24 @@ def assert_bits(gpu: np.ndarray, ref: np.ndarray, what: str):
         i = int(np.argmax(bad))
         raise AssertionError(f"{what}: {n} of {bad.size} elements differ; first at {i}: "
                              f"gpu={gpu[i]!r} ref={ref[i]!r}")
+
+
+def bf16_wire_bound(contribs_fp64_abs_sum, P):
+    """Rigorous bound on |fp32 ring mean - bf16-wire ring mean|, elementwise.
+
+    Both are recursive sums of the same P values, compared with the exact
+    mean E: |a - b| <= |a - E| + |E - b|.  A recursive sum whose every
+    partial sum is rounded with relative error at most u is off by at most
+    (P-1) * u * (1+u)^(P-1) * sum|c| (each of the P-1 rounded partial sums is
+    at most (1+u)^(P-1) * sum|c| in magnitude).  The fp32 sum rounds once per
+    addition: u = 2^-24.  The bf16 wire rounds each partial sum twice, the
+    fp32 addition and then to bf16: |bf16(fl32(x)) - x| <= (2^-8 + 2^-24 +
+    2^-32)|x|.  Division by P is exact for P a power of two (no underflow at
+    these magnitudes).  The bound is evaluated in fp64; the caller allows a
+    relative 1e-12 for that evaluation and nothing else."""
+    import numpy as np
+    u32 = 2.0 ** -24
+    u16 = 2.0 ** -8 + 2.0 ** -24 + 2.0 ** -32
+    k = P - 1
+    coef = k * (u16 * (1 + u16) ** k + u32 * (1 + u32) ** k)
+    return coef * np.asarray(contribs_fp64_abs_sum, dtype=np.float64) / P

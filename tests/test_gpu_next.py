@@ -16,7 +16,7 @@ from synth import gen
 from synth import workloads as W
 from tests import gpu_inputs as GI
 from tests import oracle_inputs as OI
-from tests.parity import assert_bits, host
+from tests.parity import bf16_wire_bound, assert_bits, host
 
 pytestmark = pytest.mark.gpu
 
@@ -85,11 +85,10 @@ def test_bf16_wire_reduce_all_owners(cfg):
         assert_bits(host(gc), ref, f"bf16-wire g owner {r} (shard-compact)")
         assert abs(host(part)[0] - sqnorm_partial(ref)) <= 1e-12 * sqnorm_partial(ref)
         fp32 = reduce_mean(cs, r).astype(np.float64)
-        u = 2.0 ** -8       # bf16 unit roundoff; see the oracle pin for the bound
         abs_sum = np.sum([np.abs(widen(c)).astype(np.float64) for c in cs], axis=0)
-        bound = (P - 1) * u * (1 + u) ** (P - 1) * abs_sum / P
+        bound = bf16_wire_bound(abs_sum, P)
         err = np.abs(fp32 - ref)
-        assert (err <= bound * (1 + 1e-6) + 1e-12).all()
+        assert (err <= bound * (1 + 1e-12)).all()
         worst = max(worst, float((err / np.maximum(bound, 1e-300)).max()))
         changed += int((err > 0).sum())
         n_all += err.size
