@@ -129,3 +129,40 @@ def test_counter_summary_of_any_counters(tmp_path):
     text = (tmp_path / "counters_ab_w.txt").read_text()
     body = [l.split() for l in text.splitlines() if not l.startswith("#")]
     assert body == [["k_adamw", "2", "2.0000e+01", "4.0000e+00"]]   # per-dispatch sums, then means
+
+
+def test_benchmark_and_package_import_nothing_from_tests():
+    """bench.py assembles its inputs with synth/placement.py; neither it nor
+    the product package may depend on the test package."""
+    import ast
+    files = [os.path.join(ROOT, "bench.py")]
+    for d in ("gradient_sync_zero_amd", "synth"):
+        files += [os.path.join(ROOT, d, f) for f in os.listdir(os.path.join(ROOT, d))
+                  if f.endswith(".py")]
+    for path in files:
+        tree = ast.parse(open(path).read())
+        for node in ast.walk(tree):
+            names = []
+            if isinstance(node, ast.Import):
+                names = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                names = [node.module or ""]
+            assert not any(n == "tests" or n.startswith("tests.") for n in names), (path, names)
+
+
+def test_cpu_baseline_sample_is_the_workloads_own_inputs():
+    """The oracle baseline's window holds exactly the values the oracle's own
+    placement gives the first n shard elements (all ranks and the state)."""
+    import numpy as np
+    from oracle.plan import make_plan
+    from synth import workloads as W
+    from tests import oracle_inputs as OI
+    w = W.by_id(1)
+    n, contribs, state = bench._oracle_sample(w, 2, 300_000)
+    plan = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
+    idx = OI.shard_param_index(plan, 2)[:n]
+    assert n == 300_000 and len(contribs) == w.world_size
+    for q in (0, 5, 7):
+        assert np.array_equal(contribs[q], OI.values_at(w, W.KIND_GRAD, q, w.grad_std, 2, idx))
+    for (kind, std, mode), arr in zip(OI.STATE_KINDS, state):
+        assert np.array_equal(arr.view(np.uint32), OI.values_at(w, kind, 0, std, mode, idx).view(np.uint32))
