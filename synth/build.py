@@ -21,7 +21,7 @@ def build(verbose: bool = False) -> None:
     host_out = os.path.join(_HERE, "libsynth_host.so")
     dev_out = os.path.join(_HERE, "libsynth_dev.so")
     cmds = [
-        ["gcc", "-O3", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-std=gnu11",
+        ["gcc", "-O3", "-ffp-contract=off", "-fno-trapping-math", "-fopenmp", "-fPIC", "-shared", "-std=gnu11",
          "philox_host.c", "-o", host_out + ".tmp"],
         [HIPCC, *HIP_FLAGS, "philox_dev.hip", "-o", dev_out + ".tmp"],
     ]

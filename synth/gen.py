@@ -7,7 +7,6 @@ produce the same bits for the same (workload id, kind, rank, element index).
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import numpy as np
@@ -31,8 +30,8 @@ def key1(cfg_id: int, kind: int, rank: int) -> int:
 
 
 def scale_for(std: float) -> np.float32:
-    """fp32 multiplier that gives the Irwin-Hall sum the requested std."""
-    return np.float32(std / math.sqrt(8.0 * (65536.0 ** 2 - 1.0) / 3.0))
+    """fp32 multiplier of the standard normal value: the standard deviation."""
+    return np.float32(std)
 
 
 def _load_host():
@@ -51,6 +50,8 @@ def _load_host():
         lib.synth_fill_host_idx.restype = ctypes.c_int
         lib.synth_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.synth_philox4x32_10.restype = None
+        lib.synth_normal_quantile_host.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_normal_quantile_host.restype = None
         _host = lib
     return _host
 
@@ -97,6 +98,14 @@ def philox4x32_10(ctr, key):
     o = (ctypes.c_uint32 * 4)()
     lib.synth_philox4x32_10(c, k, o)
     return list(o)
+
+
+def normal_quantile(p):
+    """The generator's standard normal quantile at each p in (0, 1), fp64."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    out = np.empty_like(p)
+    _load_host().synth_normal_quantile_host(p.ctypes.data, p.size, out.ctypes.data)
+    return out
 
 
 def _dtype(mode):

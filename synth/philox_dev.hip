@@ -5,15 +5,73 @@
 // Same generator as the host side: Philox4x32 with 10 rounds, from its
 // published definition (Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
 // as easy as 1, 2, 3", SC'11).  Element e of stream (seed, key1) uses counter
-// (e mod 2^32, e / 2^32, 0, 0) and key (seed, key1); the eight 16-bit halves of
-// the four output words give z = 2*sum - 8*65535 (exact in fp32) and the value
-// fp32(z) * scale.  Modes: 0 fp32, 1 |fp32|, 2 bf16 bits (round to nearest even).
+// (e mod 2^32, e / 2^32, 0, 0) and key (seed, key1); the top 52 bits of its
+// first two output words give p = (k + 1/2) 2^-52, and the value is fp32 of
+// the standard normal quantile at p (P. J. Acklam's rational approximation)
+// times the standard deviation.  Modes: 0 fp32, 1 |fp32|, 2 bf16 bits (round
+// to nearest even).
 //
 // Input generation only: nothing here is part of the shard-step library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#pragma clang fp contract(off)
+
 namespace {
+
+__device__ __forceinline__ uint64_t f64_bits(double x) { return (uint64_t)__double_as_longlong(x); }
+__device__ __forceinline__ double bits_f64(uint64_t u) { return __longlong_as_double((long long)u); }
+
+// The same fp64 operations, in the same order, as the host implementation
+// (philox_host.c), so the bits agree: log from the 2 atanh series, square root
+// by Newton steps on the reciprocal root, Acklam's normal quantile with both
+// branches evaluated and one selected.
+__device__ __forceinline__ double synth_log(double x) {
+    const uint64_t u = f64_bits(x);
+    const double e0 = (bits_f64(0x4330000000000000ull | ((u >> 52) & 0x7FF)) - 0x1p52) - 1023.0;
+    const double m0 = bits_f64((u & 0x000FFFFFFFFFFFFFull) | 0x3FF0000000000000ull);
+    const int up = m0 > 1.4142135623730951;
+    const double m = up ? m0 * 0.5 : m0, e = up ? e0 + 1.0 : e0;
+    const double s = (m - 1.0) / (m + 1.0), s2 = s * s;
+    double t = 1.0 / 23.0;
+    t = t * s2 + 1.0 / 21.0; t = t * s2 + 1.0 / 19.0; t = t * s2 + 1.0 / 17.0;
+    t = t * s2 + 1.0 / 15.0; t = t * s2 + 1.0 / 13.0; t = t * s2 + 1.0 / 11.0;
+    t = t * s2 + 1.0 / 9.0; t = t * s2 + 1.0 / 7.0; t = t * s2 + 1.0 / 5.0;
+    t = t * s2 + 1.0 / 3.0; t = t * s2 + 1.0;
+    return e * 0.6931471805599453 + 2.0 * s * t;
+}
+
+__device__ __forceinline__ double synth_sqrt(double a) {
+    double y = bits_f64(0x5FE6EB50C7B537A9ull - (f64_bits(a) >> 1));
+#pragma unroll
+    for (int i = 0; i < 5; ++i) y = y * (1.5 - (0.5 * a) * (y * y));
+    const double x = a * y;
+    return x + 0.5 * y * (a - x * x);
+}
+
+__device__ __forceinline__ double synth_normal_quantile(double p) {
+    const double a1 = -3.969683028665376e+01, a2 = 2.209460984245205e+02,
+                 a3 = -2.759285104469687e+02, a4 = 1.383577518672690e+02,
+                 a5 = -3.066479806614716e+01, a6 = 2.506628277459239e+00;
+    const double b1 = -5.447609879822406e+01, b2 = 1.615858368580409e+02,
+                 b3 = -1.556989798598866e+02, b4 = 6.680131188771972e+01,
+                 b5 = -1.328068155288572e+01;
+    const double c1 = -7.784894002430293e-03, c2 = -3.223964580411365e-01,
+                 c3 = -2.400758277161838e+00, c4 = -2.549732539343734e+00,
+                 c5 = 4.374664141464968e+00, c6 = 2.938163982698783e+00;
+    const double d1 = 7.784695709041462e-03, d2 = 3.224671290700398e-01,
+                 d3 = 2.445134137142996e+00, d4 = 3.754408661907416e+00;
+    const double plow = 0.02425;
+    const double pt = p < 0.5 ? p : 1.0 - p;
+    const double q = synth_sqrt(-2.0 * synth_log(pt));
+    const double xt = (((((c1 * q + c2) * q + c3) * q + c4) * q + c5) * q + c6) /
+                      ((((d1 * q + d2) * q + d3) * q + d4) * q + 1.0);
+    const double qc = p - 0.5, r = qc * qc;
+    const double xc = (((((a1 * r + a2) * r + a3) * r + a4) * r + a5) * r + a6) * qc /
+                      (((((b1 * r + b2) * r + b3) * r + b4) * r + b5) * r + 1.0);
+    const int tail = (p < plow) | (p > 1.0 - plow);
+    return tail ? (p < 0.5 ? xt : -xt) : xc;
+}
 
 __device__ __forceinline__ float synth_value(uint32_t seed, uint32_t key1, uint64_t e,
                                              float scale) {
@@ -27,10 +85,9 @@ __device__ __forceinline__ float synth_value(uint32_t seed, uint32_t key1, uint6
         const uint32_t y0 = hi1 ^ x1 ^ k0, y2 = hi0 ^ x3 ^ k1;
         x0 = y0; x1 = lo1; x2 = y2; x3 = lo0;
     }
-    const int32_t s = (int32_t)((x0 & 0xFFFFu) + (x0 >> 16) + (x1 & 0xFFFFu) + (x1 >> 16) +
-                                (x2 & 0xFFFFu) + (x2 >> 16) + (x3 & 0xFFFFu) + (x3 >> 16));
-    const int32_t z = 2 * s - 8 * 65535;
-    return (float)z * scale;
+    const uint64_t k = (((uint64_t)x1 << 32) | x0) >> 12;
+    const double p = ((bits_f64(0x4330000000000000ull | k) - 0x1p52) + 0.5) * 0x1p-52;
+    return (float)synth_normal_quantile(p) * scale;
 }
 
 // out[i] <- x in the mode's type: fp32, |fp32|, or bf16 bits (round to nearest even).
