@@ -214,7 +214,11 @@ int gsz_bucket_pack(const gsz_plan* plan, const uint16_t* const* grads, uint16_t
  * rank c+1 and takes one fp32 addition per hop around the ring, ending at its
  * owner c), averaged as in "Data parallelism in depth" §2, accumulated in fp32 as in
  * "Distributed Training ...", section FSDP1 vs FSDP2 (reduce_dtype=fp32).
- *   contrib (host array of P device pointers), layout GSZ_LAYOUT_*.
+ *   contrib (host array of device pointers, 16-byte aligned): P buffers for
+ *     GSZ_LAYOUT_BUCKET_FLAT (flat_len elements each) and
+ *     GSZ_LAYOUT_SHARD_COMPACT (S each); one receive buffer for
+ *     GSZ_LAYOUT_RANK_INTERLEAVED (P * ceil(S/512) * 512 elements).  The three
+ *     layouts give the same g and partial bit for bit.
  *   g (device, S fp32): written.
  *   partial_out (device, one double, may be NULL): sum of g[i]^2 in fp64.
  *   ws (device, >= gsz_workspace_bytes): scratch, required if partial_out.
@@ -322,7 +326,8 @@ int gsz_shard_reduce_mean_noalloc(const gsz_plan* plan, int32_t owner,
  * FSDP1 vs FSDP2 and DTensor): the same ring order
  * ((c_{r+1} + c_{r+2}) + ...) + c_r and division by P, the inputs taken as they
  * are.  contrib: P device pointers to fp32 buffers (flat_len for
- * GSZ_LAYOUT_BUCKET_FLAT, S for GSZ_LAYOUT_SHARD_COMPACT), 16-byte aligned.
+ * GSZ_LAYOUT_BUCKET_FLAT, S for GSZ_LAYOUT_SHARD_COMPACT), or one fp32 receive
+ * buffer of P * ceil(S/512) * 512 for GSZ_LAYOUT_RANK_INTERLEAVED; 16-byte aligned.
  * Other arguments, outputs and errors as gsz_shard_reduce_mean. */
 int gsz_shard_reduce_mean_f32(const gsz_plan* plan, int32_t owner, const float* const* contrib,
                               int32_t layout, float* g, double* partial_out, void* ws,
