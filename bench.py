@@ -208,14 +208,41 @@ KERNEL_SOURCES = ("gsz_device.h", "gsz_internal.h", "gsz_kernels_adamw.h", "gsz_
                   "gsz_kernels_reduce.h", "gsz_step.hip")
 
 
+def _code_tokens(text):
+    """C++ source without its comments, whitespace runs collapsed: what a
+    comment-only edit leaves unchanged.  String literals are kept whole."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest():
-    """SHA-256 over the library's kernel sources (names and contents), the key
-    that ties a counter summary to the kernels it measured."""
+    """SHA-256 over the library's kernel sources (names and code, comments and
+    whitespace left out), the key that ties a counter summary to the kernels it
+    measured."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         h.update(name.encode() + b"\0")
-        h.update(open(os.path.join(ROOT, "gradient_sync_zero_amd", "csrc", name), "rb").read())
+        text = open(os.path.join(ROOT, "gradient_sync_zero_amd", "csrc", name)).read()
+        h.update(_code_tokens(text).encode())
     return h.hexdigest()
 
 

@@ -138,7 +138,7 @@ int check_owner(const gsz_plan* p, int32_t owner, const char* who) {
 // Calls f(std::integral_constant<int, PS>{}) with PS = P for the world sizes that
 // have unrolled kernels and PS = 0 (the runtime-P loop) for every other P.  The
 // bf16 reduces also unroll P = 3, 6, 24 and 96, where the runtime loop waits
-// for its last (P-1) mod 8 contributions one at a time (measured on two boxes:
+// for its last (P-1) mod 8 contributions one at a time (measured on two machines:
 // P = 3 7-9% faster unrolled, P = 6 2-5%, P = 24 1-2%, P = 96 0.5-6.5%; P = 12,
 // 48 and 128 gained nothing); the fp32 reduce keeps the powers of two (unrolled
 // at 48 or more it needs all 256 registers per lane).

@@ -261,6 +261,18 @@ def test_traffic_digest_covers_every_kernel_source():
     assert len(bench.kernel_source_digest()) == 64
 
 
+def test_traffic_digest_ignores_comments_but_not_code():
+    """A comment-only edit keeps a counter summary valid; any code edit, also
+    inside a string literal, voids it."""
+    import bench
+    src = 'int f(int a) { // add one\n  return a + 1; /* done */ }\nconst char* s = "a // b";\n'
+    same = 'int f(int a)   {\n  return a + 1;\n}\n// moved\nconst char* s = "a // b";'
+    assert bench._code_tokens(src) == bench._code_tokens(same)
+    for edited in (src.replace("a + 1", "a + 2"), src.replace('"a // b"', '"a // c"'),
+                   src.replace("return", "return -")):
+        assert bench._code_tokens(edited) != bench._code_tokens(src)
+
+
 def test_planner_and_error_text_are_thread_safe():
     """Eight threads create plans concurrently (each checked against the
     oracle's planner) and provoke their own errors: the last-error text is per
