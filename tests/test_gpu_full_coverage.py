@@ -18,7 +18,14 @@ The oracle regenerates each window's inputs on the host from the seeded
 generator (placed with the oracle's plan) and runs on one slice per host
 thread; GPU inputs come from the device generator placed with the library's
 plan.  The 70B share's rank-interleaved receive layout is checked against the
-shard-compact g at the full size too."""
+shard-compact g at the full size too.
+
+The unsharded (DDP) step of the 1.3B model is held to the same bar on every
+flat position, in the configuration bench.py --variant ddp times: the
+all-reduce mean (each chunk summed in the ring order that ends at its owner),
+the P chunk owners' fused norm partials against the oracle's, the clip from
+those real partials, AdamW over the whole flat buffer and the unpacked bf16
+parameters."""
 import concurrent.futures as cf
 import os
 import time
@@ -114,12 +121,18 @@ class GpuStep:
 
 
 class OracleWindows:
-    """The oracle side: owner 0's shard in windows, regenerated on the host."""
+    """The oracle side: owner 0's shard (or, with flat=True, the whole
+    bucket-major flat buffer) in windows, regenerated on the host."""
 
-    def __init__(self, w):
+    def __init__(self, w, flat=False):
         self.w = w
         self.plan = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
-        self.pieces = sorted(OI.owner_pieces(self.plan, OWNER))
+        if flat:   # (flat offset, parameter index, length) of every tensor
+            pre = OI.prefix(w.numel)
+            self.pieces = sorted((self.plan.tensor_offset[t], pre[t], n)
+                                 for t, n in enumerate(w.numel) if n)
+        else:
+            self.pieces = sorted(OI.owner_pieces(self.plan, OWNER))
         self.starts = np.array([p[0] for p in self.pieces], dtype=np.int64)
         self.pool = cf.ThreadPoolExecutor(max_workers=THREADS)
 
@@ -237,3 +250,132 @@ def test_llama_70b_share_every_shard_element(part):
         check_norm_and_clip(4)
         _cache.clear()
         torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- the DDP step
+
+class GpuDdpStep:
+    """The unsharded (DDP / NO_SHARD) step of bench.py --variant ddp, run once:
+    pack, all-reduce mean with the P chunk owners' fused norm partials, clip
+    from those partials, AdamW over the whole flat buffer, unpack."""
+
+    def __init__(self, cfg):
+        w = W.by_id(cfg)
+        P = w.world_size
+        plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
+        L = plan.flat_len
+        t0 = time.perf_counter()
+        gbuf = torch.empty(w.n_params, dtype=torch.uint16, device="cuda")
+        flats = [torch.empty(L, dtype=torch.uint16, device="cuda") for _ in range(P)]
+        for q in range(P):
+            _, views = GI.rank_grads(w, q, gbuf)
+            G.bucket_pack(plan, views, flats[q])
+        del gbuf, views
+        self.master, self.m, self.v = GI.full_state(plan, w)
+        self.g = torch.empty(L, dtype=torch.float32, device="cuda")
+        ws = torch.zeros(G.workspace_bytes(plan.shard_len) // 8, dtype=torch.float64, device="cuda")
+        partials = torch.zeros(P, dtype=torch.float64, device="cuda")
+        coef = torch.empty(1, dtype=torch.float32, device="cuda")
+        norm = torch.empty(1, dtype=torch.float32, device="cuda")
+        tot = torch.empty(1, dtype=torch.float64, device="cuda")
+        pflat = torch.full((L,), 0x7777, dtype=torch.uint16, device="cuda")
+        self.pbuf = torch.full((w.n_params,), 0x7777, dtype=torch.uint16, device="cuda")
+        params = [self.pbuf[s0:s0 + n] for s0, n in zip(GI.prefix(w.numel), w.numel)]
+        G.allreduce_mean(plan, flats, self.g, partials, ws)
+        G.clip_coef(partials, w.hp.max_norm, coef, norm, tot)
+        G.adamw_step(self.master, self.m, self.v, self.g, coef, w.hp, pflat)
+        G.bucket_unpack(plan, pflat, params)
+        torch.cuda.synchronize()
+        self.partials = host(partials).astype(np.float64)
+        self.coef, self.norm, self.total = host(coef)[0], host(norm)[0], float(host(tot)[0])
+        del flats, pflat, params
+        torch.cuda.empty_cache()
+        self.w, self.L = w, L
+        say(f"[{w.name} DDP] GPU step done in {time.perf_counter() - t0:.1f} s: L={L}, "
+            f"total={self.total:.6e}, coef={self.coef}")
+
+
+def ring_segments(oplan):
+    """(flat start, end, chunk owner) of every chunk: the all-reduce sums chunk c
+    of every bucket in the ring order that ends at rank c."""
+    out = []
+    for b, bk in enumerate(oplan.buckets):
+        for c in range(oplan.world_size):
+            cs, ce = oplan.chunk_range(b, c)
+            if cs < ce:
+                out.append((cs, ce, c))
+    return out
+
+
+_ddp = {}
+
+
+def compare_ddp_windows(cfg, part, n_parts):
+    if cfg not in _ddp:
+        _ddp.clear()
+        torch.cuda.empty_cache()
+        ow = OracleWindows(W.by_id(cfg), flat=True)
+        _ddp[cfg] = (GpuDdpStep(cfg), ow, ring_segments(ow.plan), {})
+    gs, ow, segs, acc = _ddp[cfg]
+    w, L, P = gs.w, gs.L, gs.w.world_size
+    seg_starts = np.array([sg[0] for sg in segs], dtype=np.int64)
+    pre = OI.prefix(w.numel)
+    nwin = -(-L // WINDOW)
+    lo_w, hi_w = part * nwin // n_parts, (part + 1) * nwin // n_parts
+    hp = w.hp
+    t0 = time.perf_counter()
+    for k in range(lo_w, hi_w):
+        a, b = k * WINDOW, min((k + 1) * WINDOW, L)
+        cs = [ow.fill(a, b, W.KIND_GRAD, q, w.grad_std, gen.MODE_BF16) for q in range(P)]
+        st = [ow.fill(a, b, kind, 0, std, mode) for kind, std, mode in OI.STATE_KINDS]
+        # the window cut at chunk boundaries; each piece summed in its owner's ring order
+        pieces = []
+        j = max(int(np.searchsorted(seg_starts, a, side="right")) - 1, 0)
+        for s0, e0, c in segs[j:]:
+            if s0 >= b:
+                break
+            lo, hi = max(s0, a) - a, min(e0, b) - a
+            for x in range(lo, hi, 1 << 20):          # slices of at most 1M for the threads
+                pieces.append((x, min(x + (1 << 20), hi), c))
+
+        def run(piece):
+            lo, hi, c = piece
+            g = reduce_mean([x[lo:hi] for x in cs], c)
+            th, m, v, p = adamw(st[0][lo:hi], st[1][lo:hi], st[2][lo:hi], g, gs.coef, hp.lr,
+                                hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step)
+            return c, sqnorm_partial(g), g, th, m, v, p
+
+        res = list(ow.pool.map(run, pieces))
+        for c, sq, *_ in res:
+            acc.setdefault(c, []).append((k, sq))
+        out = [np.concatenate([r[i] for r in res]) for i in range(2, 7)]
+        assert_bits(host(gs.g[a:b]), out[0], f"DDP g [{a}, {b})")
+        assert_bits(host(gs.master[a:b]), out[1], f"DDP master [{a}, {b})")
+        assert_bits(host(gs.m[a:b]), out[2], f"DDP m [{a}, {b})")
+        assert_bits(host(gs.v[a:b]), out[3], f"DDP v [{a}, {b})")
+        # the unpacked parameters: flat position f of tensor t is parameter pre_t + (f - off_t)
+        pidx = OI.param_index_of_flat(ow.plan, np.arange(a, b, dtype=np.int64))
+        real = pidx >= 0
+        got = host(gs.pbuf.view(torch.int16)[torch.from_numpy(pidx[real]).to("cuda")]
+                   .view(torch.uint16))
+        assert_bits(got, out[4][real], f"DDP unpacked bf16 [{a}, {b})")
+        assert not out[0][~real].any() and not out[1][~real].any()      # pads stay 0
+        if k % 8 == 0 or k == hi_w - 1:
+            say(f"[{w.name} DDP] windows {lo_w}..{k} of {nwin} equal ({time.perf_counter() - t0:.1f} s)")
+    if part == n_parts - 1:
+        # each chunk owner's fused partial against the oracle's, window order
+        for c in range(P):
+            want = 0.0
+            for _, sq in sorted(acc[c]):
+                want = want + sq
+            assert abs(gs.partials[c] - want) <= 1e-5 * want, (c, gs.partials[c], want)
+        assert o_clip(gs.total, w.hp.max_norm) == (gs.norm, gs.coef)
+        say(f"[{w.name} DDP] {P} partials within {max(abs(gs.partials[c] - sum(s for _, s in acc[c])) / gs.partials[c] for c in range(P)):.1e}; coef {gs.coef!r}")
+        _ddp.clear()
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("part", [0, 1])
+def test_gpt_1_3b_ddp_step_every_flat_position(part):
+    compare_ddp_windows(2, part, 2)
