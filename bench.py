@@ -89,12 +89,27 @@ SHORT = {"k_pack": "k_pack", "k_reduce_mean": "k_reduce_mean", "k_adamw": "k_ada
          "synth_read_kernel": "read_probe", "synth_write_kernel": "write_probe"}
 
 
+def reduce_kernel(P, S, layout):
+    """Short name of the kernel the library runs for a bf16 shard reduce: the
+    burst kernel at P = 24, 32, 64 and 96 on shards of 2^24 elements or more,
+    else the one-tile-per-block kernel (P > 16) or the lane-contiguous one."""
+    base = "k_reduce_burst" if P in (24, 32, 64, 96) and S >= 1 << 24 else "k_reduce_mean"
+    return base + ("_ilv" if layout == "interleaved" else "")
+
+
 def short_name(full):
     # template instances that move different bytes get their own names
     if "k_pack<1>" in full:
         return "k_unpack"
     if "k_pack<2>" in full:
         return "k_accumulate"
+    if "k_reduce_burst<" in full:            # <PS, NORM, LAY, W16>
+        args = [a.strip() for a in full.split("k_reduce_burst<")[1].split(">")[0].split(",")]
+        if len(args) == 4 and args[3] == "true":
+            return "k_reduce_burst_bf16_wire"
+        if len(args) >= 3 and args[2] == "2":
+            return "k_reduce_burst_ilv"
+        return "k_reduce_burst"
     if "k_reduce_mean<" in full:             # <PS, NORM, LAY, OUTFLAT, W16>
         args = [a.strip() for a in full.split("k_reduce_mean<")[1].split(">")[0].split(",")]
         if len(args) == 5 and args[4] == "true":
@@ -720,8 +735,8 @@ def main():
     dom = max(("shard_reduce_mean", "shard_adamw_step"), key=lambda n: per[n])
     dom_bytes, dom_ms = byts[dom], per[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    kernel_symbol = {"shard_reduce_mean": "k_reduce_mean_ilv" if layout == "interleaved"
-                     else "k_reduce_mean", "shard_adamw_step": "k_adamw"}[dom]
+    kernel_symbol = {"shard_reduce_mean": reduce_kernel(P, S, layout),
+                     "shard_adamw_step": "k_adamw"}[dom]
     traffic = read_traffic(kernel_symbol, profile_name(w.name, "zero", layout))
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"[gpu] {ms_step:.3f} ms/step, {step_gbps:.0f} GB/s; " + "; ".join(

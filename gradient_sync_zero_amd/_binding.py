@@ -88,7 +88,8 @@ _SIGS = {
     "gsz_adamw_step": [_P, _P, _P, _P, _I64, _P, ctypes.POINTER(AdamWHP), _P, _P],
 }
 
-_TEST_SIGS = {"gsz_test_set_grid_limit": [ctypes.c_int64]}
+_TEST_SIGS = {"gsz_test_set_grid_limit": [ctypes.c_int64],
+              "gsz_test_set_reduce_path": [_I32]}
 
 _libs = {}
 _active = threading.local()
@@ -128,7 +129,7 @@ def load(path=None):
 @contextlib.contextmanager
 def test_hooks():
     """Within the block, calls made by this thread go to libgsz_test.so, the
-    same sources built with the test hooks (set_grid_limit).  Plans keep the
+    same sources built with the test hooks (set_grid_limit, set_reduce_path).  Plans keep the
     library they were created with, so create them inside the block."""
     load(TEST_LIB_PATH)
     prev = getattr(_active, "path", LIB_PATH)
@@ -320,15 +321,30 @@ def workspace_bytes(n):
     return out.value
 
 
+def _test_lib(what):
+    lib = load()
+    if lib is not _libs.get(TEST_LIB_PATH):
+        raise RuntimeError(f"{what} exists only in the test build; call it inside test_hooks()")
+    return lib
+
+
 def set_grid_limit(max_blocks):
     """Test build only (inside test_hooks()): caps the blocks of every later
     data-sized launch, process-wide (0 restores the built-in caps); blocks then
     stride over several tiles."""
-    lib = load()
-    if not hasattr(lib, "gsz_test_set_grid_limit") or lib is not _libs.get(TEST_LIB_PATH):
-        raise RuntimeError("set_grid_limit exists only in the test build; call it inside "
-                           "test_hooks()")
+    lib = _test_lib("set_grid_limit")
     _check(lib.gsz_test_set_grid_limit(int(max_blocks)), lib)
+
+
+REDUCE_PATH_BY_SIZE, REDUCE_PATH_BURST, REDUCE_PATH_TILE = 0, 1, 2
+
+
+def set_reduce_path(path):
+    """Test build only (inside test_hooks()): the kernel of every later bf16
+    reduce at P > 16, process-wide: REDUCE_PATH_BY_SIZE (the product's rule),
+    REDUCE_PATH_BURST or REDUCE_PATH_TILE."""
+    lib = _test_lib("set_reduce_path")
+    _check(lib.gsz_test_set_reduce_path(int(path)), lib)
 
 
 def bucket_pack(plan, grads, flat, stream=None):

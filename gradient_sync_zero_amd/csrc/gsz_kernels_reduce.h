@@ -39,19 +39,63 @@ __device__ __forceinline__ int64_t contrib_index(SegCursor& cur, int64_t i, int 
     else return i;
 }
 
-// g[i] = (((c0 + c1) + c2) + ... + c_{P-1}) / P with rp.p[k] = contribution of
-// rank (owner+1+k) mod P, so the owner's own value is added last.  Each lane
-// handles 8 consecutive shard elements per iteration (one 16-byte load per
-// rank).  PS > 0 fixes P at compile time; loads are issued in groups of up to
-// 32 ranks before their adds so many 16-byte requests are in flight.  With
-// OUTFLAT (bucket-flat input only) g is indexed by flat position instead of
-// shard index: P launches, one per chunk owner, give the all-reduce result.
-// W16: the partial sum is rounded to bf16 after every addition (a ring whose
-// wire carries bf16 partial sums); the final division stays fp32.  Loads and
-// stores are nontemporal (2% faster at P = 8, 5% at P = 64 than plain ones).
-// This kernel serves P > 16 (compile-time P for 24, 32, 64 and 96, its
-// runtime-P loop for the others); P <= 16 runs k_reduce_mean_lc below.  LAY
-// is one of the layouts above (kLayFlat for OUTFLAT).
+// a[0..8) = the ring-order mean of the 8 consecutive elements at offset off of
+// every contribution: (((c0 + c1) + c2) + ... + c_{P-1}) / P with rp.p[k] the
+// contribution of rank (owner+1+k) mod P, so the owner's own value is added
+// last.  PS > 0 fixes P at compile time; loads are issued in groups of up to
+// 32 ranks before their adds so many 16-byte requests are in flight.  W16: the
+// partial sum is rounded to bf16 after every addition (a ring whose wire
+// carries bf16 partial sums); the final division stays fp32.
+template <int PS, bool W16>
+__device__ __forceinline__ void ring_mean8(const RankPtrs& rp, int P, float invP, int pow2,
+                                           int64_t off, float a[8]) {
+    if constexpr (PS > 0) {
+        // up to 32 loads before their adds (at P = 64 that measured 1.4% faster than 16)
+        constexpr int G = load_group(PS, 32);
+        static_assert(PS % G == 0, "the groups cover exactly the P contributions");
+#pragma unroll
+        for (int k0 = 0; k0 < PS; k0 += G) {
+            u32x4 w[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) w[j] = ld16_nt(rp.p[k0 + j] + off);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                if (k0 + j == 0) widen8(w[j], a);
+                else { add8(w[j], a); if (W16) round8_bf16(a); }
+            }
+        }
+    } else {
+        widen8(ld16_nt(rp.p[0] + off), a);
+        int k = 1;
+        for (; k + 8 <= P; k += 8) {
+            u32x4 w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w[j] = ld16_nt(rp.p[k + j] + off);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { add8(w[j], a); if (W16) round8_bf16(a); }
+        }
+        for (; k < P; ++k) { add8(ld16_nt(rp.p[k] + off), a); if (W16) round8_bf16(a); }
+    }
+    if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = a[j] * invP;   // exact: invP is a power of two
+    } else {
+        const float fP = (float)P;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a[j] = a[j] / fP;
+    }
+}
+
+// g[i] = ring_mean8 of element i, one tile of kRedTile shard elements per
+// block.  Each lane handles 8 consecutive shard elements per iteration (one
+// 16-byte load per rank).  With OUTFLAT (bucket-flat input only) g is indexed
+// by flat position instead of shard index: P launches, one per chunk owner,
+// give the all-reduce result.  Loads and stores are nontemporal (2% faster at
+// P = 8, 5% at P = 64 than plain ones).  This kernel serves P > 16 on shards
+// below the burst kernel's size (compile-time P for 24, 32, 64 and 96, its
+// runtime-P loop for the others) and the all-reduce; P <= 16 runs
+// k_reduce_mean_lc below.  LAY is one of the layouts above (kLayFlat for
+// OUTFLAT).
 template <int PS, bool NORM, int LAY, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
                                                         const int64_t* __restrict__ seg,
@@ -76,47 +120,13 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
     SegCursor cur{seg, owner, 0, 0, 0};
     const int64_t S = nvec * 8;
     if (FLAT && bx * kRedTile < S) cur.seek(bx * kRedTile, slut, sshift);  // uniform: scalar loads
-    const float fP = (float)P;
     for (int64_t v0 = bx * kBlock + wave * 64; v0 < nvec; v0 += stride) {
         const int64_t v = v0 + lane;
         const bool ok = v < nvec;
         const int64_t i = v * 8;
         const int64_t off = ok ? contrib_index<LAY>(cur, i, PS > 0 ? PS : P) : 0;
         float a[8];
-        if constexpr (PS > 0) {
-            // up to 32 loads before their adds (at P = 64 that measured 1.4% faster than 16)
-            constexpr int G = load_group(PS, 32);
-            static_assert(PS % G == 0, "the groups cover exactly the P contributions");
-#pragma unroll
-            for (int k0 = 0; k0 < PS; k0 += G) {
-                u32x4 w[G];
-#pragma unroll
-                for (int j = 0; j < G; ++j) w[j] = ld16_nt(rp.p[k0 + j] + off);
-#pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    if (k0 + j == 0) widen8(w[j], a);
-                    else { add8(w[j], a); if (W16) round8_bf16(a); }
-                }
-            }
-        } else {
-            widen8(ld16_nt(rp.p[0] + off), a);
-            int k = 1;
-            for (; k + 8 <= P; k += 8) {
-                u32x4 w[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) w[j] = ld16_nt(rp.p[k + j] + off);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) { add8(w[j], a); if (W16) round8_bf16(a); }
-            }
-            for (; k < P; ++k) { add8(ld16_nt(rp.p[k] + off), a); if (W16) round8_bf16(a); }
-        }
-        if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a[j] = a[j] * invP;   // exact: invP is a power of two
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) a[j] = a[j] / fP;
-        }
+        ring_mean8<PS, W16>(rp, P, invP, pow2, off, a);
         if constexpr (OUTFLAT) {
             if (ok) {                           // all-reduce output: the flat position
                 stf4_nt(g + off, f32x4{a[0], a[1], a[2], a[3]});
@@ -147,6 +157,89 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
     if (NORM) {
         const double s = block_sum(sq);
         if (threadIdx.x == 0) ws[bx] = s;
+    }
+}
+
+// ------------------------------------------------------ burst reduce-mean --
+
+// The same g as k_reduce_mean, for large shards at P > 16, with g reaching HBM
+// in bursts: one block per CU (its 128 KiB of LDS admit no second one) takes
+// chunks of kBurstElems shard elements, reduces a whole chunk into LDS (wave w
+// takes the chunk's 512-element rows w, w + 4, ...) and then writes it to g as
+// one contiguous run of whole-line stores.  Against the one-tile-per-block
+// launch, whose every wave stores its 2 KiB as soon as it is reduced, this ran
+// 5% faster at P = 64 on 64 separate 2.2 GB contributions and 10% faster over
+// one interleaved receive buffer: stores scattered among the reads cost the
+// read stream far more than their bytes (without its stores the same kernel
+// reads 10-20% faster; writing half as many g lines costs nearly as much as
+// writing all of them).  Chunks go to XCDs in contiguous ranges (xcd_chunks);
+// the norm partials, one per block, are summed in block order by the
+// finalize.
+constexpr int kBurstRows = 64;
+constexpr int64_t kBurstElems = (int64_t)kBurstRows * 512;   // 128 KiB of fp32
+
+// Chunk range of block b in a grid of G blocks over `chunks` chunks.  The blocks
+// with b mod 8 == x run on XCD x; that class takes a contiguous share of the
+// chunks in proportion to its number of blocks, and its blocks advance through
+// the share together: block b takes the share's chunk b / 8, then every
+// n_x-th after it.  Every chunk goes to exactly one block.
+__device__ __forceinline__ void xcd_chunks(int64_t chunks, int64_t G, int64_t b, int64_t& c0,
+                                           int64_t& c1, int64_t& step) {
+    const int64_t x = b % kXcds;
+    int64_t before = 0;                                  // blocks in the classes below x
+    for (int64_t y = 0; y < x; ++y) before += (G - y + kXcds - 1) / kXcds;
+    const int64_t nx = (G - x + kXcds - 1) / kXcds;      // blocks in class x (>= 1: b is one)
+    c0 = chunks * before / G + b / kXcds;
+    c1 = chunks * (before + nx) / G;
+    step = nx;
+}
+
+template <int PS, bool NORM, int LAY, bool W16 = false>
+__global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, float invP, int pow2,
+                                                         const int64_t* __restrict__ seg,
+                                                         const uint64_t* __restrict__ slut, int sshift,
+                                                         int64_t owner, int64_t S,
+                                                         float* __restrict__ g,
+                                                         double* __restrict__ ws) {
+    __shared__ float res[kBurstElems];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t chunks = (S + kBurstElems - 1) / kBurstElems;
+    int64_t c, c1, step;
+    xcd_chunks(chunks, gridDim.x, blockIdx.x, c, c1, step);
+    double sq = 0.0;
+    SegCursor cur{seg, owner, 0, 0, 0};
+    for (; c < c1; c += step) {
+        const int64_t base = c * kBurstElems;
+        const int64_t n = S - base < kBurstElems ? S - base : kBurstElems;   // a multiple of 8
+        if (LAY == kLayFlat) cur.seek(base, slut, sshift);                   // uniform: scalar loads
+        // Rows r with r * 512 < n: r <= kBurstRows - 1, so j < kBurstElems (LDS in
+        // bounds).  Lanes past n load position 0 of every contribution (in
+        // bounds; unconditional loads keep them in flight together) and their
+        // results are never stored to g.
+        for (int r = wave; (int64_t)r * 512 < n; r += kBlock / 64) {
+            const int j = r * 512 + 8 * lane;
+            const bool ok = j < n;
+            const int64_t off = ok ? contrib_index<LAY>(cur, base + j, PS > 0 ? PS : P) : 0;
+            float a[8];
+            ring_mean8<PS, W16>(rp, P, invP, pow2, off, a);
+            *reinterpret_cast<f32x4*>(res + j) = f32x4{a[0], a[1], a[2], a[3]};
+            *reinterpret_cast<f32x4*>(res + j + 4) = f32x4{a[4], a[5], a[6], a[7]};
+            if (NORM && ok) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const double d = (double)a[k];
+                    sq = __fma_rn(d, d, sq);                        // d*d is exact in fp64
+                }
+            }
+        }
+        __syncthreads();
+        for (int64_t e = 4 * (int64_t)threadIdx.x; e < n; e += 4 * kBlock)
+            stf4_nt(g + base + e, *reinterpret_cast<const f32x4*>(res + e));
+        __syncthreads();                                 // the next chunk overwrites res
+    }
+    if (NORM) {
+        const double s = block_sum(sq);
+        if (threadIdx.x == 0) ws[blockIdx.x] = s;
     }
 }
 

@@ -27,6 +27,7 @@ namespace {
 // ------------------------------------------------------------ host side --
 
 std::atomic<int> g_dev_state[64];   // 0 unknown, 1 gfx950, -1 other
+std::atomic<int> g_dev_cus[64];     // compute units, set before g_dev_state
 
 int hip_fail(const char* what, hipError_t e) {
     set_error("%s: %s", what, hipGetErrorString(e));
@@ -45,6 +46,7 @@ int current_device(int* dev_out) {
         e = hipGetDeviceProperties(&prop, dev);
         if (e != hipSuccess) return hip_fail("hipGetDeviceProperties", e);
         st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_dev_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1);
         g_dev_state[dev].store(st);
     }
     if (st != 1) { set_error("device %d is not gfx950 (MI355X); this library targets gfx950 only", dev); return GSZ_ERR_DEVICE; }
@@ -58,6 +60,9 @@ int current_device(int* dev_out) {
 // run the block-striding path that otherwise only inputs of more than about
 // 17e9 elements reach.  The product library has no such state.
 std::atomic<int64_t> g_grid_limit{0};
+// Which kernel the bf16 reduce at P > 16 uses: 0 by shard size, 1 always the
+// burst kernel, 2 never (so that small test shards reach both).
+std::atomic<int> g_reduce_path{0};
 #endif
 
 // Blocks of a one-tile-per-block launch over n_tiles tiles: at most `builtin`
@@ -207,10 +212,63 @@ void launch_reduce(bool norm, int lay, dim3 grid, hipStream_t st, const RankPtrs
     }
 }
 
+// The largest world size of the lane-contiguous bf16 reduce (launch_reduce_lc).
+constexpr int kLcMaxP = 16;
+
+// The burst reduce (k_reduce_burst) serves bf16 contributions at the world sizes
+// above kLcMaxP with unrolled kernels (24, 32, 64 and 96) on shards of at least
+// kBurstMinElems elements: one block per CU, at most one per chunk.  Measured
+// against the one-tile-per-block kernel on 64 GB of shard-compact
+// contributions: 2-3% faster at P = 24, 32, 64 and 96; the runtime-P loop
+// (P = 17, 48, 128, 256) gained nothing or lost up to 13% with only four waves
+// per CU to hide its latency, so those P keep the tile kernel.  Below
+// kBurstMinElems the tile kernel has more blocks to spread over the chip.
+constexpr int64_t kBurstMinElems = (int64_t)1 << 24;
+
+bool use_burst(int P, int64_t S) {
+#ifdef GSZ_TEST_HOOKS
+    const int forced = g_reduce_path.load(std::memory_order_relaxed);
+    if (forced == 1) return P > kLcMaxP;
+    if (forced == 2) return false;
+#endif
+    return (P == 24 || P == 32 || P == 64 || P == 96) && S >= kBurstMinElems;
+}
+
+int burst_grid(int dev, int64_t S) {
+    const int64_t chunks = (S + kBurstElems - 1) / kBurstElems;
+    int64_t g = g_dev_cus[dev].load();
+    if (g < 1) g = 1;
+#ifdef GSZ_TEST_HOOKS
+    const int64_t lim = g_grid_limit.load(std::memory_order_relaxed);
+    if (lim > 0 && lim < g) g = lim;
+#endif
+    return (int)(chunks < g ? (chunks < 1 ? 1 : chunks) : g);
+}
+
+template <int PS>
+void launch_reduce_burst(bool norm, int lay, bool wire16, dim3 grid, hipStream_t st,
+                         const RankPtrs& rp, int P, float invP, int pow2, const int64_t* seg,
+                         const uint64_t* slut, int sshift, int64_t owner, int64_t S, float* g,
+                         double* ws) {
+    auto go = [&](auto nm, auto ly, auto w16) {
+        hipLaunchKernelGGL((k_reduce_burst<PS, decltype(nm)::value, decltype(ly)::value,
+                                           decltype(w16)::value>),
+                           grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner,
+                           S, g, ws);
+    };
+    auto layouts = [&](auto w16) {
+        with_layout(lay, [&](auto ly) {
+            if (norm) go(std::true_type{}, ly, w16);
+            else go(std::false_type{}, ly, w16);
+        });
+    };
+    if (wire16) layouts(std::true_type{});
+    else layouts(std::false_type{});
+}
+
 // The lane-contiguous reduce (k_reduce_mean_lc) for bf16 contributions at
 // P <= kLcMaxP (compile-time P for 2, 3, 4, 6, 8 and 16, its runtime-P loop for
 // the others) and for fp32 contributions at every P.
-constexpr int kLcMaxP = 16;
 
 template <typename T, int PS>
 void launch_reduce_lc(bool norm, int lay, bool outflat, bool wire16, dim3 grid, hipStream_t st,
@@ -258,6 +316,15 @@ extern "C" int gsz_test_set_grid_limit(int64_t max_blocks) {
         return GSZ_ERR_INVALID_ARG;
     }
     g_grid_limit.store(max_blocks, std::memory_order_relaxed);
+    return GSZ_OK;
+}
+
+extern "C" int gsz_test_set_reduce_path(int32_t path) {
+    if (path < 0 || path > 2) {
+        set_error("gsz_test_set_reduce_path: path %d is not 0, 1 or 2", (int)path);
+        return GSZ_ERR_INVALID_ARG;
+    }
+    g_reduce_path.store(path, std::memory_order_relaxed);
     return GSZ_OK;
 }
 #endif
@@ -407,8 +474,12 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         }
     }
     const int64_t nvec = S / 8;
-    const int grid = flat_grid((S + kRedTile - 1) / kRedTile);
+    int grid = flat_grid((S + kRedTile - 1) / kRedTile);
     const int lay = layout == GSZ_LAYOUT_BUCKET_FLAT ? kLayFlat : ilv ? kLayInterleaved : kLayCompact;
+    // The bf16 reduce at P > kLcMaxP on a large shard runs the burst kernel,
+    // whose grid is one block per CU (at most one per chunk).
+    const bool burst = !f32in && use_burst(P, S);
+    if (burst) grid = burst_grid(p->device, S);
     // p[k] = the contribution of rank (owner + 1 + k) mod P: its buffer, or its
     // piece of the first tile of the interleaved buffer.
     auto rank_ptr = [&](int k, size_t esize) -> const void* {
@@ -448,9 +519,14 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
                     sshift, owner, S, g, wsd);
             };
             auto wide = [&](auto pc) {
-                launch_reduce<decltype(pc)::value>(norm, lay, dim3(grid), stream, rp, P, invP, pow2,
-                                                   p->d_seg, slut, sshift, owner, nvec, g, wsd,
-                                                   false, wire16);
+                if (burst)
+                    launch_reduce_burst<decltype(pc)::value>(norm, lay, wire16, dim3(grid), stream, rp,
+                                                             P, invP, pow2, p->d_seg, slut, sshift,
+                                                             owner, S, g, wsd);
+                else
+                    launch_reduce<decltype(pc)::value>(norm, lay, dim3(grid), stream, rp, P, invP,
+                                                       pow2, p->d_seg, slut, sshift, owner, nvec, g,
+                                                       wsd, false, wire16);
             };
             if constexpr (PS > kLcMaxP) wide(ps);
             else if constexpr (PS > 0) lc(ps);

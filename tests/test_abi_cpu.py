@@ -42,18 +42,25 @@ def test_test_hooks_live_only_in_the_test_build():
     have it; the test build exports everything the product does plus the
     hooks of gsz_test.h."""
     hooks = declared_symbols(TEST_HEADER)
-    assert hooks == ["gsz_test_set_grid_limit"]
+    assert hooks == ["gsz_test_set_grid_limit", "gsz_test_set_reduce_path"]
     prod = ctypes.CDLL(G.LIB_PATH)
     test = ctypes.CDLL(G._binding.TEST_LIB_PATH)
     assert not any(hasattr(prod, h) for h in hooks)
     assert all(hasattr(test, s) for s in declared_symbols() + hooks)
     with pytest.raises(RuntimeError):
         G.set_grid_limit(4)                      # outside test_hooks(): refused
+    with pytest.raises(RuntimeError):
+        G.set_reduce_path(G.REDUCE_PATH_BURST)
     with G.test_hooks():
         with pytest.raises(G.GszError) as e:     # the cap is a count of blocks
             G.set_grid_limit(-1)
         assert "-1" in str(e.value)
         G.set_grid_limit(0)
+        for bad in (-1, 3):
+            with pytest.raises(G.GszError) as e:
+                G.set_reduce_path(bad)
+            assert str(bad) in str(e.value)
+        G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
         p = G.Plan([5], 100, 2)
     with pytest.raises(ValueError):              # a plan is tied to its build
         G._binding._lib_for(p)

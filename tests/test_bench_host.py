@@ -61,6 +61,25 @@ def test_lane_contiguous_reduce_instances_are_named_by_row():
     assert bench.short_name(wide.format("64, true, 1, false, false")) == "k_reduce_mean"
     assert bench.short_name(wide.format("64, true, 2, false, false")) == "k_reduce_mean_ilv"
     assert bench.short_name(wide.format("0, true, 0, true, false")) == "k_allreduce_mean"
+    burst = "void (anonymous namespace)::k_reduce_burst<{}>(RankPtrs, int, float, int)"
+    assert bench.short_name(burst.format("64, true, 1, false")) == "k_reduce_burst"
+    assert bench.short_name(burst.format("64, true, 0, false")) == "k_reduce_burst"
+    assert bench.short_name(burst.format("64, true, 2, false")) == "k_reduce_burst_ilv"
+    assert bench.short_name(burst.format("24, true, 1, true")) == "k_reduce_burst_bf16_wire"
+
+
+def test_bench_names_the_reduce_kernel_the_library_runs():
+    """The burst kernel at the unrolled world sizes above 16 on shards of
+    2^24 elements or more; the tile kernel for the other world sizes and below
+    that size; the lane-contiguous kernel (named like the tile one) at P <= 16."""
+    big = 1 << 24
+    assert bench.reduce_kernel(64, 1077760128, "compact") == "k_reduce_burst"
+    assert bench.reduce_kernel(64, 1077760128, "interleaved") == "k_reduce_burst_ilv"
+    for P in (24, 32, 96):
+        assert bench.reduce_kernel(P, big, "flat") == "k_reduce_burst"
+        assert bench.reduce_kernel(P, big - 8, "flat") == "k_reduce_mean"
+    for P in (8, 16, 17, 48, 100, 128, 256):
+        assert bench.reduce_kernel(P, 1 << 30, "compact") == "k_reduce_mean"
 
 
 def test_counter_summary_scales_by_the_copy_kernel_and_is_keyed(tmp_path):
