@@ -221,17 +221,19 @@ constexpr int kLcMaxP = 16;
 // against the one-tile-per-block kernel on 64 GB of shard-compact
 // contributions: 2-3% faster at P = 24, 32, 64 and 96; the runtime-P loop
 // (P = 17, 48, 128, 256) gained nothing or lost up to 13% with only four waves
-// per CU to hide its latency, so those P keep the tile kernel.  Below
+// per CU to hide its latency, so those P keep the tile kernel; so does the
+// bf16 wire, whose rounding after every addition made the burst kernel 58%
+// slower at P = 64 (36 ms against 22.7 ms on the 70B share).  Below
 // kBurstMinElems the tile kernel has more blocks to spread over the chip.
 constexpr int64_t kBurstMinElems = (int64_t)1 << 24;
 
-bool use_burst(int P, int64_t S) {
+bool use_burst(int P, int64_t S, bool wire16) {
 #ifdef GSZ_TEST_HOOKS
     const int forced = g_reduce_path.load(std::memory_order_relaxed);
     if (forced == 1) return P > kLcMaxP;
     if (forced == 2) return false;
 #endif
-    return (P == 24 || P == 32 || P == 64 || P == 96) && S >= kBurstMinElems;
+    return !wire16 && (P == 24 || P == 32 || P == 64 || P == 96) && S >= kBurstMinElems;
 }
 
 int burst_grid(int dev, int64_t S) {
@@ -478,7 +480,7 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
     const int lay = layout == GSZ_LAYOUT_BUCKET_FLAT ? kLayFlat : ilv ? kLayInterleaved : kLayCompact;
     // The bf16 reduce at P > kLcMaxP on a large shard runs the burst kernel,
     // whose grid is one block per CU (at most one per chunk).
-    const bool burst = !f32in && use_burst(P, S);
+    const bool burst = !f32in && use_burst(P, S, wire16);
     if (burst) grid = burst_grid(p->device, S);
     // p[k] = the contribution of rank (owner + 1 + k) mod P: its buffer, or its
     // piece of the first tile of the interleaved buffer.

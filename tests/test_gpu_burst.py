@@ -1,5 +1,5 @@
 """GPU parity of the burst reduce (k_reduce_burst): the kernel of the bf16
-reduce at P = 24, 32, 64 and 96 on shards of 2^24 elements or more, which
+reduce (fp32 wire) at P = 24, 32, 64 and 96 on shards of 2^24 elements or more, which
 reduces chunks of 32768 shard elements into LDS and writes each chunk to g in
 one run.  The test build's gsz_test_set_reduce_path sends small shards and the
 other world sizes above 16 to it, so that every world size the 16-byte kernels
