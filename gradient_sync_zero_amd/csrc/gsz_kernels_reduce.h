@@ -168,30 +168,44 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
 // takes the chunk's 512-element rows w, w + 4, ...) and then writes it to g as
 // one contiguous run of whole-line stores.  Against the one-tile-per-block
 // launch, whose every wave stores its 2 KiB as soon as it is reduced, this ran
-// 5% faster at P = 64 on 64 separate 2.2 GB contributions and 10% faster over
-// one interleaved receive buffer: stores scattered among the reads cost the
-// read stream far more than their bytes (without its stores the same kernel
-// reads 10-20% faster; writing half as many g lines costs nearly as much as
-// writing all of them).  Chunks go to XCDs in contiguous ranges (xcd_chunks);
-// the norm partials, one per block, are summed in block order by the
-// finalize.
+// 3-5% faster at P = 64 on 64 separate contributions of 1.08e9 elements:
+// stores scattered among the reads cost the read stream far more than their
+// bytes (without its stores the same kernel takes 14-23% less time, and
+// writing half as many g lines costs 82% as much time as writing all of them).
+// Chunks go to XCDs in contiguous ranges (burst_work); the norm partials, one
+// per block, are summed in block order by the finalize.
 constexpr int kBurstRows = 64;
 constexpr int64_t kBurstElems = (int64_t)kBurstRows * 512;   // 128 KiB of fp32
 
-// Chunk range of block b in a grid of G blocks over `chunks` chunks.  The blocks
+// The work of block b in a grid of G blocks over S shard elements.  The blocks
 // with b mod 8 == x run on XCD x; that class takes a contiguous share of the
-// chunks in proportion to its number of blocks, and its blocks advance through
-// the share together: block b takes the share's chunk b / 8, then every
-// n_x-th after it.  Every chunk goes to exactly one block.
-__device__ __forceinline__ void xcd_chunks(int64_t chunks, int64_t G, int64_t b, int64_t& c0,
-                                           int64_t& c1, int64_t& step) {
-    const int64_t x = b % kXcds;
+// chunks in proportion to its n_x blocks, and its blocks advance through the
+// share together: `rounds` times, block b takes chunk first + i * n_x.  What
+// is left of the share after the last round in which every block of the class
+// has a whole chunk (fewer than n_x chunks) is split into n_x pieces of whole
+// 512-element rows, [tail0, tail1) for this block, so that the blocks of a
+// class finish together instead of half of them idling for a chunk's time.
+// Every element goes to exactly one block; a piece has at most kBurstRows rows.
+struct BurstWork { int64_t first, rounds, step, tail0, tail1; };
+
+__device__ __forceinline__ BurstWork burst_work(int64_t S, int64_t G, int64_t b) {
+    const int64_t chunks = (S + kBurstElems - 1) / kBurstElems;
+    const int64_t x = b % kXcds, kb = b / kXcds;
     int64_t before = 0;                                  // blocks in the classes below x
     for (int64_t y = 0; y < x; ++y) before += (G - y + kXcds - 1) / kXcds;
     const int64_t nx = (G - x + kXcds - 1) / kXcds;      // blocks in class x (>= 1: b is one)
-    c0 = chunks * before / G + b / kXcds;
-    c1 = chunks * (before + nx) / G;
-    step = nx;
+    const int64_t c0 = chunks * before / G, c1 = chunks * (before + nx) / G;
+    BurstWork w;
+    w.first = c0 + kb;
+    w.step = nx;
+    w.rounds = (c1 - c0) / nx;
+    const int64_t e0 = (c0 + w.rounds * nx) * kBurstElems;
+    const int64_t e1 = c1 * kBurstElems < S ? c1 * kBurstElems : S;
+    const int64_t rows = e1 > e0 ? (e1 - e0 + 511) / 512 : 0;  // fewer than n_x chunks' rows
+    const int64_t t0 = e0 + rows * kb / nx * 512, t1 = e0 + rows * (kb + 1) / nx * 512;
+    w.tail0 = t0 < e1 ? t0 : e1;
+    w.tail1 = t1 < e1 ? t1 : e1;
+    return w;
 }
 
 template <int PS, bool NORM, int LAY, bool W16 = false>
@@ -203,14 +217,12 @@ __global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, flo
                                                          double* __restrict__ ws) {
     __shared__ float res[kBurstElems];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t chunks = (S + kBurstElems - 1) / kBurstElems;
-    int64_t c, c1, step;
-    xcd_chunks(chunks, gridDim.x, blockIdx.x, c, c1, step);
+    const BurstWork w = burst_work(S, gridDim.x, blockIdx.x);
     double sq = 0.0;
     SegCursor cur{seg, owner, 0, 0, 0};
-    for (; c < c1; c += step) {
-        const int64_t base = c * kBurstElems;
-        const int64_t n = S - base < kBurstElems ? S - base : kBurstElems;   // a multiple of 8
+    // Elements [base, base + n) of the shard, 0 < n <= kBurstElems, n and base
+    // multiples of 8: reduced into res, then written to g in one run.
+    auto burst = [&](int64_t base, int64_t n) {
         if (LAY == kLayFlat) cur.seek(base, slut, sshift);                   // uniform: scalar loads
         // Rows r with r * 512 < n: r <= kBurstRows - 1, so j < kBurstElems (LDS in
         // bounds).  Lanes past n load position 0 of every contribution (in
@@ -236,7 +248,12 @@ __global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, flo
         for (int64_t e = 4 * (int64_t)threadIdx.x; e < n; e += 4 * kBlock)
             stf4_nt(g + base + e, *reinterpret_cast<const f32x4*>(res + e));
         __syncthreads();                                 // the next chunk overwrites res
+    };
+    for (int64_t i = 0; i < w.rounds; ++i) {
+        const int64_t base = (w.first + i * w.step) * kBurstElems;
+        burst(base, S - base < kBurstElems ? S - base : kBurstElems);
     }
+    if (w.tail1 > w.tail0) burst(w.tail0, w.tail1 - w.tail0);
     if (NORM) {
         const double s = block_sum(sq);
         if (threadIdx.x == 0) ws[blockIdx.x] = s;
