@@ -92,3 +92,11 @@ def test_c_program_uses_the_abi(tmp_path):
     assert float(out["ledger"][0][0]) == G.ledger_bytes_per_param(8, 2)
     assert int(out["ledger"][0][2]) == G.workspace_bytes(842301952)
     assert int(out["bad"][0][0]) < 0
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no C compiler")
+def test_c_step_client_compiles(tmp_path):
+    """tests/c_step_client.c, the C-only client that the GPU tests run through
+    the whole step, builds against the header with no warning."""
+    from tests.test_gpu_c_client import build_client
+    assert os.path.exists(build_client(str(tmp_path)))

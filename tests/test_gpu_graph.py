@@ -139,3 +139,69 @@ def test_graph_replays_equal_eager_ddp_steps(cfg):
         for i, (x, y) in enumerate(zip(got, want[k])):
             assert_bits(x, y, f"DDP replay {k}, buffer {i}")
         del junk
+
+
+def test_graph_replays_equal_eager_burst_steps():
+    """The P=64 step with the burst reduce (forced on a shard of about three
+    chunks through the test build), shard-compact contributions, the bf16
+    parameters in shard layout, and the no-allocation reduce beside it,
+    captured once and replayed."""
+    import numpy as np
+    P, r = 64, 9
+    rng = np.random.default_rng(91)
+    with G.test_hooks():
+        G.set_reduce_path(G.REDUCE_PATH_BURST)
+        try:
+            plan = G.Plan([int(2.6 * 32768) * P], 1 << 40, P, 8).upload()
+            S = plan.shard_len
+            hp = G.make_hp(lr=2e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=10)
+            cs = [torch.from_numpy(rng.normal(0, 1e-3, S).astype(np.float32)).to(torch.bfloat16)
+                  .view(torch.uint16).cuda() for _ in range(P)]
+            ws = torch.zeros(G.workspace_bytes(S) // 8, dtype=torch.float64, device="cuda")
+
+            def buffers():
+                gen = torch.Generator(device="cuda").manual_seed(5)
+                th = torch.randn(S, device="cuda", generator=gen) * 0.02
+                m = torch.randn(S, device="cuda", generator=gen) * 1e-4
+                v = (torch.randn(S, device="cuda", generator=gen) * 1e-6).abs()
+                return dict(th=th, m=m, v=v, g=torch.empty(S, device="cuda"),
+                            g2=torch.empty(S, device="cuda"),
+                            parts=torch.full((P,), 0.25, dtype=torch.float64, device="cuda"),
+                            p2=torch.zeros(1, dtype=torch.float64, device="cuda"),
+                            coef=torch.empty(1, device="cuda"),
+                            out=torch.zeros(S, dtype=torch.uint16, device="cuda"))
+
+            def step(b):
+                G.shard_reduce_mean(plan, r, cs, G.LAYOUT_SHARD_COMPACT, b["g"], b["parts"][r:r + 1], ws)
+                G.shard_reduce_mean_noalloc(plan, r, cs, G.LAYOUT_SHARD_COMPACT, b["g2"], b["p2"])
+                G.clip_coef(b["parts"], 1.0, b["coef"])
+                G.shard_adamw_step(plan, r, b["th"], b["m"], b["v"], b["g"], b["coef"], hp, None, b["out"])
+
+            def snapshot(b):
+                torch.cuda.synchronize()
+                return [host(b[k]) for k in ("g", "g2", "parts", "p2", "coef", "th", "m", "v", "out")]
+
+            eager = buffers()
+            want = []
+            for _ in range(3):
+                step(eager)
+                want.append(snapshot(eager))
+            assert_bits(want[0][1], want[0][0], "no-allocation g against the workspace form")
+            b = buffers()
+            torch.cuda.synchronize()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                step(b)
+            torch.cuda.synchronize()
+            for k in range(3):
+                graph.replay()
+                junk = torch.randn(1 << 20, device="cuda").sum()    # eager work between replays
+                torch.cuda.synchronize()
+                got = snapshot(b)
+                for i, (x, y) in enumerate(zip(got, want[k])):
+                    assert_bits(x, y, f"burst replay {k}, buffer {i}")
+                del junk
+        finally:
+            G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
