@@ -60,8 +60,8 @@ int current_device(int* dev_out) {
 // run the block-striding path that otherwise only inputs of more than about
 // 17e9 elements reach.  The product library has no such state.
 std::atomic<int64_t> g_grid_limit{0};
-// Which kernel the bf16 reduce at P > 16 uses: 0 by shard size, 1 always the
-// burst kernel, 2 never (so that small test shards reach both).
+// Which kernel the bf16 reduce at P > 16 uses: 0 the product's rule (use_burst),
+// 1 always the burst kernel, 2 never (so that small test shards reach both).
 std::atomic<int> g_reduce_path{0};
 #endif
 
@@ -271,7 +271,6 @@ void launch_reduce_burst(bool norm, int lay, bool wire16, dim3 grid, hipStream_t
 // The lane-contiguous reduce (k_reduce_mean_lc) for bf16 contributions at
 // P <= kLcMaxP (compile-time P for 2, 3, 4, 6, 8 and 16, its runtime-P loop for
 // the others) and for fp32 contributions at every P.
-
 template <typename T, int PS>
 void launch_reduce_lc(bool norm, int lay, bool outflat, bool wire16, dim3 grid, hipStream_t st,
                       const RankPtrsT<T>& rp, int P, float invP, int pow2, const int64_t* seg,
