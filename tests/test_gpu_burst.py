@@ -201,3 +201,34 @@ def test_burst_noalloc_entry_point():
     torch.cuda.synchronize()
     assert_bits(host(g), ref, "burst, no-allocation entry point")
     check_partial(float(host(part)[0]), ref, "burst, no-allocation entry point")
+
+
+def test_product_rule_at_its_threshold():
+    """Without the forcing hook, P = 24 on a shard of exactly 2^24 elements
+    takes the burst kernel (its norm partial has the burst grid's grouping,
+    bit for bit) and 8 elements fewer take the tile kernel; g equals the
+    oracle either way."""
+    P = 24
+    rng = np.random.default_rng(67)
+    G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
+    for S in (1 << 24, (1 << 24) - 8):
+        plan = G.Plan([S * P], 1 << 40, P, 8).upload()
+        assert plan.shard_len == S
+        # bf16 bits with exponents 2^-27..2^12 and either sign: finite, quick to draw
+        cs = [(rng.integers(100, 140, S, dtype=np.uint16) << 7 | rng.integers(0, 128, S, dtype=np.uint16)
+               | (rng.integers(0, 2, S, dtype=np.uint16) << 15)).astype(np.uint16) for _ in range(P)]
+        dev_cs = [dev(c) for c in cs]
+        r = 11
+        ref = reduce_mean(cs, r)
+        g, part = reduce(plan, r, dev_cs, G.LAYOUT_SHARD_COMPACT, S)
+        assert_bits(g, ref, f"product rule, S={S}")
+        check_partial(part, ref, f"product rule, S={S}")
+        G.set_reduce_path(G.REDUCE_PATH_BURST)
+        _, part_burst = reduce(plan, r, dev_cs, G.LAYOUT_SHARD_COMPACT, S)
+        G.set_reduce_path(G.REDUCE_PATH_TILE)
+        _, part_tile = reduce(plan, r, dev_cs, G.LAYOUT_SHARD_COMPACT, S)
+        G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
+        want = part_burst if S >= 1 << 24 else part_tile
+        assert part == want, (S, part, part_burst, part_tile)
+        assert part_burst != part_tile or S < 4096, "the two groupings should differ in the last bits"
+        del dev_cs
