@@ -223,9 +223,11 @@ constexpr int kLcMaxP = 16;
 // (P = 17, 48, 128, 256) gained nothing or lost up to 13% with only four waves
 // per CU to hide its latency, so those P keep the tile kernel; so does the
 // bf16 wire, whose rounding after every addition made the burst kernel 58%
-// slower at P = 64 (36 ms against 22.7 ms on the 70B share).  Below
-// kBurstMinElems the tile kernel has more blocks to spread over the chip.
-constexpr int64_t kBurstMinElems = (int64_t)1 << 24;
+// slower at P = 64 (36 ms against 22.7 ms on the 70B share).  Over shard
+// sizes (P = 64 and 24): 4-12% faster from 2^23 to 2^27 elements, 3% at the
+// 70B share's 1.08e9, and 13-70% slower at 2^22 and below, where the tile
+// kernel has more blocks to spread over the chip.
+constexpr int64_t kBurstMinElems = (int64_t)1 << 23;
 
 bool use_burst(int P, int64_t S, bool wire16) {
 #ifdef GSZ_TEST_HOOKS

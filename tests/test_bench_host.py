@@ -70,9 +70,9 @@ def test_lane_contiguous_reduce_instances_are_named_by_row():
 
 def test_bench_names_the_reduce_kernel_the_library_runs():
     """The burst kernel at the unrolled world sizes above 16 on shards of
-    2^24 elements or more; the tile kernel for the other world sizes and below
+    2^23 elements or more; the tile kernel for the other world sizes and below
     that size; the lane-contiguous kernel (named like the tile one) at P <= 16."""
-    big = 1 << 24
+    big = 1 << 23
     assert bench.reduce_kernel(64, 1077760128, "compact") == "k_reduce_burst"
     assert bench.reduce_kernel(64, 1077760128, "interleaved") == "k_reduce_burst_ilv"
     for P in (24, 32, 96):

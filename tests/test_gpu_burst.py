@@ -1,5 +1,5 @@
 """GPU parity of the burst reduce (k_reduce_burst): the kernel of the bf16
-reduce (fp32 wire) at P = 24, 32, 64 and 96 on shards of 2^24 elements or more, which
+reduce (fp32 wire) at P = 24, 32, 64 and 96 on shards of 2^23 elements or more, which
 reduces chunks of 32768 shard elements into LDS and writes each chunk to g in
 one run.  The test build's gsz_test_set_reduce_path sends small shards and the
 other world sizes above 16 to it, so that every world size the 16-byte kernels
@@ -204,14 +204,14 @@ def test_burst_noalloc_entry_point():
 
 
 def test_product_rule_at_its_threshold():
-    """Without the forcing hook, P = 24 on a shard of exactly 2^24 elements
+    """Without the forcing hook, P = 24 on a shard of exactly 2^23 elements
     takes the burst kernel (its norm partial has the burst grid's grouping,
     bit for bit) and 8 elements fewer take the tile kernel; g equals the
     oracle either way."""
     P = 24
     rng = np.random.default_rng(67)
     G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
-    for S in (1 << 24, (1 << 24) - 8):
+    for S in (1 << 23, (1 << 23) - 8):
         plan = G.Plan([S * P], 1 << 40, P, 8).upload()
         assert plan.shard_len == S
         # bf16 bits with exponents 2^-27..2^12 and either sign: finite, quick to draw
@@ -228,7 +228,7 @@ def test_product_rule_at_its_threshold():
         G.set_reduce_path(G.REDUCE_PATH_TILE)
         _, part_tile = reduce(plan, r, dev_cs, G.LAYOUT_SHARD_COMPACT, S)
         G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
-        want = part_burst if S >= 1 << 24 else part_tile
+        want = part_burst if S >= 1 << 23 else part_tile
         assert part == want, (S, part, part_burst, part_tile)
         assert part_burst != part_tile or S < 4096, "the two groupings should differ in the last bits"
         del dev_cs
