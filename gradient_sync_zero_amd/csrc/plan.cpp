@@ -6,7 +6,8 @@
 // layer order); whole tensors only, a bucket closes once its bf16 bytes reach
 // the cap; each bucket is zero-padded to a multiple of P*align so it splits
 // into P equal chunks ("Data Parallelism: From Parameter Server to Ring
-// All-Reduce" §5: N chunks of size M/N); rank r owns chunk r of every bucket.
+// All-Reduce" §5: the buffer cut into N equal chunks); rank r owns chunk r of
+// every bucket.
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>

@@ -1,9 +1,10 @@
 """All-gather layout of the updated bf16 parameters.
 
-"Data Parallelism: DDP, ZeRO and FSDP", section "The three stages": ZeRO-1/2
-update the shard each rank owns and then all-gather the updated parameters.
-"Data Parallelism: From Parameter Server to Ring All-Reduce" §5: the
-all-gather leaves every rank with the full tensor, chunk c in position c.  So
+"Data Parallelism: DDP, ZeRO and FSDP", section "The three stages": under
+ZeRO-1/2 each rank updates its own shard, and an all-gather then gives every
+rank all of the new parameters.  "Data Parallelism: From Parameter Server to
+Ring All-Reduce" §5: after the all-gather each rank has the whole tensor, with
+chunk c back at position c.  So
 rank r's updated chunk of bucket b sits at flat [base_b + r*C_b, +C_b) of the
 gathered bucket-major buffer.
 """

@@ -1,17 +1,18 @@
 """Bucket plan: which gradient goes in which bucket, and which rank owns what.
 
 Followed passages:
-  * "Data parallelism in depth" §4.2 (The Bucket mechanism): gradients are
-    packed into buckets in reverse-compute order, default about 25 MB each; a
-    bucket's collective fires when every gradient in it is ready.
+  * "Data parallelism in depth" §4.2 (The Bucket mechanism): the buckets are
+    filled in the opposite of the order in which the forward pass computes the
+    tensors, about 25 MB by default, and a bucket's collective starts once all
+    of its gradients exist.
   * "Data Parallelism: DDP, ZeRO and FSDP", section "DDP, and why it works":
-    gradients are grouped into buckets of roughly 25 MB, produced in reverse
-    layer order; every rank must issue its buckets in the same order.
-  * "Data Parallelism: From Parameter Server to Ring All-Reduce" §5: a tensor of
-    size M is split into N chunks of size M/N; after the reduce-scatter every
-    rank owns one fully reduced chunk.
-  * "Data Parallelism: DDP, ZeRO and FSDP", section "The three stages": ZeRO-1/2
-    update the shard each rank owns after the reduce-scatter.
+    the same ~25 MB buckets in the backward (last layer first) order, and the
+    order must agree across ranks.
+  * "Data Parallelism: From Parameter Server to Ring All-Reduce" §5: the buffer
+    is cut into N equal chunks; when the reduce-scatter ends, each rank holds
+    the complete sum of exactly one of them.
+  * "Data Parallelism: DDP, ZeRO and FSDP", section "The three stages": under
+    ZeRO-1/2 a rank updates only its own shard, after the reduce-scatter.
 
 Readings where the pages are silent:
   * reverse order = the forward tensor list reversed (also inside a block);

@@ -5,7 +5,7 @@ reduce-scatter the gradients, clip with the global norm, update the owned
 shard, all-gather the updated bf16 parameters.  DDP / NO_SHARD ("Data
 parallelism in depth" §4.1 and §6.3): all-reduce the gradients, every rank
 updates the whole model.  "Data Parallelism: From Parameter Server to Ring
-All-Reduce" §1 and §10: every rank applies the same update (replica invariant).
+All-Reduce" §1 and §10: the replicas stay identical because each rank applies an identical update.
 """
 from __future__ import annotations
 
