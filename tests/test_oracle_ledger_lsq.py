@@ -24,6 +24,9 @@ def test_ledger_matches_printed_figures():
         (pp["param"], pp["grad"], pp["master"], pp["exp_avg"], pp["exp_avg_sq"])
     assert ledger.bytes_per_param(8, 0) == pp["total"]
     assert ledger.optimizer_share() == g["optimizer_share"]["value"]
+    f = g["fits_70B_on_32x80GB"]
+    assert (ledger.model_state_bytes(f["psi"], f["P"], 3) <= f["cap_bytes"]) == f["zero3_fits"]
+    assert (ledger.model_state_bytes(f["psi"], f["P"], 0) <= f["cap_bytes"]) == f["ddp_fits"]
     s = g["smallest_P_70B_zero3_80GB"]
     P = next(P for P in range(1, 1000)
              if ledger.model_state_bytes(s["psi"], P, 3) <= s["cap_bytes"])
