@@ -232,3 +232,33 @@ def test_product_rule_at_its_threshold():
         assert part == want, (S, part, part_burst, part_tile)
         assert part_burst != part_tile or S < 4096, "the two groupings should differ in the last bits"
         del dev_cs
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_burst_random_plans(seed):
+    """Random plans (1-40 tensors of 0-20,000 elements, caps 2-400 KB, align 8
+    or 64) at the burst kernel's world sizes, bucket-flat contributions, three
+    owners each, against the oracle."""
+    rng = np.random.default_rng([71, seed])
+    P = int(rng.choice([24, 32, 64, 96]))
+    align = int(rng.choice([8, 64]))
+    numel = [int(x) for x in rng.integers(0, 20000, int(rng.integers(1, 41)))]
+    cap = int(rng.integers(2_000, 400_000))
+    plan = G.Plan(numel, cap, P, align).upload()
+    oplan = make_plan(numel, cap, P, align)
+    S = plan.shard_len
+    say(f"seed {seed}: P={P} align={align} tensors={len(numel)} buckets={plan.n_buckets} S={S}")
+    pre = OI.prefix(numel)
+    flats, flats_dev = [], []
+    for q in range(P):
+        bits = wide_bf16(rng, sum(numel))
+        grads = [bits[s:s + k] for s, k in zip(pre, numel)]
+        flats.append(opack.pack(oplan, grads))
+        f = torch.full((plan.flat_len,), 0x7f7f, dtype=torch.int16, device="cuda").view(torch.uint16)
+        G.bucket_pack(plan, [dev(gq) for gq in grads], f)
+        flats_dev.append(f)
+    for r in sorted({0, P - 1, int(rng.integers(0, P))}):
+        ref = reduce_mean([opack.owner_view(oplan, f, r) for f in flats], r)
+        g, part = reduce(plan, r, flats_dev, G.LAYOUT_BUCKET_FLAT, S)
+        assert_bits(g, ref, f"burst, random plan {seed}, owner {r}")
+        check_partial(part, ref, f"burst, random plan {seed}, owner {r}")
