@@ -1,14 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of one rank's share of a synchronous data-parallel step on one
-MI355X: bucket pack -> ring-order reduce-mean (+ squared-norm partial) ->
-clip coefficient -> AdamW writing bf16 parameters in all-gather layout.
+MI355X.  The timed step is the metric's: ring-order reduce-mean of the P
+ranks' contributions (with the fused squared-norm partial) -> clip
+coefficient -> AdamW on the owned shard (fp32 master/m/v in place, bf16
+parameters out), (2P + 34) bytes per shard element.  The bucket pack, the
+first part of a rank's share, is timed as its own row.
 
-Workload (default): the 7B Llama-shaped share -- 6,738,415,616 parameters in
-291 tensors, P = 8 simulated ranks, 25 MiB buckets, owner 0's shard of
-842,301,952 elements.  All P ranks' bucket-major gradient buffers are resident
-in HBM; each timed step packs owner 0's per-tensor gradients into its own flat
-buffer, reduces owner 0's chunks over the 8 flat buffers, forms the clip
-coefficient, and updates the shard's fp32 master/m/v in place.
+Workload (default, --config 4): the 70B Llama-shaped share -- 68,976,648,192
+parameters in 723 tensors, P = 64 simulated ranks, 25 MiB buckets, owner 0's
+shard of 1,077,760,128 elements, its 64 shard-compact contributions (138 GB)
+resident in HBM with the fp32 state.  --config 2 and 3 (the 1.3B model and
+the 7B share, P = 8) reduce over the ranks' whole bucket-flat buffers and
+write the all-gather layout.
 
 Prints one JSON line (see the fields below).  Only N = 1 is supported: the
 simulated ranks live on one GPU.
