@@ -94,10 +94,10 @@ SHORT = {"k_pack": "k_pack", "k_reduce_mean": "k_reduce_mean", "k_adamw": "k_ada
 
 def reduce_kernel(P, S, layout):
     """Short name of the kernel the library runs for a bf16 shard reduce (fp32
-    on the wire): the burst kernel at P = 24, 32, 64 and 96 on shards of 2^23
-    elements or more, else the one-tile-per-block kernel (P > 16) or the
-    lane-contiguous one."""
-    base = "k_reduce_burst" if P in (24, 32, 64, 96) and S >= 1 << 23 else "k_reduce_mean"
+    on the wire): at P > 16 the burst kernel on shards of 2^23 elements or
+    more, else the one-tile-per-block kernel; the lane-contiguous kernel
+    (named like the tile one) at P <= 16."""
+    base = "k_reduce_burst" if P > 16 and S >= 1 << 23 else "k_reduce_mean"
     return base + ("_ilv" if layout == "interleaved" else "")
 
 

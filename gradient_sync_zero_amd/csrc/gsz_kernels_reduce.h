@@ -45,8 +45,11 @@ __device__ __forceinline__ int64_t contrib_index(SegCursor& cur, int64_t i, int 
 // last.  PS > 0 fixes P at compile time; loads are issued in groups of up to
 // 32 ranks before their adds so many 16-byte requests are in flight.  W16: the
 // partial sum is rounded to bf16 after every addition (a ring whose wire
-// carries bf16 partial sums); the final division stays fp32.
-template <int PS, bool W16>
+// carries bf16 partial sums); the final division stays fp32.  RG: loads in
+// flight per group of the runtime-P loop: 8, one contribution at a time for the
+// last (P-1) mod 8; or (where few waves share a CU) 32, then 8, then the rest as
+// one group.
+template <int PS, bool W16, int RG = 8>
 __device__ __forceinline__ void ring_mean8(const RankPtrs& rp, int P, float invP, int pow2,
                                            int64_t off, float a[8]) {
     if constexpr (PS > 0) {
@@ -67,6 +70,15 @@ __device__ __forceinline__ void ring_mean8(const RankPtrs& rp, int P, float invP
     } else {
         widen8(ld16_nt(rp.p[0] + off), a);
         int k = 1;
+        if constexpr (RG >= 32) {
+            for (; k + 32 <= P; k += 32) {
+                u32x4 w[32];
+#pragma unroll
+                for (int j = 0; j < 32; ++j) w[j] = ld16_nt(rp.p[k + j] + off);
+#pragma unroll
+                for (int j = 0; j < 32; ++j) { add8(w[j], a); if (W16) round8_bf16(a); }
+            }
+        }
         for (; k + 8 <= P; k += 8) {
             u32x4 w[8];
 #pragma unroll
@@ -74,7 +86,21 @@ __device__ __forceinline__ void ring_mean8(const RankPtrs& rp, int P, float invP
 #pragma unroll
             for (int j = 0; j < 8; ++j) { add8(w[j], a); if (W16) round8_bf16(a); }
         }
-        for (; k < P; ++k) { add8(ld16_nt(rp.p[k] + off), a); if (W16) round8_bf16(a); }
+        if constexpr (RG >= 32) {
+            // The last (P-1) mod 8 contributions as one group: slots past P
+            // reload contribution k (in bounds, the same lines) and are not
+            // added.  k and P are wave-uniform, so nothing diverges.
+            if (k < P) {
+                u32x4 w[7];
+#pragma unroll
+                for (int j = 0; j < 7; ++j) w[j] = ld16_nt(rp.p[k + j < P ? k + j : k] + off);
+#pragma unroll
+                for (int j = 0; j < 7; ++j)
+                    if (k + j < P) { add8(w[j], a); if (W16) round8_bf16(a); }
+            }
+        } else {
+            for (; k < P; ++k) { add8(ld16_nt(rp.p[k] + off), a); if (W16) round8_bf16(a); }
+        }
     }
     if (PS > 0 ? ((PS & (PS - 1)) == 0) : pow2) {
 #pragma unroll
@@ -233,7 +259,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, flo
             const bool ok = j < n;
             const int64_t off = ok ? contrib_index<LAY>(cur, base + j, PS > 0 ? PS : P) : 0;
             float a[8];
-            ring_mean8<PS, W16>(rp, P, invP, pow2, off, a);
+            ring_mean8<PS, W16, 32>(rp, P, invP, pow2, off, a);
             *reinterpret_cast<f32x4*>(res + j) = f32x4{a[0], a[1], a[2], a[3]};
             *reinterpret_cast<f32x4*>(res + j + 4) = f32x4{a[4], a[5], a[6], a[7]};
             if (NORM && ok) {

@@ -215,17 +215,18 @@ void launch_reduce(bool norm, int lay, dim3 grid, hipStream_t st, const RankPtrs
 // The largest world size of the lane-contiguous bf16 reduce (launch_reduce_lc).
 constexpr int kLcMaxP = 16;
 
-// The burst reduce (k_reduce_burst) serves bf16 contributions at the world sizes
-// above kLcMaxP with unrolled kernels (24, 32, 64 and 96) on shards of at least
-// kBurstMinElems elements: one block per CU, at most one per chunk.  Measured
-// against the one-tile-per-block kernel on 64 GB of shard-compact
-// contributions: 2-3% faster at P = 24, 32, 64 and 96; the runtime-P loop
-// (P = 17, 48, 128, 256) gained nothing or lost up to 13% with only four waves
-// per CU to hide its latency, so those P keep the tile kernel; so does the
-// bf16 wire, whose rounding after every addition made the burst kernel 58%
-// slower at P = 64 (36 ms against 22.7 ms on the 70B share).  Over shard
-// sizes (P = 64 and 24): 4-12% faster from 2^23 to 2^27 elements, 3% at the
-// 70B share's 1.08e9, and 13-70% slower at 2^22 and below, where the tile
+// The burst reduce (k_reduce_burst) serves bf16 contributions at every P above
+// kLcMaxP on shards of at least kBurstMinElems elements: one block per CU, at
+// most one per chunk.  Measured against the one-tile-per-block kernel on 64 GB
+// of shard-compact contributions: 2-3% faster at P = 24, 32, 64 and 96 (the
+// unrolled kernels) and 1.5-7% faster at P = 17, 33, 40, 48, 100, 128, 200 and
+// 256 (the runtime-P loop, which in this kernel keeps 32 loads in flight and
+// issues its last (P-1) mod 8 together; one at a time, as the tile kernel's
+// loop does with more waves to hide them, it was up to 13% slower).  The bf16
+// wire keeps the tile kernel: its rounding after every addition made the burst
+// kernel 58% slower at P = 64 (36 ms against 22.7 ms on the 70B share).  Over
+// shard sizes (P = 64 and 24): 4-12% faster from 2^23 to 2^27 elements, 3% at
+// the 70B share's 1.08e9, and 13-70% slower at 2^22 and below, where the tile
 // kernel has more blocks to spread over the chip.
 constexpr int64_t kBurstMinElems = (int64_t)1 << 23;
 
@@ -235,7 +236,7 @@ bool use_burst(int P, int64_t S, bool wire16) {
     if (forced == 1) return P > kLcMaxP;
     if (forced == 2) return false;
 #endif
-    return !wire16 && (P == 24 || P == 32 || P == 64 || P == 96) && S >= kBurstMinElems;
+    return !wire16 && P > kLcMaxP && S >= kBurstMinElems;
 }
 
 int burst_grid(int dev, int64_t S) {

@@ -28,10 +28,10 @@ int gsz_test_set_grid_limit(int64_t max_blocks);
 
 /* Chooses the kernel of the bf16 reduce at P > 16 (gsz_shard_reduce_mean, its
  * bf16-wire and no-allocation forms) for every call made after this one, for
- * the whole process: 0 the product's rule (the burst kernel at P = 24, 32, 64
- * and 96 from 2^23 shard elements without the bf16 wire, else the
- * one-tile-per-block kernel), 1 always the burst kernel (every P > 16, the
- * bf16 wire too), 2 always the one-tile-per-block kernel.  g is
+ * the whole process: 0 the product's rule (the burst kernel from 2^23 shard
+ * elements without the bf16 wire, else the one-tile-per-block kernel), 1
+ * always the burst kernel (the bf16 wire too), 2 always the
+ * one-tile-per-block kernel.  g is
  * bit-identical either way; the norm partial's fp64 summation grouping
  * follows the kernel and its grid (the burst kernel's grid is one block per
  * compute unit, at most one per 32768 elements, and gsz_test_set_grid_limit

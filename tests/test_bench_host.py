@@ -69,16 +69,16 @@ def test_lane_contiguous_reduce_instances_are_named_by_row():
 
 
 def test_bench_names_the_reduce_kernel_the_library_runs():
-    """The burst kernel at the unrolled world sizes above 16 on shards of
-    2^23 elements or more; the tile kernel for the other world sizes and below
-    that size; the lane-contiguous kernel (named like the tile one) at P <= 16."""
+    """The burst kernel at every world size above 16 on shards of 2^23
+    elements or more; the tile kernel below that size; the lane-contiguous
+    kernel (named like the tile one) at P <= 16."""
     big = 1 << 23
     assert bench.reduce_kernel(64, 1077760128, "compact") == "k_reduce_burst"
     assert bench.reduce_kernel(64, 1077760128, "interleaved") == "k_reduce_burst_ilv"
-    for P in (24, 32, 96):
+    for P in (17, 24, 32, 48, 96, 100, 256):
         assert bench.reduce_kernel(P, big, "flat") == "k_reduce_burst"
         assert bench.reduce_kernel(P, big - 8, "flat") == "k_reduce_mean"
-    for P in (8, 16, 17, 48, 100, 128, 256):
+    for P in (2, 8, 16):
         assert bench.reduce_kernel(P, 1 << 30, "compact") == "k_reduce_mean"
 
 

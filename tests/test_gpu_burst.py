@@ -1,10 +1,10 @@
 """GPU parity of the burst reduce (k_reduce_burst): the kernel of the bf16
-reduce (fp32 wire) at P = 24, 32, 64 and 96 on shards of 2^23 elements or more, which
+reduce (fp32 wire) at P > 16 on shards of 2^23 elements or more, which
 reduces chunks of 32768 shard elements into LDS and writes each chunk to g in
-one run.  The test build's gsz_test_set_reduce_path sends small shards and the
-other world sizes above 16 to it, so that every world size the 16-byte kernels
-specialise (compile-time P 24, 32, 64, 96; the runtime-P loop at 17, 48, 100,
-256, which the product keeps on the tile kernel), every contribution layout, the bf16 wire,
+one run.  The test build's gsz_test_set_reduce_path sends small shards (and
+the bf16 wire) to it, so that every world size the 16-byte kernels specialise
+(compile-time P 24, 32, 64, 96; the runtime-P loop at 17, 48, 100, 256, whose
+last (P-1) mod 8 contributions go as one group here), every contribution layout, the bf16 wire,
 ragged last chunks and rows, shards below one chunk, capped grids (blocks
 walking several chunks; XCD classes with no block) and the no-allocation entry
 point are compared with the oracle: g bit for bit, the fp64 norm partial within
@@ -203,13 +203,13 @@ def test_burst_noalloc_entry_point():
     check_partial(float(host(part)[0]), ref, "burst, no-allocation entry point")
 
 
-def test_product_rule_at_its_threshold():
-    """Without the forcing hook, P = 24 on a shard of exactly 2^23 elements
-    takes the burst kernel (its norm partial has the burst grid's grouping,
-    bit for bit) and 8 elements fewer take the tile kernel; g equals the
-    oracle either way."""
-    P = 24
-    rng = np.random.default_rng(67)
+@pytest.mark.parametrize("P", [24, 33])
+def test_product_rule_at_its_threshold(P):
+    """Without the forcing hook, a shard of exactly 2^23 elements takes the
+    burst kernel (its norm partial has the burst grid's grouping, bit for bit)
+    and 8 elements fewer take the tile kernel, at an unrolled P and at one on
+    the runtime-P loop; g equals the oracle either way."""
+    rng = np.random.default_rng([67, P])
     G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
     for S in (1 << 23, (1 << 23) - 8):
         plan = G.Plan([S * P], 1 << 40, P, 8).upload()
