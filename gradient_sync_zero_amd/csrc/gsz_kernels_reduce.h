@@ -250,6 +250,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, flo
     // multiples of 8: reduced into res, then written to g in one run.
     auto burst = [&](int64_t base, int64_t n) {
         if (LAY == kLayFlat) cur.seek(base, slut, sshift);                   // uniform: scalar loads
+        double csq = 0.0;          // this chunk's squares, added to sq once: shorter fp64 sums
         // Rows r with r * 512 < n: r <= kBurstRows - 1, so j < kBurstElems (LDS in
         // bounds).  Lanes past n load position 0 of every contribution (in
         // bounds; unconditional loads keep them in flight together) and their
@@ -266,10 +267,11 @@ __global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, flo
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const double d = (double)a[k];
-                    sq = __fma_rn(d, d, sq);                        // d*d is exact in fp64
+                    csq = __fma_rn(d, d, csq);                      // d*d is exact in fp64
                 }
             }
         }
+        sq = sq + csq;
         __syncthreads();
         for (int64_t e = 4 * (int64_t)threadIdx.x; e < n; e += 4 * kBlock)
             stf4_nt(g + base + e, *reinterpret_cast<const f32x4*>(res + e));
