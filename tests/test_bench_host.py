@@ -185,3 +185,33 @@ def test_cpu_baseline_sample_is_the_workloads_own_inputs():
         assert np.array_equal(contribs[q], OI.values_at(w, W.KIND_GRAD, q, w.grad_std, 2, idx))
     for (kind, std, mode), arr in zip(OI.STATE_KINDS, state):
         assert np.array_equal(arr.view(np.uint32), OI.values_at(w, kind, 0, std, mode, idx).view(np.uint32))
+
+
+def test_product_path_never_reaches_the_oracle():
+    """The oracle is test infrastructure: the product package and the input
+    placement import nothing from it, and bench.py only inside its CPU
+    baseline (_oracle_sample and cpu_baseline)."""
+    import ast
+    files = []
+    for d in ("gradient_sync_zero_amd", "synth"):
+        files += [os.path.join(ROOT, d, f) for f in os.listdir(os.path.join(ROOT, d))
+                  if f.endswith(".py")]
+    for path in files:
+        for node in ast.walk(ast.parse(open(path).read())):
+            names = []
+            if isinstance(node, ast.Import):
+                names = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                names = [node.module or ""]
+            assert not any(n == "oracle" or n.startswith("oracle.") for n in names), (path, names)
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    allowed = {"_oracle_sample", "cpu_baseline"}
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef) and fn.name not in allowed:
+            for node in ast.walk(fn):
+                if isinstance(node, ast.ImportFrom) and (node.module or "").startswith("oracle"):
+                    raise AssertionError(f"bench.py: {fn.name} imports {node.module}")
+    for node in tree.body:                       # nothing at module level either
+        if isinstance(node, (ast.Import, ast.ImportFrom)):
+            mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
+            assert not any(m.startswith("oracle") for m in mods), mods
