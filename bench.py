@@ -579,7 +579,7 @@ def bench_ddp(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "variant": "ddp", "world_size_P": P,
-                   "model_params": w.n_params, "step": " + ".join(names)},
+                   "total_params": w.n_params, "step": " + ".join(names)},
         "hbm_GBps": step_gbps, "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "step_ms_gpu": step_gpu, "copy_ceiling_GBps": copy_gbps, "kernels": kern,
         "roofline": roofline}),
@@ -907,7 +907,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "world_size_P": P, "owner": r, "model_params": w.n_params,
+        "config": {"workload": w.name, "world_size_P": P, "owner": r, "total_params": w.n_params,
                    "shard_params": S, "bucket_cap_MiB": w.bucket_cap_bytes // (1 << 20),
                    "buckets": plan.n_buckets,
                    "contribution_layout": {"flat": "bucket-flat", "compact": "shard-compact",
