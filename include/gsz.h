@@ -187,8 +187,10 @@ int gsz_ledger_bytes_per_param(int32_t world_size, int32_t zero_stage, double* o
  * shard_len) or gsz_shard_grad_sqnorm (n = its element count) needs, per call
  * in flight: one fp64 partial per 2048 elements (at most 2^23 of them) plus
  * 1024 for the second stage of the fixed-order sum, i.e. 8 * (min(ceil(n /
- * 2048), 2^23) + 1024) with ceil(0 / 2048) taken as 1.  About 0.4% of the
- * bytes of the fp32 values it reduces.  Needs no initialisation.
+ * 2048), 2^23) + 1024) with ceil(0 / 2048) taken as 1 (an upper bound: the
+ * reduce of a large shard at P > 16 writes one partial per compute unit).
+ * About 0.4% of the bytes of the fp32 values it reduces.  Needs no
+ * initialisation.
  * GSZ_ERR_INVALID_ARG if n < 0 or out is NULL. */
 int gsz_workspace_bytes(int64_t n, size_t* out);
 
