@@ -45,3 +45,20 @@ def test_bench_line_on_the_gpt2_small_share():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
 
+
+
+def test_ddp_bench_line_on_the_gpt2_small_model():
+    """The unsharded step's line (--variant ddp): the same contract, its
+    kernels' times adding up to at most the step."""
+    run = run_bench("--config", "1", "--variant", "ddp", "--steps", "5", "--warmup", "2")
+    assert run.returncode == 0, run.stderr[-2000:]
+    lines = [l for l in run.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, run.stdout
+    d = json.loads(lines[0])
+    assert d["n_gpus"] == 1 and d["steps"] == 5 and d["unit"] == "params/s"
+    assert d["config"]["variant"] == "ddp" and "model" not in d["config"]
+    assert abs(d["value"] - d["config"]["total_params"] / (d["ms_per_step"] * 1e-3)) <= 1e-6 * d["value"]
+    parts = sum(v["ms"] for v in d["kernels"].values())
+    assert parts <= d["ms_per_step"] * 1.05, (parts, d["ms_per_step"])
+    rl = d["roofline"]
+    assert rl["bound"] == "hbm" and abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-12
