@@ -118,10 +118,10 @@ __device__ __forceinline__ void ring_mean8(const RankPtrs& rp, int P, float invP
 // by flat position instead of shard index: P launches, one per chunk owner,
 // give the all-reduce result.  Loads and stores are nontemporal (2% faster at
 // P = 8, 5% at P = 64 than plain ones).  This kernel serves P > 16 on shards
-// below the burst kernel's size (compile-time P for 24, 32, 64 and 96, its
-// runtime-P loop for the others) and the all-reduce; P <= 16 runs
-// k_reduce_mean_lc below.  LAY is one of the layouts above (kLayFlat for
-// OUTFLAT).
+// below the burst kernel's size and on the bf16 wire (compile-time P for 24,
+// 32, 64 and 96, its runtime-P loop for the others) and the all-reduce;
+// P <= 16 runs k_reduce_mean_lc below.  LAY is one of the layouts above
+// (kLayFlat for OUTFLAT).
 template <int PS, bool NORM, int LAY, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, float invP, int pow2,
                                                         const int64_t* __restrict__ seg,
