@@ -11,7 +11,7 @@ from ._binding import (AdamWHP, GszError, INTERLEAVE_PIECE, LAYOUT_BUCKET_FLAT,
                        bucket_accumulate, bucket_accumulate_f32, bucket_pack, bucket_pack_f32,
                        bucket_unpack, clip_coef, load, ledger_bytes_per_param, make_hp,
                        shard_adamw_step, shard_grad_sqnorm, shard_reduce_mean, shard_reduce_mean_noalloc,
-                       set_grid_limit, set_reduce_path, REDUCE_PATH_BURST, REDUCE_PATH_BY_SIZE,
+                       set_burst_window, set_grid_limit, set_reduce_path, REDUCE_PATH_BURST, REDUCE_PATH_BY_SIZE,
                        REDUCE_PATH_TILE, shard_reduce_mean_f32, test_hooks, workspace_bytes)
 from . import _binding
 
@@ -22,7 +22,7 @@ __all__ = ["AdamWHP", "GszError", "INTERLEAVE_PIECE", "LAYOUT_BUCKET_FLAT",
            "MAX_RANKS", "Plan", "adamw_step", "allgather_layout_write", "allreduce_mean",
            "bucket_accumulate", "bucket_accumulate_f32", "bucket_pack", "bucket_pack_f32",
            "bucket_unpack", "clip_coef", "ledger_bytes_per_param", "make_hp", "set_grid_limit",
-           "set_reduce_path", "REDUCE_PATH_BURST", "REDUCE_PATH_BY_SIZE", "REDUCE_PATH_TILE",
+           "set_burst_window", "set_reduce_path", "REDUCE_PATH_BURST", "REDUCE_PATH_BY_SIZE", "REDUCE_PATH_TILE",
            "shard_adamw_step", "shard_grad_sqnorm", "shard_reduce_mean", "shard_reduce_mean_f32",
            "shard_reduce_mean_noalloc",
            "test_hooks", "workspace_bytes"]

@@ -89,7 +89,8 @@ _SIGS = {
 }
 
 _TEST_SIGS = {"gsz_test_set_grid_limit": [ctypes.c_int64],
-              "gsz_test_set_reduce_path": [_I32]}
+              "gsz_test_set_reduce_path": [_I32],
+              "gsz_test_set_burst_window": [ctypes.c_uint32, ctypes.c_uint32]}
 
 _libs = {}
 _active = threading.local()
@@ -129,8 +130,9 @@ def load(path=None):
 @contextlib.contextmanager
 def test_hooks():
     """Within the block, calls made by this thread go to libgsz_test.so, the
-    same sources built with the test hooks (set_grid_limit, set_reduce_path).  Plans keep the
-    library they were created with, so create them inside the block."""
+    same sources built with the test hooks (set_grid_limit, set_reduce_path,
+    set_burst_window).  Plans keep the library they were created with, so
+    create them inside the block."""
     load(TEST_LIB_PATH)
     prev = getattr(_active, "path", LIB_PATH)
     _active.path = TEST_LIB_PATH
@@ -345,6 +347,16 @@ def set_reduce_path(path):
     REDUCE_PATH_BURST or REDUCE_PATH_TILE."""
     lib = _test_lib("set_reduce_path")
     _check(lib.gsz_test_set_reduce_path(int(path)), lib)
+
+
+def set_burst_window(period, window):
+    """Test build only (inside test_hooks()): how the burst reduce writes g in
+    every later launch, process-wide.  period 0 restores the product's choice;
+    else period (100 MHz clock ticks) is a power of two and window 0 means
+    chunk writes, window > 0 per-wave rings written while (clock mod period) <
+    window or when full."""
+    lib = _test_lib("set_burst_window")
+    _check(lib.gsz_test_set_burst_window(int(period), int(window)), lib)
 
 
 def bucket_pack(plan, grads, flat, stream=None):

@@ -189,19 +189,31 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean(RankPtrs rp, int P, floa
 // ------------------------------------------------------ burst reduce-mean --
 
 // The same g as k_reduce_mean, for large shards at P > 16, with g reaching HBM
-// in bursts: one block per CU (its 128 KiB of LDS admit no second one) takes
-// chunks of kBurstElems shard elements, reduces a whole chunk into LDS (wave w
-// takes the chunk's 512-element rows w, w + 4, ...) and then writes it to g as
-// one contiguous run of whole-line stores.  Against the one-tile-per-block
-// launch, whose every wave stores its 2 KiB as soon as it is reduced, this ran
-// 3-5% faster at P = 64 on 64 separate contributions of 1.08e9 elements:
-// stores scattered among the reads cost the read stream far more than their
-// bytes (without its stores the same kernel takes 14-23% less time, and
-// writing half as many g lines costs 82% as much time as writing all of them).
+// in bursts.  Stores of g scattered among the contribution reads cost the
+// read stream far more than their bytes (without its stores the one-tile
+// kernel takes 14-23% less time, and writing half as many g lines costs 82%
+// as much time as writing all of them).  So one block per CU (its 128 KiB of
+// LDS admit no second one) walks chunks of kBurstElems shard elements (wave w
+// takes a chunk's 512-element rows w, w + 4, ...) and keeps the rows it
+// reduces in LDS, to write them in one of two ways (`chunked`, chosen by the
+// host from P and S):
+//  - chunk writes: once a chunk is reduced, the whole block writes its 128 KiB
+//    as one run (3-5% faster than the one-tile-per-block launch at P = 64);
+//  - clock windows: each wave keeps its rows in its own ring of kRingRows rows
+//    and writes what it holds, each row as two whole-line stores per lane,
+//    when the chip-wide 100 MHz constant clock is in a write window (clock &
+//    pmask below `window`) or when the ring is full.  All CUs read the same
+//    clock, so their writes fall in the same windows and the DRAM sees a few
+//    long write runs between long read runs: 1.5-7% faster than chunk writes
+//    on large shards at P = 24-128.  The clock is read as a row starts, so
+//    that its latency hides under the row's loads (read as a row ended and
+//    taken modulo a period that was no power of two, it made the kernel 4%
+//    slower at P = 17).
 // Chunks go to XCDs in contiguous ranges (burst_work); the norm partials, one
 // per block, are summed in block order by the finalize.
 constexpr int kBurstRows = 64;
-constexpr int64_t kBurstElems = (int64_t)kBurstRows * 512;   // 128 KiB of fp32
+constexpr int64_t kBurstElems = (int64_t)kBurstRows * 512;
+constexpr int kRingRows = 16;                                  // per wave: 32 KiB of fp32
 
 // The work of block b in a grid of G blocks over S shard elements.  The blocks
 // with b mod 8 == x run on XCD x; that class takes a contiguous share of the
@@ -240,29 +252,55 @@ __global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, flo
                                                          const uint64_t* __restrict__ slut, int sshift,
                                                          int64_t owner, int64_t S,
                                                          float* __restrict__ g,
-                                                         double* __restrict__ ws) {
-    __shared__ float res[kBurstElems];
+                                                         double* __restrict__ ws,
+                                                         int chunked, uint32_t pmask,
+                                                         uint32_t window) {
+    // Per wave a ring of kRingRows rows; with chunk writes the same 128 KiB
+    // hold one chunk, row r at r * 512.
+    __shared__ float lds[kBurstElems];
+    __shared__ int64_t row_all[kBlock / 64][kRingRows];
+    static_assert(kBlock / 64 * kRingRows * 512 == kBurstElems, "rings fill the chunk buffer");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float* const chunk = lds;
+    float* const ring = lds + wave * kRingRows * 512;
+    int64_t* const row_at = row_all[wave];  // shard index of each held row's first element
     const BurstWork w = burst_work(S, gridDim.x, blockIdx.x);
     double sq = 0.0;
     SegCursor cur{seg, owner, 0, 0, 0};
+    int head = 0, held = 0;                // wave-uniform: slots [head - held, head) are held
+    // Writes the held rows: lane l stores elements 4l..4l+3 and 256+4l.. of
+    // each (whole lines per instruction), those below S.
+    auto flush = [&]() {
+        for (int k = 0; k < held; ++k) {
+            const int slot = (head - held + k + kRingRows) % kRingRows;
+            const float* src = ring + slot * 512;
+            const int64_t e0 = row_at[slot] + 4 * lane, e1 = e0 + 256;
+            if (e0 < S) stf4_nt(g + e0, *reinterpret_cast<const f32x4*>(src + 4 * lane));
+            if (e1 < S) stf4_nt(g + e1, *reinterpret_cast<const f32x4*>(src + 256 + 4 * lane));
+        }
+        held = 0;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();   // a slot is reused only after every lane read it
+    };
     // Elements [base, base + n) of the shard, 0 < n <= kBurstElems, n and base
-    // multiples of 8: reduced into res, then written to g in one run.
-    auto burst = [&](int64_t base, int64_t n) {
+    // multiples of 8.
+    auto piece = [&](int64_t base, int64_t n) {
         if (LAY == kLayFlat) cur.seek(base, slut, sshift);                   // uniform: scalar loads
-        double csq = 0.0;          // this chunk's squares, added to sq once: shorter fp64 sums
-        // Rows r with r * 512 < n: r <= kBurstRows - 1, so j < kBurstElems (LDS in
-        // bounds).  Lanes past n load position 0 of every contribution (in
-        // bounds; unconditional loads keep them in flight together) and their
-        // results are never stored to g.
+        double csq = 0.0;          // this piece's squares, added to sq once: shorter fp64 sums
+        // Lanes past n load position 0 of every contribution (in bounds;
+        // unconditional loads keep them in flight together) and their results
+        // are never stored to g.
         for (int r = wave; (int64_t)r * 512 < n; r += kBlock / 64) {
+            // Read before the row's loads, so that the clock's latency hides under theirs.
+            const uint32_t t = chunked ? 0u : (uint32_t)__builtin_amdgcn_s_memrealtime() & pmask;
             const int j = r * 512 + 8 * lane;
             const bool ok = j < n;
             const int64_t off = ok ? contrib_index<LAY>(cur, base + j, PS > 0 ? PS : P) : 0;
             float a[8];
             ring_mean8<PS, W16, 32>(rp, P, invP, pow2, off, a);
-            *reinterpret_cast<f32x4*>(res + j) = f32x4{a[0], a[1], a[2], a[3]};
-            *reinterpret_cast<f32x4*>(res + j + 4) = f32x4{a[4], a[5], a[6], a[7]};
+            float* st = chunked ? chunk + r * 512 : ring + head * 512;
+            *reinterpret_cast<f32x4*>(st + 8 * lane) = f32x4{a[0], a[1], a[2], a[3]};
+            *reinterpret_cast<f32x4*>(st + 8 * lane + 4) = f32x4{a[4], a[5], a[6], a[7]};
             if (NORM && ok) {
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
@@ -270,18 +308,28 @@ __global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, flo
                     csq = __fma_rn(d, d, csq);                      // d*d is exact in fp64
                 }
             }
+            if (chunked) continue;
+            if (lane == 0) row_at[head] = base + r * 512;
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();   // the row is in LDS before any lane reads it
+            head = (head + 1) % kRingRows;
+            ++held;
+            if (held == kRingRows || t < window) flush();
         }
         sq = sq + csq;
-        __syncthreads();
-        for (int64_t e = 4 * (int64_t)threadIdx.x; e < n; e += 4 * kBlock)
-            stf4_nt(g + base + e, *reinterpret_cast<const f32x4*>(res + e));
-        __syncthreads();                                 // the next chunk overwrites res
+        if (chunked) {                     // the whole block writes the piece's n elements
+            __syncthreads();
+            for (int e = 4 * threadIdx.x; e < n; e += 4 * kBlock)
+                stf4_nt(g + base + e, *reinterpret_cast<const f32x4*>(chunk + e));
+            __syncthreads();
+        }
     };
     for (int64_t i = 0; i < w.rounds; ++i) {
         const int64_t base = (w.first + i * w.step) * kBurstElems;
-        burst(base, S - base < kBurstElems ? S - base : kBurstElems);
+        piece(base, S - base < kBurstElems ? S - base : kBurstElems);
     }
-    if (w.tail1 > w.tail0) burst(w.tail0, w.tail1 - w.tail0);
+    if (w.tail1 > w.tail0) piece(w.tail0, w.tail1 - w.tail0);
+    flush();
     if (NORM) {
         const double s = block_sum(sq);
         if (threadIdx.x == 0) ws[blockIdx.x] = s;

@@ -63,6 +63,11 @@ std::atomic<int64_t> g_grid_limit{0};
 // Which kernel the bf16 reduce at P > 16 uses: 0 the product's rule (use_burst),
 // 1 always the burst kernel, 2 never (so that small test shards reach both).
 std::atomic<int> g_reduce_path{0};
+// The burst kernel's write window (period, window) in clock ticks; period 0:
+// the product's choice (burst_write), else these, so that tests can reach
+// every write policy: chunk writes (window 0), windows, every row at once
+// (window >= period).
+std::atomic<uint32_t> g_win_period{0}, g_win_window{0};
 #endif
 
 // Blocks of a one-tile-per-block launch over n_tiles tiles: at most `builtin`
@@ -239,6 +244,39 @@ bool use_burst(int P, int64_t S, bool wire16) {
     return !wire16 && P > kLcMaxP && S >= kBurstMinElems;
 }
 
+// How the burst kernel writes g: with `chunked`, each chunk (or tail piece)
+// by the whole block once it is reduced; else each wave writes the rows it
+// holds when (100 MHz constant clock & (period - 1)) < window, or when its
+// ring of kRingRows rows is full.  A wave fills its ring in about 250 * P
+// ticks when the chip reads at 6.5 TB/s (16 rows of P KiB each at a CU's
+// 25 GB/s shared by 4 waves), so a period of the largest power of two up to
+// 256 * P has each ring written in a window before it fills, in 15% of the
+// period.
+//
+// Measured against chunk writes on shard-compact contributions (P x S): the
+// windows are 1.5-7% faster at P = 24-128 on 2^28 elements and 3% faster on
+// the 70B share (P = 64, 1.08e9); at P = 32 and 64 also 2-6% faster on 2^26
+// and 2^27.  Below 2^26 they are up to 6% slower, and 1-2.5% slower at
+// P = 17-20 (equal at 2^28) and at P = 200-256, where writes are under 1% of
+// the bytes: there the per-wave rings, which give up the block's lockstep
+// over a chunk's rows, cost more than the windows save.
+constexpr int kWinMinP = 24, kWinMaxP = 128;
+constexpr int64_t kWinMinElems = (int64_t)1 << 27;
+struct BurstWrite { int chunked; uint32_t period, window; };
+BurstWrite burst_write(int P, int64_t S) {
+#ifdef GSZ_TEST_HOOKS
+    const uint32_t tp = g_win_period.load(std::memory_order_relaxed);
+    if (tp > 0) {
+        const uint32_t tw = g_win_window.load(std::memory_order_relaxed);
+        return {tw == 0, tp, tw};
+    }
+#endif
+    uint32_t period = 1;
+    while (period * 2 <= 256u * (uint32_t)P) period *= 2;
+    const bool windows = P >= kWinMinP && P <= kWinMaxP && S >= kWinMinElems;
+    return {!windows, period, period * 3 / 20};
+}
+
 int burst_grid(int dev, int64_t S) {
     const int64_t chunks = (S + kBurstElems - 1) / kBurstElems;
     int64_t g = g_dev_cus[dev].load();
@@ -255,11 +293,12 @@ void launch_reduce_burst(bool norm, int lay, bool wire16, dim3 grid, hipStream_t
                          const RankPtrs& rp, int P, float invP, int pow2, const int64_t* seg,
                          const uint64_t* slut, int sshift, int64_t owner, int64_t S, float* g,
                          double* ws) {
+    const BurstWrite wr = burst_write(P, S);
     auto go = [&](auto nm, auto ly, auto w16) {
         hipLaunchKernelGGL((k_reduce_burst<PS, decltype(nm)::value, decltype(ly)::value,
                                            decltype(w16)::value>),
                            grid, dim3(kBlock), 0, st, rp, P, invP, pow2, seg, slut, sshift, owner,
-                           S, g, ws);
+                           S, g, ws, wr.chunked, wr.period - 1, wr.window);
     };
     auto layouts = [&](auto w16) {
         with_layout(lay, [&](auto ly) {
@@ -329,6 +368,16 @@ extern "C" int gsz_test_set_reduce_path(int32_t path) {
         return GSZ_ERR_INVALID_ARG;
     }
     g_reduce_path.store(path, std::memory_order_relaxed);
+    return GSZ_OK;
+}
+
+extern "C" int gsz_test_set_burst_window(uint32_t period, uint32_t window) {
+    if (period & (period - 1)) {
+        set_error("gsz_test_set_burst_window: period %u is not 0 or a power of two", period);
+        return GSZ_ERR_INVALID_ARG;
+    }
+    g_win_period.store(period, std::memory_order_relaxed);
+    g_win_window.store(window, std::memory_order_relaxed);
     return GSZ_OK;
 }
 #endif

@@ -39,6 +39,16 @@ int gsz_test_set_grid_limit(int64_t max_blocks);
  * GSZ_ERR_INVALID_ARG if path is not 0, 1 or 2. */
 int gsz_test_set_reduce_path(int32_t path);
 
+/* Sets how the burst kernel writes g, for every launch made after the call,
+ * for the whole process.  period 0 restores the product's choice.  Else
+ * period must be a power of two: with window 0 each chunk is written by its
+ * block once reduced; with window > 0 each wave writes the g rows it holds
+ * when (constant clock, 100 MHz) mod period < window, or when its ring of 16
+ * rows is full (window >= period: every row as soon as it is reduced).  Only
+ * when g is written changes: g and the norm partials are bit-identical for
+ * every setting.  GSZ_ERR_INVALID_ARG if period is not 0 or a power of two. */
+int gsz_test_set_burst_window(uint32_t period, uint32_t window);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,7 +42,8 @@ def test_test_hooks_live_only_in_the_test_build():
     have it; the test build exports everything the product does plus the
     hooks of gsz_test.h."""
     hooks = declared_symbols(TEST_HEADER)
-    assert hooks == ["gsz_test_set_grid_limit", "gsz_test_set_reduce_path"]
+    assert hooks == ["gsz_test_set_burst_window", "gsz_test_set_grid_limit",
+                     "gsz_test_set_reduce_path"]
     prod = ctypes.CDLL(G.LIB_PATH)
     test = ctypes.CDLL(G._binding.TEST_LIB_PATH)
     assert not any(hasattr(prod, h) for h in hooks)
@@ -51,6 +52,8 @@ def test_test_hooks_live_only_in_the_test_build():
         G.set_grid_limit(4)                      # outside test_hooks(): refused
     with pytest.raises(RuntimeError):
         G.set_reduce_path(G.REDUCE_PATH_BURST)
+    with pytest.raises(RuntimeError):
+        G.set_burst_window(64, 8)
     with G.test_hooks():
         with pytest.raises(G.GszError) as e:     # the cap is a count of blocks
             G.set_grid_limit(-1)
@@ -61,6 +64,13 @@ def test_test_hooks_live_only_in_the_test_build():
                 G.set_reduce_path(bad)
             assert str(bad) in str(e.value)
         G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
+        for bad in (3, 100, (1 << 31) + 1):      # the period is a power of two (or 0)
+            with pytest.raises(G.GszError) as e:
+                G.set_burst_window(bad, 1)
+            assert str(bad) in str(e.value)
+        for good in ((0, 0), (1, 1), (64, 24), (1 << 31, 0)):
+            G.set_burst_window(*good)
+        G.set_burst_window(0, 0)
         p = G.Plan([5], 100, 2)
     with pytest.raises(ValueError):              # a plan is tied to its build
         G._binding._lib_for(p)

@@ -1,8 +1,12 @@
 """GPU parity of the burst reduce (k_reduce_burst): the kernel of the bf16
 reduce (fp32 wire) at P > 16 on shards of 2^23 elements or more, which
-reduces chunks of 32768 shard elements into LDS and writes each chunk to g in
-one run.  The test build's gsz_test_set_reduce_path sends small shards (and
-the bf16 wire) to it, so that every world size the 16-byte kernels specialise
+reduces chunks of 32768 shard elements into LDS and writes g either a chunk at
+a time or, on large shards, from per-wave rings inside clock windows common to
+the chip.  Every reduce here runs under five write policies (the product's
+choice, chunk writes, full rings only, short jittery windows that leave rings
+partly held and wrapping, every row at once), which must give the same g and
+norm partial bit for bit.  The test build's gsz_test_set_reduce_path sends
+small shards (and the bf16 wire) to it, so that every world size the 16-byte kernels specialise
 (compile-time P 24, 32, 64, 96; the runtime-P loop at 17, 48, 100, 256, whose
 last (P-1) mod 8 contributions go as one group here), every contribution layout, the bf16 wire,
 ragged last chunks and rows, shards below one chunk, capped grids (blocks
@@ -40,6 +44,7 @@ def _burst_path():
         finally:
             G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
             G.set_grid_limit(0)
+            G.set_burst_window(0, 0)
 
 
 def say(*a):
@@ -69,13 +74,35 @@ def interleave(contribs, P, S):
     return buf.reshape(-1)
 
 
-def reduce(plan, r, src, layout, S, wire=False):
+# (period, window) of gsz_test_set_burst_window: the product's choice, chunk
+# writes, full rings only, windows of 0.24 us every 0.64 us, every row at once.
+WRITES = [(0, 0), (1 << 14, 0), (1 << 20, 1), (64, 24), (1, 1)]
+
+
+def reduce_once(plan, r, src, layout, S, wire=False):
     g = torch.full((S,), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.zeros(G.workspace_bytes(S) // 8, dtype=torch.float64, device="cuda")
     part = torch.zeros(1, dtype=torch.float64, device="cuda")
     G.shard_reduce_mean(plan, r, src, layout, g, part, ws, bf16_wire=wire)
     torch.cuda.synchronize()
     return host(g), float(host(part)[0])
+
+
+def reduce(plan, r, src, layout, S, wire=False):
+    """The reduce under every write policy: the same g and partial bit for bit."""
+    out = None
+    try:
+        for pw in WRITES:
+            G.set_burst_window(*pw)
+            g, part = reduce_once(plan, r, src, layout, S, wire)
+            if out is None:
+                out = (g, part)
+            else:
+                assert_bits(g, out[0], f"g under write policy {pw}")
+                assert part == out[1], ("norm partial under write policy", pw, part, out[1])
+    finally:
+        G.set_burst_window(0, 0)
+    return out
 
 
 def check_partial(got, ref, what):
@@ -195,12 +222,18 @@ def test_burst_noalloc_entry_point():
     cs = [wide_bf16(rng, S) for _ in range(P)]
     r = 63
     ref = reduce_mean(cs, r)
-    g = torch.full((S,), float("nan"), dtype=torch.float32, device="cuda")
-    part = torch.zeros(1, dtype=torch.float64, device="cuda")
-    G.shard_reduce_mean_noalloc(plan, r, [dev(c) for c in cs], G.LAYOUT_SHARD_COMPACT, g, part)
-    torch.cuda.synchronize()
-    assert_bits(host(g), ref, "burst, no-allocation entry point")
-    check_partial(float(host(part)[0]), ref, "burst, no-allocation entry point")
+    src = [dev(c) for c in cs]
+    try:
+        for pw in WRITES:
+            G.set_burst_window(*pw)
+            g = torch.full((S,), float("nan"), dtype=torch.float32, device="cuda")
+            part = torch.zeros(1, dtype=torch.float64, device="cuda")
+            G.shard_reduce_mean_noalloc(plan, r, src, G.LAYOUT_SHARD_COMPACT, g, part)
+            torch.cuda.synchronize()
+            assert_bits(host(g), ref, f"burst, no-allocation entry point, writes {pw}")
+            check_partial(float(host(part)[0]), ref, f"burst, no-allocation entry point, writes {pw}")
+    finally:
+        G.set_burst_window(0, 0)
 
 
 @pytest.mark.parametrize("P", [24, 33])
