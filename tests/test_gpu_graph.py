@@ -141,16 +141,19 @@ def test_graph_replays_equal_eager_ddp_steps(cfg):
         del junk
 
 
-def test_graph_replays_equal_eager_burst_steps():
+@pytest.mark.parametrize("writes", [(0, 0), (64, 24)], ids=["chunk-writes", "clock-windows"])
+def test_graph_replays_equal_eager_burst_steps(writes):
     """The P=64 step with the burst reduce (forced on a shard of about three
-    chunks through the test build), shard-compact contributions, the bf16
-    parameters in shard layout, and the no-allocation reduce beside it,
-    captured once and replayed."""
+    chunks through the test build, writing g a chunk at a time or in short
+    clock windows), shard-compact contributions, the bf16 parameters in shard
+    layout, and the no-allocation reduce beside it, captured once and
+    replayed."""
     import numpy as np
     P, r = 64, 9
     rng = np.random.default_rng(91)
     with G.test_hooks():
         G.set_reduce_path(G.REDUCE_PATH_BURST)
+        G.set_burst_window(*writes)
         try:
             plan = G.Plan([int(2.6 * 32768) * P], 1 << 40, P, 8).upload()
             S = plan.shard_len
@@ -205,3 +208,4 @@ def test_graph_replays_equal_eager_burst_steps():
                 del junk
         finally:
             G.set_reduce_path(G.REDUCE_PATH_BY_SIZE)
+            G.set_burst_window(0, 0)
