@@ -9,9 +9,9 @@ from ._binding import (AdamWHP, GszError, INTERLEAVE_PIECE, LAYOUT_BUCKET_FLAT,
                        LAYOUT_RANK_INTERLEAVED, LAYOUT_SHARD_COMPACT, LIB_PATH, interleaved_len,
                        MAX_RANKS, Plan, adamw_step, allgather_layout_write, allreduce_mean,
                        bucket_accumulate, bucket_accumulate_f32, bucket_pack, bucket_pack_f32,
-                       bucket_unpack, clip_coef, load, ledger_bytes_per_param, make_hp,
+                       bucket_unpack, clip_coef, load, ledger_bytes_per_param, make_hp, max_tile_span,
                        shard_adamw_step, shard_grad_sqnorm, shard_reduce_mean, shard_reduce_mean_noalloc,
-                       set_burst_window, set_grid_limit, set_reduce_path, REDUCE_PATH_BURST, REDUCE_PATH_BY_SIZE,
+                       set_burst_window, set_flat_wide, set_grid_limit, set_reduce_path, REDUCE_PATH_BURST, REDUCE_PATH_BY_SIZE,
                        REDUCE_PATH_TILE, shard_reduce_mean_f32, test_hooks, workspace_bytes)
 from . import _binding
 
@@ -21,8 +21,9 @@ __all__ = ["AdamWHP", "GszError", "INTERLEAVE_PIECE", "LAYOUT_BUCKET_FLAT",
            "LAYOUT_RANK_INTERLEAVED", "LAYOUT_SHARD_COMPACT", "LIB_PATH", "interleaved_len",
            "MAX_RANKS", "Plan", "adamw_step", "allgather_layout_write", "allreduce_mean",
            "bucket_accumulate", "bucket_accumulate_f32", "bucket_pack", "bucket_pack_f32",
-           "bucket_unpack", "clip_coef", "ledger_bytes_per_param", "make_hp", "set_grid_limit",
-           "set_burst_window", "set_reduce_path", "REDUCE_PATH_BURST", "REDUCE_PATH_BY_SIZE", "REDUCE_PATH_TILE",
+           "bucket_unpack", "clip_coef", "ledger_bytes_per_param", "make_hp", "max_tile_span",
+           "set_grid_limit",
+           "set_burst_window", "set_flat_wide", "set_reduce_path", "REDUCE_PATH_BURST", "REDUCE_PATH_BY_SIZE", "REDUCE_PATH_TILE",
            "shard_adamw_step", "shard_grad_sqnorm", "shard_reduce_mean", "shard_reduce_mean_f32",
            "shard_reduce_mean_noalloc",
            "test_hooks", "workspace_bytes"]

@@ -90,7 +90,9 @@ _SIGS = {
 
 _TEST_SIGS = {"gsz_test_set_grid_limit": [ctypes.c_int64],
               "gsz_test_set_reduce_path": [_I32],
-              "gsz_test_set_burst_window": [ctypes.c_uint32, ctypes.c_uint32]}
+              "gsz_test_set_burst_window": [ctypes.c_uint32, ctypes.c_uint32],
+              "gsz_test_set_flat_wide": [_I32],
+              "gsz_test_max_tile_span": [_P, _I32, _I64, ctypes.POINTER(ctypes.c_int64)]}
 
 _libs = {}
 _active = threading.local()
@@ -131,7 +133,7 @@ def load(path=None):
 def test_hooks():
     """Within the block, calls made by this thread go to libgsz_test.so, the
     same sources built with the test hooks (set_grid_limit, set_reduce_path,
-    set_burst_window).  Plans keep the library they were created with, so
+    set_burst_window, set_flat_wide).  Plans keep the library they were created with, so
     create them inside the block."""
     load(TEST_LIB_PATH)
     prev = getattr(_active, "path", LIB_PATH)
@@ -357,6 +359,25 @@ def set_burst_window(period, window):
     window or when full."""
     lib = _test_lib("set_burst_window")
     _check(lib.gsz_test_set_burst_window(int(period), int(window)), lib)
+
+
+def set_flat_wide(on):
+    """Test build only (inside test_hooks()): while on, every later
+    bucket-flat reduce on the lane-contiguous kernel (bf16 at P <= 16, fp32 at
+    any P) reads its contributions through 64-bit addresses, the path of plans
+    whose buckets exceed 2^29 elements; process-wide."""
+    lib = _test_lib("set_flat_wide")
+    _check(lib.gsz_test_set_flat_wide(1 if on else 0), lib)
+
+
+def max_tile_span(plan, owner, tile):
+    """Test build only (inside test_hooks(), host only): the largest span of
+    positions in the bucket-flat layout that `tile` consecutive shard
+    elements of `owner` take."""
+    lib = _test_lib("max_tile_span")
+    out = ctypes.c_int64(0)
+    _check(lib.gsz_test_max_tile_span(plan.handle, int(owner), int(tile), ctypes.byref(out)), lib)
+    return out.value
 
 
 def bucket_pack(plan, grads, flat, stream=None):

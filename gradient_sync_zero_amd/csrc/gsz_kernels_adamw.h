@@ -28,7 +28,12 @@ __device__ __forceinline__ void adamw1(float& th, float& mm, float& vv, float gg
 // instruction covers 1 KiB of whole 128-byte lines (a lane that loads 32
 // contiguous bytes as two 16-byte halves makes each instruction touch half of
 // every line, and half-line misses to the same line are fetched twice).  Every
-// access is nontemporal.  The bf16 result goes out as 8 bytes per lane.
+// access goes through a buffer descriptor based at the tile: loads
+// nontemporal, stores nontemporal with sc1.  The bf16 result goes out as 8
+// bytes per lane, in shard layout and/or at its all-gather position (glen
+// elements in `gathered`); gwide: a tile's all-gather positions may span
+// 2^31 bytes or more (a bucket of over 2^30 elements), so those stores take
+// 64-bit addresses.
 template <bool GATH, bool SHARD>
 __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master, float* __restrict__ m,
                                                       float* __restrict__ v, const float* __restrict__ g,
@@ -36,7 +41,8 @@ __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master
                                                       const int64_t* __restrict__ seg,
                                                       const uint64_t* __restrict__ slut, int sshift,
                                                       int64_t owner, int64_t S,
-                                                      uint16_t* __restrict__ gathered,
+                                                      uint16_t* __restrict__ gathered, int64_t glen,
+                                                      int gwide,
                                                       uint16_t* __restrict__ shard_bf16) {
     static_assert(kAdamBlock == 64 && kAdamTile == 4 * kAdamBlock, "one wave, 4 elements per lane");
     const int lane = threadIdx.x;
@@ -46,23 +52,33 @@ __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master
     SegCursor cur{seg, owner, 0, 0, 0};
     if (GATH && t < ntile) cur.seek(t * kAdamTile, slut, sshift);   // block-uniform: scalar loads
     for (; t < ntile; t += gridDim.x) {
-        const int64_t i = t * kAdamTile + 4 * lane;
+        const int64_t base = t * kAdamTile;
+        const int64_t i = base + 4 * lane;
+        const int64_t fb = GATH ? uniform64(cur.map(base)) : 0;    // the tile's first all-gather position
         if (i < S) {                           // S and i are multiples of 4
-            const f32x4 g4 = ldf4_nt(g + i);
-            const f32x4 t4 = ldf4_nt(master + i), m4 = ldf4_nt(m + i), v4 = ldf4_nt(v + i);
+            const int64_t rem = (S - base) * 4;
+            const BufRes rg = buf_res(g + base, rem), rt = buf_res(master + base, rem);
+            const BufRes rm = buf_res(m + base, rem), rv = buf_res(v + base, rem);
+            const int o = 16 * lane;
+            const f32x4 g4 = bldf4_nt(rg, o);
+            const f32x4 t4 = bldf4_nt(rt, o), m4 = bldf4_nt(rm, o), v4 = bldf4_nt(rv, o);
             float th[4] = {t4.x, t4.y, t4.z, t4.w};
             float mm[4] = {m4.x, m4.y, m4.z, m4.w};
             float vv[4] = {v4.x, v4.y, v4.z, v4.w};
             const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) adamw1(th[j], mm[j], vv[j], gg[j], coef, s);
-            stf4_nt(master + i, f32x4{th[0], th[1], th[2], th[3]});
-            stf4_nt(m + i, f32x4{mm[0], mm[1], mm[2], mm[3]});
-            stf4_nt(v + i, f32x4{vv[0], vv[1], vv[2], vv[3]});
+            bstf4<kCpNtSc1>(rt, o, f32x4{th[0], th[1], th[2], th[3]});
+            bstf4<kCpNtSc1>(rm, o, f32x4{mm[0], mm[1], mm[2], mm[3]});
+            bstf4<kCpNtSc1>(rv, o, f32x4{vv[0], vv[1], vv[2], vv[3]});
             const u32x2 p = u32x2{bf16_rne(th[0]) | (bf16_rne(th[1]) << 16),
                                   bf16_rne(th[2]) | (bf16_rne(th[3]) << 16)};
-            if (GATH) st8_nt(gathered + cur.map(i), p);
-            if (SHARD) st8_nt(shard_bf16 + i, p);
+            if (GATH) {
+                const int64_t fi = cur.map(i);
+                if (gwide) st8_nt(gathered + fi, p);
+                else bst8<kCpNtSc1>(buf_res(gathered + fb, (glen - fb) * 2), (int)(fi - fb) * 2, p);
+            }
+            if (SHARD) bst8<kCpNtSc1>(buf_res(shard_bf16 + base, (S - base) * 2), 8 * lane, p);
         }
     }
 }

@@ -24,7 +24,10 @@ constexpr int load_group(int ps, int cap) {
 // every contribution), or rank-interleaved (one receive buffer in which rank
 // q's values for shard elements [512t, 512t + 512) sit at (t*P + q)*512; the
 // host passes p[k] = buffer + q_k * 512, so index i reads p[k] + ilv_index(i)).
-constexpr int kLayFlat = 0, kLayCompact = 1, kLayInterleaved = 2;
+// kLayFlatWide is bucket-flat for a plan whose tiles span 2^31 bytes or more
+// of a contribution (see k_reduce_mean_lc); kernels other than the
+// lane-contiguous one treat it as kLayFlat.
+constexpr int kLayFlat = 0, kLayCompact = 1, kLayInterleaved = 2, kLayFlatWide = 3;
 constexpr int64_t kIlvPiece = 512;
 static_assert(kIlvPiece == GSZ_INTERLEAVE_PIECE, "the header's piece size");
 
@@ -34,7 +37,7 @@ __device__ __forceinline__ int64_t ilv_index(int64_t i, int P) {
 
 template <int LAY>
 __device__ __forceinline__ int64_t contrib_index(SegCursor& cur, int64_t i, int P) {
-    if constexpr (LAY == kLayFlat) return cur.map(i);
+    if constexpr (LAY == kLayFlat || LAY == kLayFlatWide) return cur.map(i);
     else if constexpr (LAY == kLayInterleaved) return ilv_index(i, P);
     else return i;
 }
@@ -347,14 +350,23 @@ __global__ __launch_bounds__(kBlock) void k_reduce_burst(RankPtrs rp, int P, flo
 // its twice as many (half-size) bf16 loads make it 6-7% slower, so the larger
 // P keep k_reduce_mean.  OUTFLAT and W16 as there; blocks, XCD order and norm
 // partials as there; LAY as there.
+//
+// Contributions are read through buffer descriptors based at the tile's first
+// position in each contribution (clen elements per contribution buffer), and g
+// is written through one based at the tile's first g element (sc1 stores).  A
+// lane's offsets are relative to the tile, so they stay below 2^31 bytes for
+// every layout except a bucket-flat plan whose tiles span more (a bucket of
+// over 2^29 elements next to a chunk boundary): the host passes kLayFlatWide
+// for that, and the kernel reads through 64-bit addresses instead.
 template <typename T, int PS, bool NORM, int LAY, bool OUTFLAT = false, bool W16 = false>
 __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int P, float invP, int pow2,
                                                            const int64_t* __restrict__ seg,
                                                            const uint64_t* __restrict__ slut, int sshift,
-                                                           int64_t owner, int64_t S,
+                                                           int64_t owner, int64_t S, int64_t clen,
                                                            float* __restrict__ g,
                                                            double* __restrict__ ws) {
-    constexpr bool FLAT = LAY == kLayFlat;
+    constexpr bool FLAT = LAY == kLayFlat || LAY == kLayFlatWide;
+    constexpr bool BUF = LAY != kLayFlatWide;
     static_assert(!OUTFLAT || FLAT, "the all-gather-position output reads bucket-flat input");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t bx = xcd_remap(blockIdx.x, gridDim.x);
@@ -367,11 +379,20 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int 
     for (; t < S; t += (int64_t)gridDim.x * kRedTile) {
         const int64_t i0 = t + 512 * wave + 4 * lane, i1 = i0 + 256;
         const bool ok0 = i0 < S, ok1 = i1 < S;               // S and i are multiples of 4
-        // Past the end a lane reads position 0 of each contribution (in bounds) and
-        // discards the result: loads under a condition became one branch and one
-        // full wait per load, serialising them.
-        const int64_t off0 = ok0 ? contrib_index<LAY>(cur, i0, PS > 0 ? PS : P) : 0;
-        const int64_t off1 = ok1 ? contrib_index<LAY>(cur, i1, PS > 0 ? PS : P) : 0;
+        // Past the end a lane reads the tile's first position of each
+        // contribution (in bounds) and discards the result: loads under a
+        // condition became one branch and one full wait per load, serialising them.
+        // tb: the contribution index of the tile's first element (the same in
+        // every lane; the cursor only moves forward, so mapping t first is fine).
+        const int64_t tb = uniform64(contrib_index<LAY>(cur, t, PS > 0 ? PS : P));
+        const int64_t off0 = ok0 ? contrib_index<LAY>(cur, i0, PS > 0 ? PS : P) : tb;
+        const int64_t off1 = ok1 ? contrib_index<LAY>(cur, i1, PS > 0 ? PS : P) : tb;
+        const int r0 = (int)(off0 - tb) * (int)sizeof(T), r1 = (int)(off1 - tb) * (int)sizeof(T);
+        const int64_t rbytes = (clen - tb) * (int64_t)sizeof(T);
+        auto ld = [&](int k, bool second) -> f32x4 {
+            if constexpr (BUF) return bld4f(buf_res(rp.p[k] + tb, rbytes), second ? r1 : r0, rp.p[k]);
+            else return ld4f_nt(rp.p[k] + (second ? off1 : off0));
+        };
         f32x4 a = zero, b = zero;
         if constexpr (PS > 0) {
             constexpr int G = load_group(PS, 16);
@@ -381,8 +402,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int 
                 f32x4 w0[G], w1[G];
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
-                    w0[j] = ld4f_nt(rp.p[k0 + j] + off0);
-                    w1[j] = ld4f_nt(rp.p[k0 + j] + off1);
+                    w0[j] = ld(k0 + j, false);
+                    w1[j] = ld(k0 + j, true);
                 }
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
@@ -393,15 +414,15 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int 
                 }
             }
         } else {
-            a = ld4f_nt(rp.p[0] + off0);
-            b = ld4f_nt(rp.p[0] + off1);
+            a = ld(0, false);
+            b = ld(0, true);
             int k = 1;
             for (; k + 8 <= P; k += 8) {                      // 16 loads in flight, then the adds
                 f32x4 w0[8], w1[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    w0[j] = ld4f_nt(rp.p[k + j] + off0);
-                    w1[j] = ld4f_nt(rp.p[k + j] + off1);
+                    w0[j] = ld(k + j, false);
+                    w1[j] = ld(k + j, true);
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -411,8 +432,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int 
                 }
             }
             for (; k < P; ++k) {
-                a = add4(a, ld4f_nt(rp.p[k] + off0));
-                b = add4(b, ld4f_nt(rp.p[k] + off1));
+                a = add4(a, ld(k, false));
+                b = add4(b, ld(k, true));
                 if (W16) { a = round4_bf16(a); b = round4_bf16(b); }
             }
         }
@@ -423,8 +444,18 @@ __global__ __launch_bounds__(kBlock) void k_reduce_mean_lc(RankPtrsT<T> rp, int 
             a = f32x4{a.x / fP, a.y / fP, a.z / fP, a.w / fP};
             b = f32x4{b.x / fP, b.y / fP, b.z / fP, b.w / fP};
         }
-        if (ok0) stf4_nt(g + (OUTFLAT ? off0 : i0), a);      // all-reduce output: the flat position
-        if (ok1) stf4_nt(g + (OUTFLAT ? off1 : i1), b);
+        if constexpr (OUTFLAT && BUF) {                      // all-reduce output: the flat position
+            const BufRes rg = buf_res(g + tb, (clen - tb) * 4);
+            if (ok0) bstf4<kCpSc1>(rg, (int)(off0 - tb) * 4, a);
+            if (ok1) bstf4<kCpSc1>(rg, (int)(off1 - tb) * 4, b);
+        } else if constexpr (OUTFLAT) {
+            if (ok0) stf4_nt(g + off0, a);
+            if (ok1) stf4_nt(g + off1, b);
+        } else {
+            const BufRes rg = buf_res(g + t, (S - t) * 4);
+            if (ok0) bstf4<kCpSc1>(rg, (int)(i0 - t) * 4, a);
+            if (ok1) bstf4<kCpSc1>(rg, (int)(i1 - t) * 4, b);
+        }
         if (NORM) {
             a = ok0 ? a : zero;
             b = ok1 ? b : zero;

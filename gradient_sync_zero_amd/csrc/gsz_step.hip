@@ -68,6 +68,10 @@ std::atomic<int> g_reduce_path{0};
 // every write policy: chunk writes (window 0), windows, every row at once
 // (window >= period).
 std::atomic<uint32_t> g_win_period{0}, g_win_window{0};
+// Nonzero: bucket-flat reduces take the 64-bit-address path of the
+// lane-contiguous kernel (kLayFlatWide), which otherwise only plans with
+// buckets of over 2^29 elements reach.
+std::atomic<int> g_force_flat_wide{0};
 #endif
 
 // Blocks of a one-tile-per-block launch over n_tiles tiles: at most `builtin`
@@ -310,36 +314,85 @@ void launch_reduce_burst(bool norm, int lay, bool wire16, dim3 grid, hipStream_t
     else layouts(std::false_type{});
 }
 
+// The largest flat span (last position - first position + 1) of a tile of T
+// consecutive shard elements of owner r, over the shard's tiles.  Positions
+// rise with the shard index, so only tiles that cross a bucket boundary span
+// more than T.
+int64_t max_tile_span(const gsz_plan* p, int64_t owner, int64_t T) {
+    const std::vector<int64_t>& seg = p->seg;     // {shard_off, base, chunk} per bucket, then {S, 0, 0}
+    const int64_t S = p->shard_len;
+    const size_t B = seg.size() / 3 - 1;
+    auto map = [&](int64_t i, size_t& b) {      // b: a bucket at or before i's, moved to i's
+        while (b + 1 < B && seg[3 * (b + 1)] <= i) ++b;
+        return i - seg[3 * b] + seg[3 * b + 1] + owner * seg[3 * b + 2];
+    };
+    int64_t best = S < T ? S : T;
+    size_t b0 = 0;
+    for (size_t b = 1; b < B; ++b) {
+        const int64_t s0 = seg[3 * b];
+        if (s0 >= S) break;
+        const int64_t first = s0 / T * T;
+        if (first == s0) continue;              // the tile starts in bucket b
+        const int64_t last = (first + T < S ? first + T : S) - 1;
+        size_t bb = b0;
+        const int64_t lo = map(first, bb);
+        b0 = bb;
+        const int64_t hi = map(last, bb);
+        if (hi - lo + 1 > best) best = hi - lo + 1;
+    }
+    return best;
+}
+
+// The layout the lane-contiguous kernel takes for bucket-flat contributions of
+// esize bytes: kLayFlatWide when a 2048-element tile's offsets can reach 2^31
+// bytes (its buffer descriptors take 32-bit offsets), else kLayFlat.
+int flat_lay_for(const gsz_plan* p, int64_t owner, int64_t esize) {
+#ifdef GSZ_TEST_HOOKS
+    if (g_force_flat_wide.load(std::memory_order_relaxed)) return kLayFlatWide;
+#endif
+    return max_tile_span(p, owner, kRedTile) * esize >= ((int64_t)1 << 31) ? kLayFlatWide : kLayFlat;
+}
+
 // The lane-contiguous reduce (k_reduce_mean_lc) for bf16 contributions at
 // P <= kLcMaxP (compile-time P for 2, 3, 4, 6, 8 and 16, its runtime-P loop for
 // the others) and for fp32 contributions at every P.
+// clen: elements of each contribution buffer (flat_len, S, or S * P for the
+// interleaved receive buffer); lay may be kLayFlatWide (flat_lay_for).
 template <typename T, int PS>
 void launch_reduce_lc(bool norm, int lay, bool outflat, bool wire16, dim3 grid, hipStream_t st,
                       const RankPtrsT<T>& rp, int P, float invP, int pow2, const int64_t* seg,
-                      const uint64_t* slut, int sshift, int64_t owner, int64_t S, float* g,
-                      double* ws) {
+                      const uint64_t* slut, int sshift, int64_t owner, int64_t S, int64_t clen,
+                      float* g, double* ws) {
     const size_t lds = (int64_t)P * (int64_t)sizeof(T) >= kRedLcLdsMinBytes ? kRedLcLdsBytes : 0;
     auto go = [&](auto nm, auto ly, auto of, auto w16) {
         hipLaunchKernelGGL((k_reduce_mean_lc<T, PS, decltype(nm)::value, decltype(ly)::value,
                                              decltype(of)::value, decltype(w16)::value>),
-                           grid, dim3(kBlock), lds, st, rp, P, invP, pow2, seg, slut, sshift, owner, S, g,
-                           ws);
+                           grid, dim3(kBlock), lds, st, rp, P, invP, pow2, seg, slut, sshift, owner, S,
+                           clen, g, ws);
     };
     using Y = std::true_type;
     using N = std::false_type;
     using Flat = std::integral_constant<int, kLayFlat>;
+    using FlatWide = std::integral_constant<int, kLayFlatWide>;
     auto layouts = [&](auto w16) {
-        with_layout(lay, [&](auto ly) {
+        auto pick = [&](auto ly) {
             if (norm) go(Y{}, ly, N{}, w16);
             else go(N{}, ly, N{}, w16);
-        });
+        };
+        if (lay == kLayFlatWide) pick(FlatWide{});
+        else with_layout(lay, pick);
     };
     if constexpr (std::is_same<T, float>::value) {
         layouts(N{});                            // fp32 contributions: the reduce rows only
     } else {
         if (outflat) {
-            if (norm) go(Y{}, Flat{}, Y{}, N{});
-            else go(N{}, Flat{}, Y{}, N{});
+            if (lay == kLayFlatWide) {
+                if (norm) go(Y{}, FlatWide{}, Y{}, N{});
+                else go(N{}, FlatWide{}, Y{}, N{});
+            } else {
+                if (norm) go(Y{}, Flat{}, Y{}, N{});
+                else go(N{}, Flat{}, Y{}, N{});
+            }
         } else if (wire16) {
             layouts(Y{});
         } else {
@@ -368,6 +421,18 @@ extern "C" int gsz_test_set_reduce_path(int32_t path) {
         return GSZ_ERR_INVALID_ARG;
     }
     g_reduce_path.store(path, std::memory_order_relaxed);
+    return GSZ_OK;
+}
+
+extern "C" int gsz_test_max_tile_span(const gsz_plan* p, int32_t owner, int64_t tile, int64_t* out) {
+    if (!p || !out || tile < 1) { set_error("gsz_test_max_tile_span: bad arguments"); return GSZ_ERR_INVALID_ARG; }
+    if (owner < 0 || owner >= p->P) { set_error("gsz_test_max_tile_span: owner %d outside [0, %d)", owner, p->P); return GSZ_ERR_BAD_RANK; }
+    *out = max_tile_span(p, owner, tile);
+    return GSZ_OK;
+}
+
+extern "C" int gsz_test_set_flat_wide(int32_t on) {
+    g_force_flat_wide.store(on != 0, std::memory_order_relaxed);
     return GSZ_OK;
 }
 
@@ -529,6 +594,11 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
     const int64_t nvec = S / 8;
     int grid = flat_grid((S + kRedTile - 1) / kRedTile);
     const int lay = layout == GSZ_LAYOUT_BUCKET_FLAT ? kLayFlat : ilv ? kLayInterleaved : kLayCompact;
+    // Elements of each contribution buffer, and the layout the lane-contiguous
+    // kernel takes (bucket-flat plans with very large buckets read through
+    // 64-bit addresses).
+    const int64_t clen = lay == kLayFlat ? p->flat_len : ilv ? S * P : S;
+    const int lay_lc = lay == kLayFlat && S > 0 ? flat_lay_for(p, owner, f32in ? 4 : 2) : lay;
     // The bf16 reduce at P > kLcMaxP on a large shard runs the burst kernel,
     // whose grid is one block per CU (at most one per chunk).
     const bool burst = !f32in && use_burst(P, S, wire16);
@@ -550,9 +620,9 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
         const int sshift = p->seg_lut.shift;
         double* wsd = static_cast<double*>(ws);
         with_static_p(P, [&](auto ps) {
-            launch_reduce_lc<float, decltype(ps)::value>(norm, lay, false, false, dim3(grid), stream,
+            launch_reduce_lc<float, decltype(ps)::value>(norm, lay_lc, false, false, dim3(grid), stream,
                                                          rp, P, invP, pow2, p->d_seg, slut, sshift,
-                                                         owner, S, g, wsd);
+                                                         owner, S, clen, g, wsd);
         });
         if ((rc = launched(who))) return rc;
     } else if (S > 0) {
@@ -568,8 +638,8 @@ int reduce_impl(const gsz_plan* p, int32_t owner, const void* const* contrib, in
             constexpr int PS = decltype(ps)::value;
             auto lc = [&](auto pc) {
                 launch_reduce_lc<uint16_t, decltype(pc)::value>(
-                    norm, lay, false, wire16, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
-                    sshift, owner, S, g, wsd);
+                    norm, lay_lc, false, wire16, dim3(grid), stream, rp, P, invP, pow2, p->d_seg, slut,
+                    sshift, owner, S, clen, g, wsd);
             };
             auto wide = [&](auto pc) {
                 if (burst)
@@ -733,12 +803,16 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
     const dim3 grid(tile_grid((S + kAdamTile - 1) / kAdamTile, kMaxWorkItems / kAdamBlock));
     const uint64_t* slut = p->d_seg_lut;
     const int sshift = p->seg_lut.shift;
+    // The bf16 all-gather stores take 32-bit offsets from each tile's first
+    // position unless a tile's positions span 2^31 bytes or more.
+    const int gwide = gathered && max_tile_span(p, owner, kAdamTile) * 2 >= ((int64_t)1 << 31);
+    const int64_t glen = p->flat_len;
     if (gathered && shard_bf16)
-        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, glen, gwide, shard_bf16);
     else if (gathered)
-        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<true, false>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, glen, gwide, shard_bf16);
     else
-        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, shard_bf16);
+        hipLaunchKernelGGL((k_adamw<false, true>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, glen, gwide, shard_bf16);
     return launched(who);
 }
 
@@ -802,6 +876,7 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
     const int sshift = p->seg_lut.shift;
     const bool norm = partials != nullptr;
     double* wsd = static_cast<double*>(ws);
+    const int64_t clen = p->flat_len;
     // chunk c of every bucket, summed in ring order ending at rank c; its norm
     // partial is finalized before the next launch reuses the workspace (stream order)
     for (int c = 0; c < P; ++c) {
@@ -810,9 +885,10 @@ extern "C" int gsz_allreduce_mean(const gsz_plan* p, const uint16_t* const* cont
         with_static_p<true>(P, [&](auto ps) {
             constexpr int PS = decltype(ps)::value;
             auto lc = [&](auto pc) {
+                // g_flat takes 4-byte offsets relative to the tile, like the contributions
                 launch_reduce_lc<uint16_t, decltype(pc)::value>(
-                    norm, kLayFlat, true, false, gr, stream, rp, P, invP, pow2, p->d_seg, slut, sshift, c,
-                    S, g_flat, wsd);
+                    norm, flat_lay_for(p, c, 4), true, false, gr, stream, rp, P, invP, pow2, p->d_seg,
+                    slut, sshift, c, S, clen, g_flat, wsd);
             };
             auto wide = [&](auto pc) {
                 launch_reduce<decltype(pc)::value>(norm, kLayFlat, gr, stream, rp, P, invP, pow2, p->d_seg,
@@ -850,6 +926,6 @@ extern "C" int gsz_adamw_step(float* master, float* m, float* v, const float* g,
     const AdamScalars s = adam_scalars(*hp);
     const int blocks = tile_grid((n + kAdamTile - 1) / kAdamTile, kMaxWorkItems / kAdamBlock);
     hipLaunchKernelGGL((k_adamw<false, true>), dim3(blocks), dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g,
-                       coef, s, nullptr, nullptr, 0, (int64_t)0, n, nullptr, out_bf16);
+                       coef, s, nullptr, nullptr, 0, (int64_t)0, n, nullptr, (int64_t)0, 0, out_bf16);
     return launched(who);
 }

@@ -49,6 +49,24 @@ int gsz_test_set_reduce_path(int32_t path);
  * every setting.  GSZ_ERR_INVALID_ARG if period is not 0 or a power of two. */
 int gsz_test_set_burst_window(uint32_t period, uint32_t window);
 
+/* Nonzero: every bucket-flat reduce made after the call (the shard reduce in
+ * all its forms and the all-reduce) on P <= 16 bf16 or any fp32
+ * contributions reads them through 64-bit addresses, the path the product
+ * takes only for plans whose 2048-element shard tiles span 2^31 bytes or more
+ * of a contribution buffer (buckets of over 2^29 elements); 0 restores the
+ * product's choice.  For the whole process.  Results are bit-identical either
+ * way. */
+int gsz_test_set_flat_wide(int32_t on);
+
+/* *out = the largest span (last position - first position + 1) that the
+ * owner's shard elements [k * tile, (k + 1) * tile) take in the bucket-flat
+ * layout, over every k with k * tile below the shard length (at most tile
+ * when no such range crosses a bucket boundary); the quantity the library
+ * checks against 32-bit buffer offsets.  Host only.  GSZ_ERR_INVALID_ARG for
+ * a NULL plan or out or tile < 1, GSZ_ERR_BAD_RANK for an owner outside
+ * [0, P). */
+int gsz_test_max_tile_span(const gsz_plan* plan, int32_t owner, int64_t tile, int64_t* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,7 +42,8 @@ def test_test_hooks_live_only_in_the_test_build():
     have it; the test build exports everything the product does plus the
     hooks of gsz_test.h."""
     hooks = declared_symbols(TEST_HEADER)
-    assert hooks == ["gsz_test_set_burst_window", "gsz_test_set_grid_limit",
+    assert hooks == ["gsz_test_max_tile_span", "gsz_test_set_burst_window",
+                     "gsz_test_set_flat_wide", "gsz_test_set_grid_limit",
                      "gsz_test_set_reduce_path"]
     prod = ctypes.CDLL(G.LIB_PATH)
     test = ctypes.CDLL(G._binding.TEST_LIB_PATH)
@@ -54,7 +55,11 @@ def test_test_hooks_live_only_in_the_test_build():
         G.set_reduce_path(G.REDUCE_PATH_BURST)
     with pytest.raises(RuntimeError):
         G.set_burst_window(64, 8)
+    with pytest.raises(RuntimeError):
+        G.set_flat_wide(True)
     with G.test_hooks():
+        G.set_flat_wide(True)
+        G.set_flat_wide(False)
         with pytest.raises(G.GszError) as e:     # the cap is a count of blocks
             G.set_grid_limit(-1)
         assert "-1" in str(e.value)
@@ -74,6 +79,50 @@ def test_test_hooks_live_only_in_the_test_build():
         p = G.Plan([5], 100, 2)
     with pytest.raises(ValueError):              # a plan is tied to its build
         G._binding._lib_for(p)
+
+
+def _spans_brute_force(oplan, r, tile):
+    """Largest flat span of `tile` consecutive shard elements of owner r, from
+    the oracle's plan: each shard index's flat position, tile by tile."""
+    offs = np.array([b.shard_off for b in oplan.buckets], dtype=np.int64)
+    bases = np.array([b.base + r * b.chunk for b in oplan.buckets], dtype=np.int64)
+    S = oplan.shard_len
+
+    def pos(i):
+        b = np.searchsorted(offs, i, side="right") - 1
+        return bases[b] + (i - offs[b])
+
+    first = np.arange(0, S, tile, dtype=np.int64)
+    last = np.minimum(first + tile, S) - 1
+    return int((pos(last) - pos(first) + 1).max())
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_max_tile_span_matches_brute_force(case):
+    """The span the library checks against 32-bit buffer offsets (its reduce
+    and AdamW read and write bucket-flat buffers through descriptors based at
+    each tile's first position) equals a brute-force count over every tile,
+    for every owner and several tile sizes, including plans whose tiles cross
+    several small buckets and one bucket holding a single large tensor."""
+    rng = np.random.default_rng(900 + case)
+    P = int(rng.choice([2, 3, 4, 8, 16]))
+    T = int(rng.integers(3, 40))
+    numel = [int(x) for x in rng.choice([0, 1, 7, 64, 500, 3000, 40000], size=T)]
+    numel[int(rng.integers(T))] = int(rng.integers(1, 4)) * 1_000_003
+    cap = int(rng.choice([256, 4096, 100_000, 25 << 20]))
+    oplan = make_plan(numel, cap, P)
+    if oplan.shard_len == 0:
+        pytest.skip("empty shard")
+    with G.test_hooks():
+        plan = G.Plan(numel, cap, P)
+        for r in range(P):
+            for tile in (1, 64, 256, 2048, 5000):
+                got = G.max_tile_span(plan, r, tile)
+                assert got == _spans_brute_force(oplan, r, tile), (r, tile)
+        with pytest.raises(G.GszError):
+            G.max_tile_span(plan, P, 256)
+        with pytest.raises(G.GszError):
+            G.max_tile_span(plan, 0, 0)
 
 
 def test_library_neither_allocates_device_memory_nor_waits():
