@@ -66,8 +66,8 @@ def parse():
                     help="zero: the ZeRO-1/2 shard step (default); ddp: the unsharded step "
                          "(all-reduce, replicated AdamW, unpack)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured as one HIP graph (graph_ms_per_step)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step captured as one HIP graph (graph_ms_per_step)")
     ap.add_argument("--copy-gib", type=float, default=4.0,
                     help="size of the plain copy used as the measured HBM ceiling")
     args = ap.parse_args()
@@ -160,6 +160,54 @@ def gpu_step_stats(ev):
     import numpy as np
     t = [e[0].elapsed_time(e[-1]) for e in ev]
     return dict(mean=float(np.mean(t)), median=float(np.median(t)), min=float(np.min(t)))
+
+
+def timed_steps(step, names, steps):
+    """Times `steps` steps back to back, with one event before the first and one
+    after the last: an event recorded between the calls of a step costs it
+    10-16 us (measured on the 1.3B model and the 7B share), so the per-call
+    breakdown comes from a second pass of as many steps with events between the
+    calls.  Returns (wall ms per step, GPU ms per step, per-call samples in ms,
+    per-step GPU stats of the second pass)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_wall = (time.perf_counter() - t0) / steps * 1e3
+    ms_gpu = e0.elapsed_time(e1) / steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(steps)]
+    for k in range(steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    samples = {n: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)]
+               for i, n in enumerate(names)}
+    return ms_wall, ms_gpu, samples, gpu_step_stats(ev)
+
+
+def graph_steps(step, warmup, steps):
+    """The same step captured once into a HIP graph and replayed `steps` times:
+    wall ms per replay.  The launch gaps between the calls shrink."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
 
 
 def profile_commands(config, trace_dir, fetch_dir, write_dir, variant="zero", layout="auto"):
@@ -504,8 +552,6 @@ def bench_ddp(args):
     parts = torch.zeros(P, dtype=torch.float64, device="cuda")
     coef = torch.empty(1, dtype=torch.float32, device="cuda")
     names = ["bucket_pack", "allreduce_mean", "clip_coef", "adamw_step", "bucket_unpack"]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
 
     def step(e=None):
         calls = [lambda: G.bucket_pack(plan, my_grads, flats[r]),
@@ -520,16 +566,9 @@ def bench_ddp(args):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(ev[k])
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
-    samples = {n: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]
-               for i, n in enumerate(names)}
+    ms_step, gpu_ms, samples, step_gpu = timed_steps(step, names, args.steps)
+    step_gpu = dict(timed=gpu_ms, with_call_events=step_gpu)
     per = {n: float(np.mean(v)) for n, v in samples.items()}
-    step_gpu = gpu_step_stats(ev)
     byts = {"bucket_pack": 4 * w.n_params + 2 * (L - w.n_params),
             "allreduce_mean": (2 * P + 4) * L, "clip_coef": 8 * P + 12,
             "adamw_step": 30 * L, "bucket_unpack": 4 * w.n_params}
@@ -683,9 +722,6 @@ def main():
     calls = [lambda: G.shard_reduce_mean(plan, r, contribs, lay, g, partials[r:r + 1], ws),
              lambda: G.clip_coef(partials, w.hp.max_norm, coef),
              lambda: G.shard_adamw_step(plan, r, master, m, v, g, coef, w.hp, gathered, shard_out)]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
-
     def step(e=None):
         for k, c in enumerate(calls):
             if e: e[k].record()
@@ -694,35 +730,13 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(ev[k])
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
-    samples = {n: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)]
-               for i, n in enumerate(names)}
+    ms_step, gpu_ms, samples, step_gpu = timed_steps(step, names, args.steps)
+    step_gpu = dict(timed=gpu_ms, with_call_events=step_gpu)
     per = {n: float(np.mean(v)) for n, v in samples.items()}
-    step_gpu = gpu_step_stats(ev)
 
     graph_ms = None
-    if args.graph:
-        # The same step captured once into a HIP graph and replayed: the launch
-        # gaps between the calls disappear (this matters for small workloads).
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            step()
-        torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    if not args.no_graph:
+        graph_ms = graph_steps(step, args.warmup, args.steps)
         log(f"[gpu] captured step: {graph_ms:.3f} ms/step over {args.steps} replays")
 
     # Algorithmic bytes (what the method must move), per call: the step's
@@ -916,6 +930,8 @@ def main():
                    "step": " + ".join(names) + (" (all-gather layout)" if gathered is not None
                                                  else " (shard-layout bf16)")},
         "graph_ms_per_step": graph_ms,
+        "graph_hbm_frac_of_peak": (None if graph_ms is None else
+                                   step_bytes / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS),
         "step_ms_gpu": step_gpu,
         "hbm_GBps": step_gbps,
         "hbm_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
