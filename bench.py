@@ -354,6 +354,8 @@ def summarize_counters(csv_path, workload, command, tag, out_dir=None):
                                                           "hip_runtime_copy"})
     out = [f"# rocprofv3 counters per dispatch (mean over dispatches): {workload}", "#",
            f"# command: {command}", "#",
+           f"# kernel sources (as for the traffic summaries): source_sha256 = {kernel_source_digest()}",
+           "#",
            "# " + f"{'kernel':<24} {'dispatches':>10} " + " ".join(f"{n:>32}" for n in names)]
     for k in kernels:
         n_disp = max(len(by[n].get(k, [])) for n in names)
