@@ -364,8 +364,9 @@ def set_burst_window(period, window):
 def set_flat_wide(on):
     """Test build only (inside test_hooks()): while on, every later
     bucket-flat reduce on the lane-contiguous kernel (bf16 at P <= 16, fp32 at
-    any P) reads its contributions through 64-bit addresses, the path of plans
-    whose buckets exceed 2^29 elements; process-wide."""
+    any P) reads its contributions, and every shard AdamW writes its
+    all-gather output, through 64-bit addresses: the paths of plans whose
+    buckets exceed 2^29 elements; process-wide."""
     lib = _test_lib("set_flat_wide")
     _check(lib.gsz_test_set_flat_wide(1 if on else 0), lib)
 

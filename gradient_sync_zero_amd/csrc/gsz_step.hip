@@ -69,8 +69,8 @@ std::atomic<int> g_reduce_path{0};
 // (window >= period).
 std::atomic<uint32_t> g_win_period{0}, g_win_window{0};
 // Nonzero: bucket-flat reduces take the 64-bit-address path of the
-// lane-contiguous kernel (kLayFlatWide), which otherwise only plans with
-// buckets of over 2^29 elements reach.
+// lane-contiguous kernel (kLayFlatWide) and AdamW's all-gather stores theirs,
+// which otherwise only plans with buckets of over 2^29 elements reach.
 std::atomic<int> g_force_flat_wide{0};
 #endif
 
@@ -805,7 +805,10 @@ extern "C" int gsz_shard_adamw_step(const gsz_plan* p, int32_t owner, float* mas
     const int sshift = p->seg_lut.shift;
     // The bf16 all-gather stores take 32-bit offsets from each tile's first
     // position unless a tile's positions span 2^31 bytes or more.
-    const int gwide = gathered && max_tile_span(p, owner, kAdamTile) * 2 >= ((int64_t)1 << 31);
+    int gwide = gathered && max_tile_span(p, owner, kAdamTile) * 2 >= ((int64_t)1 << 31);
+#ifdef GSZ_TEST_HOOKS
+    if (g_force_flat_wide.load(std::memory_order_relaxed)) gwide = gathered != nullptr;
+#endif
     const int64_t glen = p->flat_len;
     if (gathered && shard_bf16)
         hipLaunchKernelGGL((k_adamw<true, true>), grid, dim3(kAdamBlock), kAdamLdsBytes, stream, master, m, v, g, coef, s, p->d_seg, slut, sshift, (int64_t)owner, S, gathered, glen, gwide, shard_bf16);

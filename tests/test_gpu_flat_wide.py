@@ -1,13 +1,14 @@
-"""GPU parity of the bucket-flat reduces on both of their addressing paths.
+"""GPU parity of the bucket-flat accesses on both of their addressing paths.
 
-The lane-contiguous reduce reads bucket-flat contributions through buffer
-descriptors based at each tile's first position, with 32-bit offsets; a plan
-whose tiles span 2^31 bytes or more of a contribution (buckets of over 2^29
-elements) takes 64-bit addresses instead.  The test build's set_flat_wide hook
-forces that second path on small plans, so both run here against the oracle:
-the shard step of every owner, the DDP all-reduce (output at flat positions)
-and the reduce over fp32 contributions, bit-exact, with the norm partials
-equal between the two paths (same grouping)."""
+The lane-contiguous reduce reads bucket-flat contributions, and AdamW writes
+its all-gather output, through buffer descriptors based at each tile's first
+position, with 32-bit offsets; a plan whose tiles span 2^31 bytes or more of a
+flat buffer (buckets of over 2^29 elements) takes 64-bit addresses instead.
+The test build's set_flat_wide hook forces that second path on small plans,
+so both run here against the oracle: the shard step of every owner (reduce
+and AdamW with the all-gather output), the DDP all-reduce (output at flat
+positions) and the reduce over fp32 contributions, bit-exact, with the norm
+partials equal between the two paths (same grouping)."""
 import pytest
 import torch
 
