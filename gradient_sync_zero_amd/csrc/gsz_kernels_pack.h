@@ -53,10 +53,13 @@ __global__ __launch_bounds__(kPackBlock) void k_pack(PackPtrs pp, const int64_t*
         if (vec && j1 - j0 == gsz::kPackTile) {
             static_assert(gsz::kPackTile == 8 * kPackBlock, "one vector per lane");
             // Nontemporal hints on both sides: the bytes are used once (2-3% faster).
-            const int64_t j = j0 + 8 * tid;
-            u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + j));
-            if (MODE == kAccumulate) w = add_bf16x8(ld16(dst + j), w);
-            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + j));
+            // Buffer descriptors at the tile, nontemporal loads, nontemporal
+            // sc1 stores: 2.6% (pack) and 3.6% (bf16 accumulation) faster than
+            // nontemporal 64-bit-address accesses on the 7B share.
+            const BufRes rs = buf_res(src + j0, 2 * gsz::kPackTile), rd = buf_res(dst + j0, 2 * gsz::kPackTile);
+            u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * tid, 0, kCpNt);
+            if (MODE == kAccumulate) w = add_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(rd, 16 * tid, 0, kCpNt), w);
+            __builtin_amdgcn_raw_buffer_store_b128(w, rd, 16 * tid, 0, kCpNtSc1);
         } else if (vec) {
             const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
             for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kPackBlock)
@@ -106,14 +109,16 @@ __global__ __launch_bounds__(kF32Block) void k_pack_f32(PackPtrs pp, const int64
         const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
         if (vec && j1 - j0 == gsz::kPackTile) {
             static_assert(gsz::kPackTile == 4 * kF32Block, "one group of 4 elements per lane");
-            const int64_t ja = j0 + 4 * tid;
-            const u32x2 wa = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src + ja));
+            // Lane l: elements 4l..4l+3 of the tile.  Buffer descriptors at the
+            // tile as in k_pack: 5.9% faster for the fp32 accumulation (7B share).
+            const BufRes rs = buf_res(src + j0, 2 * gsz::kPackTile), rd = buf_res(dst + j0, 4 * gsz::kPackTile);
+            const u32x2 wa = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * tid, 0, kCpNt);
             f32x4 xa = f32x4{bf16_lo(wa.x), bf16_hi(wa.x), bf16_lo(wa.y), bf16_hi(wa.y)};
             if (ACC) {
-                const f32x4 da = ldf4_nt(dst + ja);
+                const f32x4 da = bldf4_nt(rd, 16 * tid);
                 xa = f32x4{da.x + xa.x, da.y + xa.y, da.z + xa.z, da.w + xa.w};
             }
-            stf4_nt(dst + ja, xa);
+            bstf4<kCpNtSc1>(rd, 16 * tid, xa);
         } else if (vec) {
             const int64_t jv = j0 + ((j1 - j0) & ~(int64_t)7);
             for (int64_t j = j0 + 8 * tid; j < jv; j += 8 * kF32Block) {
