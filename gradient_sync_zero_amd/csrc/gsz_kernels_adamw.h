@@ -83,19 +83,33 @@ __global__ __launch_bounds__(kAdamBlock) void k_adamw(float* __restrict__ master
     }
 }
 
-// gathered[i + delta_b] = shard[i] for shard index i of bucket b.
+// gathered[i + delta_b] = shard[i] for shard index i of bucket b.  One block
+// per 2048-element tile (grid-striding past the dispatch limit), lane l moving
+// elements 8l..8l+7 of its wave's 512 (16 bytes): through buffer descriptors
+// based at the tile's first element and its first all-gather position, unless
+// gwide (a tile's positions may span 2^31 bytes or more), where the stores take
+// 64-bit addresses.  glen: elements in `gathered`.
 __global__ __launch_bounds__(kBlock) void k_ag_write(const uint16_t* __restrict__ shard,
                                                      const int64_t* __restrict__ seg,
                                                      const uint64_t* __restrict__ slut, int sshift,
                                                      int64_t owner, int64_t nvec,
-                                                     uint16_t* __restrict__ gathered) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    int64_t v = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+                                                     uint16_t* __restrict__ gathered, int64_t glen,
+                                                     int gwide) {
+    const int64_t S = nvec * 8;
     SegCursor cur{seg, owner, 0, 0, 0};
-    if (v < nvec) cur.seek((int64_t)blockIdx.x * kBlock * 8, slut, sshift);   // the block's first element
-    for (; v < nvec; v += stride) {
-        const int64_t i = v * 8;
-        st16_nt(gathered + cur.map(i), ld16_nt(shard + i));     // nontemporal: 3% faster
+    int64_t t = (int64_t)blockIdx.x * kRedTile;
+    if (t < S) cur.seek(t, slut, sshift);                  // block-uniform: scalar loads
+    for (; t < S; t += (int64_t)gridDim.x * kRedTile) {
+        const int64_t fb = uniform64(cur.map(t));          // the tile's first all-gather position
+        const int64_t i = t + 8 * threadIdx.x;
+        if (i < S) {                                       // S and i are multiples of 8
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(buf_res(shard + t, (S - t) * 2),
+                                                                  16 * threadIdx.x, 0, kCpNt);
+            const int64_t fi = cur.map(i);
+            if (gwide) st16_nt(gathered + fi, w);
+            else __builtin_amdgcn_raw_buffer_store_b128(w, buf_res(gathered + fb, (glen - fb) * 2),
+                                                        (int)(fi - fb) * 2, 0, kCpNtSc1);
+        }
     }
 }
 

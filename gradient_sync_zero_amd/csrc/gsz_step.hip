@@ -831,9 +831,15 @@ extern "C" int gsz_allgather_layout_write(const gsz_plan* p, int32_t owner,
     if (!shard_bf16 || !gathered) { set_error("%s: NULL buffer", who); return GSZ_ERR_INVALID_ARG; }
     if (misaligned(shard_bf16) || misaligned(gathered)) { set_error("%s: misaligned buffer", who); return GSZ_ERR_MISALIGNED; }
     const int64_t nvec = S / 8;
-    hipLaunchKernelGGL(k_ag_write, dim3(flat_grid((nvec + kBlock - 1) / kBlock)), dim3(kBlock), 0, stream, shard_bf16,
-                       p->d_seg, p->d_seg_lut, p->seg_lut.shift, (int64_t)owner, nvec,
-                       gathered);
+    // The stores take 32-bit offsets from each tile's first all-gather position
+    // unless a tile's positions span 2^31 bytes or more.
+    int gwide = max_tile_span(p, owner, kRedTile) * 2 >= ((int64_t)1 << 31);
+#ifdef GSZ_TEST_HOOKS
+    if (g_force_flat_wide.load(std::memory_order_relaxed)) gwide = 1;
+#endif
+    hipLaunchKernelGGL(k_ag_write, dim3(flat_grid((S + kRedTile - 1) / kRedTile)), dim3(kBlock), 0, stream,
+                       shard_bf16, p->d_seg, p->d_seg_lut, p->seg_lut.shift, (int64_t)owner, nvec,
+                       gathered, p->flat_len, gwide);
     return launched(who);
 }
 

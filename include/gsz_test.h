@@ -52,11 +52,12 @@ int gsz_test_set_burst_window(uint32_t period, uint32_t window);
 /* Nonzero: every bucket-flat reduce made after the call (the shard reduce in
  * all its forms and the all-reduce) on P <= 16 bf16 or any fp32
  * contributions reads them through 64-bit addresses, and every
- * gsz_shard_adamw_step writes its all-gather output through them: the paths
- * the product takes only for plans whose shard tiles (2048 elements for the
- * reduce, 256 for AdamW) span 2^31 bytes or more of a flat buffer (buckets of
- * over 2^29 elements); 0 restores the product's choice.  For the whole
- * process.  Results are bit-identical either way. */
+ * gsz_shard_adamw_step and gsz_allgather_layout_write writes its all-gather
+ * output through them: the paths the product takes only for plans whose
+ * shard tiles (2048 elements for the reduce and the writer, 256 for AdamW)
+ * span 2^31 bytes or more of a flat buffer (buckets of over 2^29 elements);
+ * 0 restores the product's choice.  For the whole process.  Results are
+ * bit-identical either way. */
 int gsz_test_set_flat_wide(int32_t on);
 
 /* *out = the largest span (last position - first position + 1) that the

@@ -6,8 +6,9 @@ position, with 32-bit offsets; a plan whose tiles span 2^31 bytes or more of a
 flat buffer (buckets of over 2^29 elements) takes 64-bit addresses instead.
 The test build's set_flat_wide hook forces that second path on small plans,
 so both run here against the oracle: the shard step of every owner (reduce
-and AdamW with the all-gather output), the DDP all-reduce (output at flat
-positions) and the reduce over fp32 contributions, bit-exact, with the norm
+and AdamW with the all-gather output), the standalone all-gather writer, the
+DDP all-reduce (output at flat positions) and the reduce over fp32
+contributions, bit-exact, with the norm
 partials equal between the two paths (same grouping)."""
 import pytest
 import torch
@@ -72,6 +73,14 @@ def test_flat_wide_zero_step(cfg):
             assert_bits(o["shard"][r], ref["p"][r], f"{name} bf16 owner {r}")
         assert_bits(o["gathered"], ref["gathered"], f"{name} gathered bf16")
     assert (wide["partials"] == buf["partials"]).all()
+    # the standalone all-gather writer on both store paths
+    for on in (True, False):
+        G.set_flat_wide(on)
+        ag = torch.full((plan.flat_len,), 0x7777, dtype=torch.uint16, device="cuda")
+        for r in range(P):
+            G.allgather_layout_write(plan, r, buf["shards_dev"][r], ag)
+        torch.cuda.synchronize()
+        assert_bits(host(ag), ref["gathered"], f"standalone all-gather layout, wide={on}")
 
 
 @pytest.mark.parametrize("cfg", [5, 1])
