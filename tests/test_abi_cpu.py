@@ -126,19 +126,20 @@ def test_max_tile_span_matches_brute_force(case):
 
 
 def test_max_tile_span_reaches_the_32_bit_limit_on_a_huge_bucket():
-    """A plan whose tensor of 3 * 2^30 elements sits between two small buckets
-    has 2048-element tiles spanning more than 2^30 flat positions (2^31 bytes
-    of bf16), the case in which the product reads bucket-flat contributions and
-    writes all-gather positions through 64-bit addresses; the 52-tensor 7B
-    share stays far below it.  Host only: the plan is metadata."""
+    """A plan whose first bucket holds a tensor of 3 * 2^30 elements has, for
+    owner 0 of 2, a 2048-element tile that crosses from that bucket's chunk to
+    the next bucket's: it spans more than 2^30 flat positions (2^31 bytes of
+    bf16), the case in which the product reads bucket-flat contributions and
+    writes all-gather positions through 64-bit addresses.  Owner 1's chunks
+    follow each other closely, and the 7B share stays far below the limit.
+    Host only: the plan is metadata."""
     numel = [1000, 3 << 30, 1000]
     oplan = make_plan(numel, 25 << 20, 2)
     with G.test_hooks():
         plan = G.Plan(numel, 25 << 20, 2)
-        for r in range(2):
-            span = G.max_tile_span(plan, r, 2048)
-            assert span == _spans_brute_force(oplan, r, 2048)
-            assert span * 2 >= 1 << 31, span
+        spans = [G.max_tile_span(plan, r, 2048) for r in range(2)]
+        assert spans == [_spans_brute_force(oplan, r, 2048) for r in range(2)]
+        assert spans[0] * 2 >= 1 << 31 > spans[1] * 2, spans
         w = W.by_id(3)
         p7 = G.Plan(w.numel, w.bucket_cap_bytes, w.world_size)
         assert G.max_tile_span(p7, 0, 2048) * 2 < 1 << 31
