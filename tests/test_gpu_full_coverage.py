@@ -1,8 +1,12 @@
 """Full-coverage GPU parity at the full sizes, in the launch configuration
 bench.py times: the 1.3B model and the 7B share (P = 8, bucket-flat
 contributions, bf16 parameters in all-gather layout) and the 70B share (P =
-64, shard-compact contributions, shard-layout bf16), owner 0.  Every shard
-element is compared with the oracle, window by window (16M elements): the
+64, shard-compact contributions, shard-layout bf16): every owner of the 1.3B
+model, owner 0 and the last owner of the 7B share (whose chunk of every bucket
+ends where the bucket does and whose ring order starts at rank 0), owner 0 of
+the 70B share.  (The pads of the padded workloads are checked on every owner
+at the small sizes.)
+Every shard element is compared with the oracle, window by window (16M elements): the
 reduced gradient g, the updated master, m and v and the bf16 parameters bit
 for bit; the fused fp64 norm partial against the oracle's partial of the
 whole shard within 1e-5 relative.
@@ -48,7 +52,6 @@ from tests.parity import assert_bits, host
 pytestmark = pytest.mark.gpu
 
 WINDOW = 1 << 24
-OWNER = 0
 THREADS = max(1, min(16, os.cpu_count() or 1))
 
 
@@ -60,9 +63,9 @@ class GpuStep:
     """The GPU side of one workload's step, run once: device outputs kept for
     the window comparisons, the contributions freed."""
 
-    def __init__(self, cfg):
+    def __init__(self, cfg, owner):
         w = W.by_id(cfg)
-        P, r = w.world_size, OWNER
+        P, r = w.world_size, owner
         plan = G.Plan(w.numel, w.bucket_cap_bytes, P).upload()
         S, L = plan.shard_len, plan.flat_len
         flat = (P + 2) * 2 * L + 2 * w.n_params + 18 * S < 240e9      # as bench.py decides
@@ -114,25 +117,25 @@ class GpuStep:
         else:
             del contribs, flats
         torch.cuda.empty_cache()
-        self.w, self.plan, self.S, self.flat = w, plan, S, flat
+        self.w, self.plan, self.S, self.flat, self.owner = w, plan, S, flat, r
         self.gathered, self.shard_out = gathered, shard_out
-        say(f"[{w.name}] GPU step done in {time.perf_counter() - t0:.1f} s: S={S}, "
+        say(f"[{w.name}] owner {r}: GPU step done in {time.perf_counter() - t0:.1f} s: S={S}, "
             f"partial={self.partial:.6e}, norm={self.norm}, coef={self.coef}")
 
 
 class OracleWindows:
-    """The oracle side: owner 0's shard (or, with flat=True, the whole
+    """The oracle side: one owner's shard (or, with flat=True, the whole
     bucket-major flat buffer) in windows, regenerated on the host."""
 
-    def __init__(self, w, flat=False):
-        self.w = w
+    def __init__(self, w, flat=False, owner=0):
+        self.w, self.owner = w, owner
         self.plan = make_plan(w.numel, w.bucket_cap_bytes, w.world_size)
         if flat:   # (flat offset, parameter index, length) of every tensor
             pre = OI.prefix(w.numel)
             self.pieces = sorted((self.plan.tensor_offset[t], pre[t], n)
                                  for t, n in enumerate(w.numel) if n)
         else:
-            self.pieces = sorted(OI.owner_pieces(self.plan, OWNER))
+            self.pieces = sorted(OI.owner_pieces(self.plan, owner))
         self.starts = np.array([p[0] for p in self.pieces], dtype=np.int64)
         self.pool = cf.ThreadPoolExecutor(max_workers=THREADS)
 
@@ -164,7 +167,7 @@ class OracleWindows:
 
         def run(sl):
             lo, hi = sl
-            g = reduce_mean([c[lo:hi] for c in cs], OWNER)
+            g = reduce_mean([c[lo:hi] for c in cs], self.owner)
             th, m, v, p = adamw(st[0][lo:hi], st[1][lo:hi], st[2][lo:hi], g, coef, hp.lr,
                                 hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step)
             return g, th, m, v, p
@@ -177,16 +180,16 @@ class OracleWindows:
 _cache = {}
 
 
-def step_for(cfg):
-    if cfg not in _cache:
+def step_for(cfg, owner=0):
+    if (cfg, owner) not in _cache:
         _cache.clear()
         torch.cuda.empty_cache()
-        _cache[cfg] = (GpuStep(cfg), OracleWindows(W.by_id(cfg)), {})
-    return _cache[cfg]
+        _cache[cfg, owner] = (GpuStep(cfg, owner), OracleWindows(W.by_id(cfg), owner=owner), {})
+    return _cache[cfg, owner]
 
 
-def compare_windows(cfg, part, n_parts):
-    gs, ow, acc = step_for(cfg)
+def compare_windows(cfg, part, n_parts, owner=0):
+    gs, ow, acc = step_for(cfg, owner)
     S = gs.S
     nwin = -(-S // WINDOW)
     lo_w, hi_w = part * nwin // n_parts, (part + 1) * nwin // n_parts
@@ -200,7 +203,7 @@ def compare_windows(cfg, part, n_parts):
         assert_bits(host(gs.m[a:b]), m, f"{gs.w.name} m [{a}, {b})")
         assert_bits(host(gs.v[a:b]), v, f"{gs.w.name} v [{a}, {b})")
         if gs.flat:
-            pos = OI.flat_pos_of_shard(ow.plan, OWNER, np.arange(a, b, dtype=np.int64))
+            pos = OI.flat_pos_of_shard(ow.plan, owner, np.arange(a, b, dtype=np.int64))
             idx = torch.from_numpy(pos).to("cuda")
             got = host(gs.gathered.view(torch.int16)[idx].view(torch.uint16))
         else:
@@ -210,8 +213,8 @@ def compare_windows(cfg, part, n_parts):
             say(f"[{gs.w.name}] windows {lo_w}..{k} of {nwin} equal ({time.perf_counter() - t0:.1f} s)")
 
 
-def check_norm_and_clip(cfg):
-    gs, ow, acc = step_for(cfg)
+def check_norm_and_clip(cfg, owner=0):
+    gs, ow, acc = step_for(cfg, owner)
     nwin = -(-gs.S // WINDOW)
     assert sorted(acc) == list(range(nwin)), "every window compared first"
     want = 0.0
@@ -226,9 +229,14 @@ def check_norm_and_clip(cfg):
 
 
 @pytest.mark.timeout(900)
-def test_gpt_1_3b_every_shard_element():
-    compare_windows(2, 0, 1)
-    check_norm_and_clip(2)
+@pytest.mark.parametrize("owner", range(8))
+def test_gpt_1_3b_every_shard_element(owner):
+    assert W.by_id(2).world_size == 8
+    compare_windows(2, 0, 1, owner)
+    check_norm_and_clip(2, owner)
+    if owner == 7:
+        _cache.clear()
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
@@ -237,6 +245,15 @@ def test_llama_7b_share_every_shard_element(part):
     compare_windows(3, part, 2)
     if part == 1:
         check_norm_and_clip(3)
+
+
+@pytest.mark.timeout(900)
+def test_llama_7b_share_last_owner_every_shard_element():
+    last = W.by_id(3).world_size - 1
+    compare_windows(3, 0, 1, last)
+    check_norm_and_clip(3, last)
+    _cache.clear()
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
